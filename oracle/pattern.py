@@ -1,0 +1,160 @@
+"""Oracle: block-selection rules and their CSR encoding (test infrastructure only).
+
+Notation follows [P1] section 3.1: sequence length N, block size ``block_size``
+(the page's 32), M = N / block_size blocks, query block ``row_i``.
+
+Readings of the pages taken here (each one is also listed in the design notes):
+
+* The log-stride exponent runs k = 1 .. ceil(log2(M)) ([P1] section 3.1 prints
+  "k=1,2,...,ceil(log2(128))=7").  ceil(log2 M) is computed with integers.
+* A stride floor(2^k / block_size) that is 0 adds the query block itself: it
+  changes nothing.
+* Targets outside [0, M) are dropped ([P1] section 3.1 intersects with
+  [0, 127]).
+* The three global anchors (block 0, M/2 and M-1) are added as *columns* of
+  every row; the anchor rows themselves are not made dense ([P1] section 3.1
+  lists them in the set of K blocks each token connects to).
+* The selected set of a row is a set: duplicates collapse, CSR columns ascend.
+
+Pins (tests/test_oracle.py): the hand-derived rows and row-size histogram of
+the page's worked example N=4096, block 32 (tests/golden/), the hand-derived
+tiny case, a closed-form offset description of every log-linear row, the
+O(log M) row bound, own-block membership and symmetry; the ±4 block band that
+the page's ±256-token window produces at block 64 (closed form 2080/4096
+coverage); CSR round trips.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+
+def ceil_log2(m: int) -> int:
+    """ceil(log2(m)) for an integer m >= 1, without floating point."""
+    if m < 1:
+        raise ValueError("ceil_log2 needs m >= 1")
+    return (m - 1).bit_length()
+
+
+def loglinear_block_sets(seq_len: int, block_size: int, *, local_radius: int = 1,
+                         k_max: int | None = None, global_blocks=None) -> list[set[int]]:
+    """Selected K blocks of every query block under the log-linear rule.
+
+    [P1] section 3.1 ("block partitioning and index mapping"), for the query
+    block row_i of a token:
+
+    1. Local: row_i - 1, row_i, row_i + 1, kept inside [0, M).
+    2. Log-stride: for k = 1 .. ceil(log2 M) add row_i - floor(2^k / block_size)
+       and row_i + floor(2^k / block_size) (the 2^k is a token distance, so it
+       is divided by the block size to become a block distance), kept inside
+       [0, M).
+    3. Global: blocks 0, M/2 and M - 1.
+
+    ``local_radius``, ``k_max`` and ``global_blocks`` generalise the printed
+    constants (1, ceil(log2 M) and {0, M/2, M-1}); the defaults are the page's.
+    """
+    if block_size <= 0 or seq_len <= 0 or seq_len % block_size != 0:
+        raise ValueError("seq_len must be a positive multiple of block_size")
+    M = seq_len // block_size
+    if k_max is None:
+        k_max = ceil_log2(M)
+    if global_blocks is None:
+        global_blocks = [0, M // 2, M - 1]
+    for g in global_blocks:
+        if not 0 <= g < M:
+            raise ValueError(f"global block {g} outside [0, {M})")
+
+    sets: list[set[int]] = []
+    for row_i in range(M):
+        selected: set[int] = set()
+        # 1. local blocks
+        for j in range(row_i - local_radius, row_i + local_radius + 1):
+            if 0 <= j < M:
+                selected.add(j)
+        # 2. log-stride blocks: token stride 2^k turned into a block stride
+        for k in range(1, k_max + 1):
+            stride = (2 ** k) // block_size
+            for j in (row_i - stride, row_i + stride):
+                if 0 <= j < M:
+                    selected.add(j)
+        # 3. global anchor blocks
+        for g in global_blocks:
+            selected.add(int(g))
+        sets.append(selected)
+    return sets
+
+
+def block_mask_from_sets(sets: list[set[int]]) -> np.ndarray:
+    """[M, M] uint8 block mask with mask[i, j] = 1 iff j is selected by row i."""
+    M = len(sets)
+    mask = np.zeros((M, M), dtype=np.uint8)
+    for i, s in enumerate(sets):
+        for j in s:
+            mask[i, j] = 1
+    return mask
+
+
+def csr_from_block_mask(mask: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """CSR of a block mask: row_ptr int32[M+1], col_idx int32[nnz].
+
+    row_ptr[0] = 0, row_ptr[i+1] = row_ptr[i] + |S(i)|, and col_idx lists S(i)
+    in ascending order.  This is the per-query-block index table of [P1]
+    section 3.2 ("precomputed on the CPU before launch"), stored as CSR because
+    the number of K blocks differs from row to row.
+    """
+    mask = np.asarray(mask)
+    if mask.ndim != 2 or mask.shape[0] != mask.shape[1]:
+        raise ValueError("block mask must be square")
+    M = mask.shape[0]
+    row_ptr = np.zeros(M + 1, dtype=np.int64)
+    cols: list[int] = []
+    for i in range(M):
+        row_cols = np.nonzero(mask[i])[0]
+        cols.extend(int(c) for c in row_cols)
+        row_ptr[i + 1] = row_ptr[i] + len(row_cols)
+    return row_ptr.astype(np.int32), np.asarray(cols, dtype=np.int32)
+
+
+def block_mask_from_csr(row_ptr, col_idx, M: int) -> np.ndarray:
+    """Decode a CSR back into an [M, M] uint8 block mask."""
+    mask = np.zeros((M, M), dtype=np.uint8)
+    for i in range(M):
+        for t in range(int(row_ptr[i]), int(row_ptr[i + 1])):
+            mask[i, int(col_idx[t])] = 1
+    return mask
+
+
+def local_global_token_mask(seq_len: int, local_window: int, global_tokens) -> np.ndarray:
+    """Token-level [N, N] bool mask: local window plus global tokens.
+
+    [P3] "sparse pattern: Local + Global": token i sees tokens
+    [i - local_window, i + local_window] (clipped to the sequence); each global
+    token g sees every position (row g) and is seen by every position
+    (column g).  Negative global indices count from the end.
+    """
+    mask = np.zeros((seq_len, seq_len), dtype=bool)
+    for i in range(seq_len):
+        start = max(0, i - local_window)
+        end = min(seq_len, i + local_window + 1)
+        mask[i, start:end] = True
+    for g in global_tokens:
+        g = int(g) % seq_len
+        mask[g, :] = True
+        mask[:, g] = True
+    return mask
+
+
+def token_mask_to_block_mask(token_mask: np.ndarray, block_size: int) -> np.ndarray:
+    """[P3] "Block-Sparse": a block is computed when more than half of its
+    token pairs are set.  The block count rounds up; a partial last block is
+    averaged over the tokens it has."""
+    seq_len = token_mask.shape[0]
+    num_blocks = (seq_len + block_size - 1) // block_size
+    out = np.zeros((num_blocks, num_blocks), dtype=np.uint8)
+    for i in range(num_blocks):
+        for j in range(num_blocks):
+            tile = token_mask[i * block_size:(i + 1) * block_size,
+                              j * block_size:(j + 1) * block_size]
+            if tile.mean() > 0.5:
+                out[i, j] = 1
+    return out

@@ -1,0 +1,311 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+None of these compares the oracle with itself: the pattern is checked against
+hand-derived rows of the pages' worked examples and a closed-form offset
+description; the attention against library routines (torch's
+scaled_dot_product_attention in float64, scipy's logsumexp), a textbook loop,
+closed forms and invariants.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import logsumexp
+
+import oracle
+from oracle import (block_mask_from_csr, block_mask_from_sets, block_sparse_attention,
+                    block_sparse_attention_head, ceil_log2, csr_from_block_mask,
+                    local_global_token_mask, loglinear_block_sets, token_mask_to_block_mask)
+from synthetic_inputs import local_global_block_mask, random_block_mask
+
+
+# ----------------------------------------------------------------------------- pattern
+
+
+def _check_golden_loglinear(g, sets):
+    N = int(g["N"][0])
+    bs = int(g["block_size"][0])
+    M = int(g["M"][0])
+    assert N // bs == M == len(sets)
+    assert ceil_log2(M) == int(g["k_max"][0])
+    globals_ = [int(x) for x in g["globals"]]
+    assert globals_ == [0, M // 2, M - 1]
+    for i, cols in g["rows"].items():
+        assert sorted(sets[i]) == cols, f"row {i}"
+    assert sum(len(s) for s in sets) == int(g["nnz"][0])
+
+
+def test_pattern_tiny_hand_derived(golden):
+    g = golden("tiny_loglinear.txt")
+    sets = loglinear_block_sets(int(g["N"][0]), int(g["block_size"][0]))
+    _check_golden_loglinear(g, sets)
+    assert len(g["rows"]) == len(sets)  # every row is listed
+
+
+def test_pattern_worked_example_hand_derived(golden):
+    g = golden("worked_example_loglinear.txt")
+    sets = loglinear_block_sets(4096, 32)
+    _check_golden_loglinear(g, sets)
+    strides = [(2 ** k) // 32 for k in range(1, ceil_log2(128) + 1)]
+    assert strides == [int(x) for x in g["strides"]]
+    hist = {}
+    for s in sets:
+        hist[len(s)] = hist.get(len(s), 0) + 1
+    want = dict(tuple(int(x) for x in item.split(":")) for item in g["histogram"])
+    assert hist == want
+
+
+def _closed_form_sets(M, bs):
+    """Log-linear rows written as an offset set: {0, +-1} and +-2^e for every
+    power of two 2^e * bs <= 2^ceil(log2 M) (the non-zero block strides),
+    plus the globals {0, M/2, M-1}.  Block size a power of two."""
+    K = (M - 1).bit_length()
+    b = bs.bit_length() - 1
+    offsets = {0, 1, -1}
+    for e in range(0, K - b + 1):
+        offsets |= {2 ** e, -(2 ** e)}
+    out = []
+    for i in range(M):
+        s = {i + o for o in offsets if 0 <= i + o < M}
+        s |= {0, M // 2, M - 1}
+        out.append(s)
+    return out
+
+
+@pytest.mark.parametrize("M,bs", [(1, 32), (2, 32), (3, 32), (4, 16), (5, 32), (7, 64),
+                                  (8, 32), (100, 32), (128, 32), (256, 16), (512, 64),
+                                  (1000, 32), (2048, 128)])
+def test_pattern_closed_form(M, bs):
+    sets = loglinear_block_sets(M * bs, bs)
+    assert sets == _closed_form_sets(M, bs)
+
+
+def test_pattern_long_config_counts():
+    # N=32768, block 64: strides floor(2^k/64), k=1..9 = 0,0,0,0,0,1,2,4,8.
+    sets = loglinear_block_sets(32768, 64)
+    assert [(2 ** k) // 64 for k in range(1, 10)] == [0, 0, 0, 0, 0, 1, 2, 4, 8]
+    hist = {}
+    for s in sets:
+        hist[len(s)] = hist.get(len(s), 0) + 1
+    # interior rows: offsets {0,+-1,+-2,+-4,+-8} (9) + 3 globals = 12
+    assert max(hist) == 12
+    assert sum(len(s) for s in sets) == sum(k * v for k, v in hist.items())
+    assert sets[300] == {0, 256, 511} | {300 + o for o in (0, 1, -1, 2, -2, 4, -4, 8, -8)}
+
+
+@pytest.mark.parametrize("bs", [16, 32, 64])
+def test_pattern_row_bound_is_logarithmic(bs):
+    # |S(i)| <= 3 local + 2 per distinct non-zero stride beyond the local one + 3 globals,
+    # i.e. 6 + 2*(ceil(log2 M) - log2 bs), reached for large M: O(log M).
+    b = bs.bit_length() - 1
+    for p in range(0, 14):
+        M = 2 ** p
+        sets = loglinear_block_sets(M * bs, bs)
+        bound = 6 + 2 * max(0, ceil_log2(M) - b)
+        assert max(len(s) for s in sets) <= bound
+        if M >= 8:  # row M/4 keeps every offset in range and off the globals
+            assert max(len(s) for s in sets) == bound
+
+
+@pytest.mark.parametrize("M,bs", [(8, 32), (128, 32), (512, 64), (77, 32)])
+def test_pattern_own_block_and_symmetry(M, bs):
+    sets = loglinear_block_sets(M * bs, bs)
+    G = {0, M // 2, M - 1}
+    for i, s in enumerate(sets):
+        assert i in s  # every token attends to its own block
+        for j in s - G:
+            if i not in G:
+                assert i in sets[j], (i, j)  # local and stride parts are symmetric
+
+
+def test_pattern_rejects_bad_input():
+    with pytest.raises(ValueError):
+        loglinear_block_sets(100, 32)
+    with pytest.raises(ValueError):
+        loglinear_block_sets(256, 32, global_blocks=[8])
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_csr_roundtrip(seed):
+    M = 1 + seed * 13
+    mask = random_block_mask(M, 0.3, seed)
+    row_ptr, col_idx = csr_from_block_mask(mask)
+    assert row_ptr.dtype == np.int32 and col_idx.dtype == np.int32
+    assert row_ptr[0] == 0 and row_ptr[-1] == int(mask.astype(bool).sum()) == len(col_idx)
+    for i in range(M):
+        cols = col_idx[row_ptr[i]:row_ptr[i + 1]]
+        assert np.all(np.diff(cols) > 0)  # ascending, unique
+    assert np.array_equal(block_mask_from_csr(row_ptr, col_idx, M), mask)
+
+
+def test_csr_worked_example_row_ptr():
+    mask = block_mask_from_sets(loglinear_block_sets(4096, 32))
+    row_ptr, col_idx = csr_from_block_mask(mask)
+    assert len(row_ptr) == 129 and row_ptr[-1] == 1251
+    assert list(col_idx[:6]) == [0, 1, 2, 4, 64, 127]
+    assert 1 - 1251 / (128 * 128) == pytest.approx(0.92365, abs=1e-5)
+
+
+def test_local_global_token_to_block(golden):
+    g = golden("local_global_window.txt")
+    bs, window = int(g["block_size"][0]), int(g["local_window"][0])
+    N = 16 * bs
+    tm = local_global_token_mask(N, window, [])
+    # coverage of each block distance, counted from the token mask
+    cov = {t: int(tm[0:bs, t * bs:(t + 1) * bs].sum()) for t in range(6)}
+    want = dict(tuple(int(x) for x in item.split(":")) for item in g["coverage"])
+    assert cov == want
+    bm = token_mask_to_block_mask(tm, bs)
+    r = int(g["band_radius"][0])
+    i = np.arange(16)[:, None]
+    j = np.arange(16)[None, :]
+    assert np.array_equal(bm, (np.abs(i - j) <= r).astype(np.uint8))
+    # global tokens [0, -1] do not survive the >50% rule on their own
+    bm_g = token_mask_to_block_mask(local_global_token_mask(N, window, [0, -1]), bs)
+    assert np.array_equal(bm_g, bm)
+    # the workload's block-level reading: the band plus global block rows/columns
+    lg = local_global_block_mask(16, radius=r)
+    assert np.array_equal(lg[1:-1, 1:-1], bm[1:-1, 1:-1])
+    assert lg[0].all() and lg[-1].all() and lg[:, 0].all() and lg[:, -1].all()
+
+
+# ----------------------------------------------------------------------------- attention
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def _sdpa(q, k, v, mask=None, scale=None):
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(torch.float64)
+    m = None if mask is None else torch.from_numpy(mask.astype(bool))
+    out = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v), attn_mask=m,
+                                                           scale=scale)
+    return out.numpy()
+
+
+def test_attention_all_ones_equals_dense_sdpa():
+    N, d, bs = 256, 64, 32
+    q, k, v = (_rand((N, d), s) for s in (1, 2, 3))
+    o, lse = block_sparse_attention_head(q, k, v, np.ones((N // bs, N // bs)), bs)
+    np.testing.assert_allclose(o, _sdpa(q, k, v), rtol=0, atol=1e-12)
+    s = q @ k.T / math.sqrt(d)
+    np.testing.assert_allclose(lse, logsumexp(s, axis=1), rtol=0, atol=1e-12)
+
+
+def test_attention_all_ones_textbook_loop():
+    N, d, bs = 48, 8, 16
+    q, k, v = (_rand((N, d), s) for s in (4, 5, 6))
+    o, lse = block_sparse_attention_head(q, k, v, np.ones((3, 3)), bs)
+    for r in range(N):
+        scores = [sum(q[r, c] * k[j, c] for c in range(d)) / math.sqrt(d) for j in range(N)]
+        mx = max(scores)
+        e = [math.exp(x - mx) for x in scores]
+        z = sum(e)
+        for c in range(d):
+            assert abs(o[r, c] - sum(e[j] * v[j, c] for j in range(N)) / z) < 1e-12
+        assert abs(lse[r] - (mx + math.log(z))) < 1e-12
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_attention_block_mask_equals_masked_sdpa(seed):
+    bs, M, d = 16, 9, 32
+    N = bs * M
+    q, k, v = (_rand((N, d), 10 * seed + s) for s in range(3))
+    mask = random_block_mask(M, 0.35, seed)
+    o, lse = block_sparse_attention_head(q, k, v, mask, bs, scale=0.37)
+    token_mask = np.kron(mask, np.ones((bs, bs), dtype=np.uint8))
+    np.testing.assert_allclose(o, _sdpa(q, k, v, token_mask, scale=0.37), rtol=0, atol=1e-12)
+    s = q @ k.T * 0.37
+    s[token_mask == 0] = -np.inf
+    np.testing.assert_allclose(lse, logsumexp(s, axis=1), rtol=0, atol=1e-12)
+
+
+def test_attention_diagonal_mask_is_per_block_dense():
+    bs, M, d = 32, 4, 64
+    N = bs * M
+    q, k, v = (_rand((N, d), s) for s in (7, 8, 9))
+    o, _ = block_sparse_attention_head(q, k, v, np.eye(M), bs)
+    for b in range(M):
+        r = slice(b * bs, (b + 1) * bs)
+        np.testing.assert_allclose(o[r], _sdpa(q[r], k[r], v[r]), rtol=0, atol=1e-12)
+
+
+def test_attention_zero_query_uniform_weights():
+    # Q = 0: every selected key gets the same weight, so O is the mean of the
+    # selected V rows and LSE = ln(bs * |S(qb)|).  Worked example pattern.
+    N, bs, d = 4096, 32, 64
+    M = N // bs
+    sets = loglinear_block_sets(N, bs)
+    mask = block_mask_from_sets(sets)
+    q = np.zeros((N, d))
+    k = _rand((N, d), 11)
+    v = _rand((N, d), 12)
+    qbs = [0, 1, 64, 126, 127]
+    o, lse = block_sparse_attention_head(q, k, v, mask, bs, query_blocks=qbs)
+    assert lse[0] == pytest.approx(math.log(192), abs=1e-12)        # |S(0)| = 6
+    assert lse[64 * bs] == pytest.approx(math.log(288), abs=1e-12)  # |S(64)| = 9
+    for qb in qbs:
+        rows = np.concatenate([np.arange(j * bs, (j + 1) * bs) for j in sorted(sets[qb])])
+        want = v[rows].mean(axis=0)
+        r = slice(qb * bs, (qb + 1) * bs)
+        np.testing.assert_allclose(o[r], np.broadcast_to(want, (bs, d)), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[r], math.log(bs * len(sets[qb])), rtol=0, atol=1e-12)
+
+
+def test_attention_constant_v():
+    bs, M, d = 32, 8, 64
+    N = bs * M
+    q, k = _rand((N, d), 13), _rand((N, d), 14)
+    v = np.full((N, d), -1.75)
+    mask = block_mask_from_sets(loglinear_block_sets(N, bs))
+    o, _ = block_sparse_attention_head(q, k, v, mask, bs)
+    np.testing.assert_allclose(o, -1.75, rtol=0, atol=1e-13)
+
+
+def test_attention_convex_combination_and_normalisation():
+    bs, M, d = 32, 16, 64
+    N = bs * M
+    q, k, v = (3 * _rand((N, d), s) for s in (15, 16, 17))
+    mask = block_mask_from_sets(loglinear_block_sets(N, bs))
+    o, _, w = block_sparse_attention_head(q, k, v, mask, bs, return_weights=True)
+    for qb in range(M):
+        token_sel = np.repeat(mask[qb] != 0, bs)
+        W = w[qb]
+        assert np.all(W >= 0)
+        assert np.all(W[:, ~token_sel] == 0)          # unconnected positions hold 0
+        np.testing.assert_allclose(W.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+        r = slice(qb * bs, (qb + 1) * bs)
+        lo = v[token_sel].min(axis=0)
+        hi = v[token_sel].max(axis=0)
+        assert np.all(o[r] >= lo - 1e-12) and np.all(o[r] <= hi + 1e-12)
+
+
+def test_attention_batched_wrapper_and_sampling():
+    B, H, N, d, bs = 2, 3, 128, 16, 32
+    rng = np.random.default_rng(3)
+    q, k, v = (rng.standard_normal((B, H, N, d)) for _ in range(3))
+    mask = random_block_mask(N // bs, 0.5, 1)
+    o, lse = block_sparse_attention(q, k, v, mask, bs, heads=[(1, 2)])
+    assert np.isnan(o[0, 0]).all() and np.isfinite(o[1, 2]).all()
+    o12, lse12 = block_sparse_attention_head(q[1, 2], k[1, 2], v[1, 2], mask, bs)
+    np.testing.assert_array_equal(o[1, 2], o12)
+    np.testing.assert_array_equal(lse[1, 2], lse12)
+
+
+def test_attention_rejects_empty_row():
+    with pytest.raises(ValueError):
+        block_sparse_attention_head(np.zeros((64, 8)), np.zeros((64, 8)), np.zeros((64, 8)),
+                                    np.array([[1, 0], [0, 0]]), 32)
+
+
+def test_oracle_imports_nothing_from_the_library():
+    import os
+    import re
+    root = os.path.dirname(oracle.__file__)
+    for name in os.listdir(root):
+        if name.endswith(".py"):
+            src = open(os.path.join(root, name)).read()
+            assert not re.search(r"block_sparse_attention_csr_amd|synthetic_inputs", src), name
