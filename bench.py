@@ -1,0 +1,317 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-sparse attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the hot path over one batch of synthetic input: the
+pattern (log-linear rule or block mask -> CSR, built on the host and uploaded
+once, then served from a device-resident cache as a model would for every
+layer and step) and one fused forward launch.  Inputs are resident in HBM
+before the timed region.  The K timed steps are captured in one HIP graph and
+replayed (the forward of a single (B=1, H=8) batch lasts a few microseconds,
+so eager launches would time the host, not the GPU); the eager rate is
+reported beside it.
+
+Prints ONE JSON line.  Metric: effective TFLOP/s over the selected blocks,
+4 * bs^2 * d flop per selected block pair per (batch, head).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "effective TFLOP/s (selected blocks) + % bf16 MFMA peak, N=4096 log-linear"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix
+PEAK_HBM_GBPS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "block_sparse_attention_csr_amd", "csrc", "forward.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def parse_args(argv=None):
+    p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=1000)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="worked_example")
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--no-graph", action="store_true", help="time eager launches only")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-saturating", action="store_true",
+                   help="skip the B=32 line of the worked-example shape")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="minimum CPU time for the oracle baseline")
+    return p.parse_args(argv)
+
+
+class Case:
+    """Inputs, cached pattern and preallocated outputs of one workload."""
+
+    def __init__(self, name, seed, device):
+        import torch
+
+        import block_sparse_attention_csr_amd as bsa
+        from synthetic_inputs import WORKLOADS, make_qkv, workload_block_mask
+
+        self.bsa = bsa
+        self.w = w = WORKLOADS[name]
+        self.mask = workload_block_mask(w, seed)
+        q, k, v = make_qkv(w.B, w.H, w.N, w.d, w.torch_dtype, seed)
+        self.q, self.k, self.v = (t.to(device) for t in (q, k, v))
+        self.out = torch.empty_like(self.q)
+        self.lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=device)
+        self.cache = bsa.PatternCache(device)
+        torch.cuda.synchronize()
+        # First step: host pattern build + upload (cache miss) + forward.
+        t0 = time.perf_counter()
+        self.step()
+        torch.cuda.synchronize()
+        self.first_step_ms = (time.perf_counter() - t0) * 1e3
+        self.nnz = self.cache.get(w.N, w.block_size, mask=self.mask)[2]
+        self.flops = 4.0 * w.block_size ** 2 * w.d * self.nnz * w.B * w.H
+        elt = 2 if w.dtype == "bf16" else 4
+        # compulsory traffic: Q, K, V read once, O written once, LSE written once
+        self.compulsory_bytes = 4.0 * w.B * w.H * w.N * w.d * elt + 4.0 * w.B * w.H * w.N
+
+    def step(self):
+        w = self.w
+        row_ptr, col_idx, nnz = self.cache.get(w.N, w.block_size, mask=self.mask)
+        self.bsa.forward(self.q, self.k, self.v, row_ptr, col_idx, w.block_size,
+                         out=self.out, lse=self.lse, nnz=nnz)
+
+
+def time_eager(case, steps):
+    import torch
+
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        case.step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall / steps
+
+
+def time_graph(case, steps):
+    """Capture `steps` forward launches in one HIP graph; replay once timed.
+    Returns (wall seconds per step, event seconds per launch)."""
+    import torch
+
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        case.step()  # pattern already cached: no host build, no upload inside capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for _ in range(steps):
+            case.step()
+    graph.replay()  # untimed warm replay
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    replay_stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(replay_stream)
+    graph.replay()
+    end.record(replay_stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall / steps, start.elapsed_time(end) * 1e-3 / steps
+
+
+def time_events_per_launch(case, steps):
+    """Average launch duration from HIP events bracketing every launch on the
+    launch stream, with the stream held by a sleep kernel while the host
+    enqueues (so the host's enqueue rate does not show up as GPU time)."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2e8))
+    for a, b in evs:
+        a.record(stream)
+        case.step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) * 1e-3 / steps
+
+
+def load_traffic(workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, valid
+    only while the kernel source is unchanged since the counters were taken."""
+    path = os.path.join(PROFILES, f"bsa_fwd_traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(workload: str, seed: int, min_seconds: float):
+    """Time the float64 oracle as it stands on this host's cores over whole
+    passes of the workload (or of a bounded head subset for large ones)."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from synthetic_inputs import WORKLOADS, make_qkv, workload_block_mask
+
+    w = WORKLOADS[workload]
+    mask = workload_block_mask(w, seed)
+    if mask is None:
+        mask = oracle.block_mask_from_sets(oracle.loglinear_block_sets(w.N, w.block_size))
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    if len(heads) > 8:
+        heads = heads[:8]
+    Bs = max(b for b, _ in heads) + 1
+    q, k, v = make_qkv(Bs, w.H, w.N, w.d, w.torch_dtype, seed)
+    f = lambda t: t.float().numpy().astype(np.float64)
+    qf, kf, vf = f(q), f(k), f(v)
+    nnz = int((mask != 0).sum())
+    flops_per_pass = 4.0 * w.block_size ** 2 * w.d * nnz * len(heads)
+    passes = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.block_sparse_attention(qf, kf, vf, mask, w.block_size, heads=heads)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or el * (passes + 1) / passes > 30.0:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {
+        "value": flops_per_pass * passes / el / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{workload}: {len(heads)} of {w.B * w.H} (batch, head) pairs, "
+                   f"{passes} full passes, {el:.1f} s wall; float64 dense masked attention"),
+        "host_affinity_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the forward shards over (batch, head) with no communication, so the N-GPU "
+              "rate is N times the one-GPU rate of the per-GPU share.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    device = torch.device("cuda:0")
+    torch.cuda.set_device(device)
+
+    case = Case(args.workload, args.seed, device)
+    w = case.w
+    for _ in range(args.warmup):
+        case.step()
+    torch.cuda.synchronize()
+
+    eager_s = time_eager(case, min(args.steps, 200))
+    graph_s, graph_evt_s = (None, None)
+    if not args.no_graph:
+        try:
+            graph_s, graph_evt_s = time_graph(case, args.steps)
+        except Exception as e:  # graph capture unsupported: report eager only
+            print(f"bench.py: graph timing unavailable ({e}); eager only", file=sys.stderr)
+    launch_s = time_events_per_launch(case, min(args.steps, 200))
+    step_s = graph_s if graph_s is not None else eager_s
+
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    value = case.flops / step_s / 1e12
+    achieved = case.flops / launch_s / 1e12
+    traffic = load_traffic(args.workload)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_s * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) Q/K/V; pattern per workload)",
+        "config": {
+            "workload": w.name, "description": w.description, "B": w.B, "H": w.H, "N": w.N,
+            "d": w.d, "block_size": w.block_size, "nnz_per_head": case.nnz,
+            "pattern": w.pattern, "parallelism": "single GPU",
+            "timing": "HIP graph of K launches" if graph_s is not None else "eager",
+        },
+        "pct_bf16_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "eager_ms_per_step": eager_s * 1e3,
+        "first_step_ms_with_pattern_build_and_upload": case.first_step_ms,
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": traffic,
+            "kernel": "bsa_fwd_kernel",
+            "avg_launch_us": launch_s * 1e6,
+            "graph_event_us_per_launch": None if graph_evt_s is None else graph_evt_s * 1e6,
+            "compulsory_hbm_gbps": round(case.compulsory_bytes / launch_s / 1e9, 1),
+            "hbm_peak_gbps": PEAK_HBM_GBPS,
+        },
+    }
+
+    if not args.no_saturating and args.workload == "worked_example":
+        del case
+        torch.cuda.empty_cache()
+        sat = Case("worked_example_b32", args.seed, device)
+        for _ in range(5):
+            sat.step()
+        sat_steps = max(10, min(100, args.steps // 10))
+        s_graph, s_evt = time_graph(sat, sat_steps) if not args.no_graph else (None, None)
+        s_launch = time_events_per_launch(sat, sat_steps)
+        s_step = s_graph if s_graph is not None else time_eager(sat, sat_steps)
+        result["saturating_worked_example_b32"] = {
+            "value": round(sat.flops / s_step / 1e12, 3),
+            "unit": "TFLOP/s",
+            "ms_per_step": s_step * 1e3,
+            "pct_bf16_mfma_peak": round(100.0 * sat.flops / s_step / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "avg_launch_us": s_launch * 1e6,
+            "achieved_tflops_per_launch": round(sat.flops / s_launch / 1e12, 3),
+            "compulsory_hbm_gbps": round(sat.compulsory_bytes / s_launch / 1e9, 1),
+            "traffic": load_traffic("worked_example_b32"),
+        }
+        del sat
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args.workload, args.seed, args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

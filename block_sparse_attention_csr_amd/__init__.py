@@ -1,0 +1,231 @@
+"""Block-sparse attention forward for AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libbsa.so`` (declared in
+``include/bsa.h``): argument marshalling only.  Every step of the attention
+runs in the native library: the pattern builder on the host, the forward in
+one HIP kernel.  PyTorch provides device memory and the current stream.
+
+    row_ptr, col_idx = build_pattern(4096, 32)                 # log-linear rule
+    row_ptr, col_idx = build_pattern(4096, 64, mask=block_mask)  # user mask
+    o, lse = forward(q, k, v, row_ptr.cuda(), col_idx.cuda(), block_size=32)
+
+There is no fallback: if the library is missing, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+__all__ = [
+    "BsaError", "build_pattern", "forward", "status_string", "abi_version", "library_path",
+    "PatternCache", "BSA_OK",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libbsa.so")
+
+BSA_OK = 0
+_PATTERN_LOGLINEAR = 0
+_PATTERN_BLOCK_MASK = 1
+_DTYPE_F32 = 0
+_DTYPE_BF16 = 1
+
+
+class BsaError(RuntimeError):
+    """A bsa_* call returned a status other than BSA_OK."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+class _PatternDesc(ctypes.Structure):
+    _fields_ = [
+        ("kind", ctypes.c_int32),
+        ("seq_len", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("local_radius", ctypes.c_int32),
+        ("k_max", ctypes.c_int32),
+        ("num_global", ctypes.c_int32),
+        ("global_blocks", ctypes.POINTER(ctypes.c_int32)),
+        ("mask", ctypes.POINTER(ctypes.c_uint8)),
+    ]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"native library not built: {_LIB_PATH} is missing "
+            "(run `python -m block_sparse_attention_csr_amd.build`)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+    p32 = ctypes.POINTER(ctypes.c_int32)
+    lib.bsa_build_pattern.argtypes = [ctypes.POINTER(_PatternDesc), p32, p32, i64,
+                                      ctypes.POINTER(i64)]
+    lib.bsa_build_pattern.restype = i32
+    lib.bsa_forward.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, i64,
+                                ctypes.c_float, vp]
+    lib.bsa_forward.restype = i32
+    lib.bsa_status_string.argtypes = [i32]
+    lib.bsa_status_string.restype = ctypes.c_char_p
+    lib.bsa_abi_version.argtypes = []
+    lib.bsa_abi_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return _load().bsa_status_string(int(status)).decode()
+
+
+def abi_version() -> int:
+    return int(_load().bsa_abi_version())
+
+
+def _desc(seq_len, block_size, mask, local_radius, k_max, global_blocks, keep):
+    d = _PatternDesc()
+    d.seq_len = int(seq_len)
+    d.block_size = int(block_size)
+    d.local_radius = -1 if local_radius is None else int(local_radius)
+    d.k_max = -1 if k_max is None else int(k_max)
+    d.num_global = -1
+    d.global_blocks = None
+    d.mask = None
+    if mask is not None:
+        d.kind = _PATTERN_BLOCK_MASK
+        m = np.ascontiguousarray(np.asarray(mask) != 0, dtype=np.uint8)
+        keep.append(m)
+        d.mask = m.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))
+    else:
+        d.kind = _PATTERN_LOGLINEAR
+        if global_blocks is not None:
+            g = np.ascontiguousarray(np.asarray(global_blocks, dtype=np.int32).reshape(-1))
+            keep.append(g)
+            d.num_global = int(g.size)
+            d.global_blocks = g.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    return d
+
+
+def build_pattern(seq_len: int, block_size: int, *, mask=None, local_radius=None, k_max=None,
+                  global_blocks=None):
+    """CSR (row_ptr int32[M+1], col_idx int32[nnz]) as CPU torch tensors.
+
+    Without ``mask``: the log-linear rule (defaults: radius 1,
+    k_max = ceil(log2 M), globals {0, M/2, M-1}).  With ``mask`` ([M, M],
+    nonzero = selected): that block mask.  Raises BsaError on a bad pattern.
+    """
+    import torch
+
+    lib = _load()
+    keep = []
+    desc = _desc(seq_len, block_size, mask, local_radius, k_max, global_blocks, keep)
+    nnz = ctypes.c_int64(0)
+    st = lib.bsa_build_pattern(ctypes.byref(desc), None, None, 0, ctypes.byref(nnz))
+    if st != BSA_OK:
+        raise BsaError(st, "bsa_build_pattern")
+    M = seq_len // block_size
+    row_ptr = np.zeros(M + 1, dtype=np.int32)
+    col_idx = np.zeros(max(nnz.value, 1), dtype=np.int32)
+    p32 = ctypes.POINTER(ctypes.c_int32)
+    st = lib.bsa_build_pattern(ctypes.byref(desc), row_ptr.ctypes.data_as(p32),
+                               col_idx.ctypes.data_as(p32), col_idx.size, ctypes.byref(nnz))
+    if st != BSA_OK:
+        raise BsaError(st, "bsa_build_pattern")
+    return torch.from_numpy(row_ptr), torch.from_numpy(col_idx[:nnz.value].copy())
+
+
+def _dtype_code(t):
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return _DTYPE_BF16
+    if t.dtype == torch.float32:
+        return _DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; bfloat16 or float32 expected")
+
+
+def forward(q, k, v, row_ptr, col_idx, block_size: int, scale: float | None = None, *,
+            out=None, lse=None, nnz: int | None = None, stream=None):
+    """Block-sparse attention forward on the GPU.
+
+    q, k, v: CUDA tensors [B, H, N, d] (bfloat16 or float32), contiguous.
+    row_ptr, col_idx: int32 CUDA tensors from ``build_pattern`` (same device).
+    Returns (o [B, H, N, d] same dtype, lse [B, H, N] float32).  The launch is
+    enqueued on the current stream (or ``stream``) and not synchronised.
+    ``nnz`` (host int) avoids reading row_ptr back; by default it is
+    col_idx.numel().
+    """
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a CUDA tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous [B, H, N, d]")
+    if q.shape != k.shape or q.shape != v.shape or q.dtype != k.dtype or q.dtype != v.dtype:
+        raise ValueError("q, k, v must share shape and dtype")
+    if q.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    if row_ptr.dtype != torch.int32 or col_idx.dtype != torch.int32:
+        raise TypeError("row_ptr / col_idx must be int32")
+    if not (row_ptr.is_cuda and col_idx.is_cuda):
+        raise ValueError("row_ptr / col_idx must be on the GPU")
+    B, H, N, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if nnz is None:
+        nnz = col_idx.numel()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = _load().bsa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                             lse.data_ptr(), B, H, N, d, int(block_size), _dtype_code(q),
+                             row_ptr.data_ptr(), col_idx.data_ptr(), int(nnz),
+                             0.0 if scale is None else float(scale), stream.cuda_stream)
+    if st != BSA_OK:
+        raise BsaError(st, "bsa_forward")
+    return out, lse
+
+
+class PatternCache:
+    """Device-resident CSR patterns keyed by their descriptor.
+
+    A model reuses one pattern for every layer and step at a given
+    (seq_len, block_size); the host build and the upload happen once.
+    """
+
+    def __init__(self, device="cuda"):
+        self.device = device
+        self._cache = {}
+
+    def get(self, seq_len: int, block_size: int, *, mask=None, local_radius=None, k_max=None,
+            global_blocks=None):
+        if mask is not None:
+            mkey = np.ascontiguousarray(np.asarray(mask) != 0, dtype=np.uint8).tobytes()
+        else:
+            mkey = None
+        gkey = None if global_blocks is None else tuple(int(g) for g in global_blocks)
+        key = (seq_len, block_size, mkey, local_radius, k_max, gkey)
+        hit = self._cache.get(key)
+        if hit is None:
+            row_ptr, col_idx = build_pattern(seq_len, block_size, mask=mask,
+                                             local_radius=local_radius, k_max=k_max,
+                                             global_blocks=global_blocks)
+            hit = (row_ptr.to(self.device, non_blocking=False),
+                   col_idx.to(self.device, non_blocking=False), int(col_idx.numel()))
+            self._cache[key] = hit
+        return hit

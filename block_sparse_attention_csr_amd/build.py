@@ -1,0 +1,63 @@
+"""Build the native library ``libbsa.so`` in-tree for gfx950.
+
+    python -m block_sparse_attention_csr_amd.build
+
+The host pattern builder is plain C++ (g++); the kernel and the forward entry
+point are HIP (hipcc --offload-arch=gfx950).  Every build recompiles.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+INCLUDE = os.path.join(ROOT, "include")
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libbsa.so")
+ARCH = "gfx950"
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+CXX = os.environ.get("CXX", "g++")
+
+# Packed fp32 VALU instructions are switched off for all device code.
+HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError(f"build step failed ({r.returncode}): {' '.join(cmd)}")
+    # hipcc's host pass does not know the packed-fp32 feature; drop that note.
+    noise = "'-packed-fp32-ops' is not a recognized feature"
+    out = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
+    if out.strip() and verbose:
+        print(out)
+
+
+def build(verbose: bool = False, extra_hip_flags=None) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    pattern_o = os.path.join(BUILD, "pattern.o")
+    forward_o = os.path.join(BUILD, "forward.o")
+    _run([CXX, *CXX_FLAGS, f"-I{INCLUDE}", "-c", os.path.join(CSRC, "pattern.cpp"),
+          "-o", pattern_o], verbose)
+    _run([HIPCC, *HIP_FLAGS, *(extra_hip_flags or []), f"-I{INCLUDE}", "-c",
+          os.path.join(CSRC, "forward.hip"), "-o", forward_o], verbose)
+    tmp = LIB + ".tmp"
+    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", pattern_o, forward_o, "-o", tmp],
+         verbose)
+    shutil.move(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,151 @@
+/*
+ * bsa.h -- block-sparse attention forward for AMD Instinct MI355X (gfx950).
+ *
+ * Plain C ABI.  All pointers are raw host or device pointers (stated per
+ * argument); no framework types cross this boundary.  Every entry point
+ * returns a bsa_status; none aborts or throws.
+ *
+ * Sources (web pages, cited by title and section):
+ *  [P1] "Block Sparse Attention: Log-Linear complexity sparse attention
+ *       implementation" (czchanglian.com, news/56740).
+ *  [P2] "How to implement efficient sparse attention for the 4090: from
+ *       principle to engineering practice" (qqiyuan.cn).
+ *  [P3] Ascend CANN SparseFlashAttention article (hwcomputing.csdn.net).
+ */
+#ifndef BSA_H_
+#define BSA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes.  Values are stable. */
+typedef enum bsa_status {
+  BSA_OK = 0,
+  BSA_ERR_NULL_POINTER = 1,     /* a required pointer is NULL */
+  BSA_ERR_INVALID_ARGUMENT = 2, /* unknown kind/dtype, unsupported block or head size */
+  BSA_ERR_SHAPE = 3,            /* sizes <= 0, seq_len % block_size != 0, nnz inconsistent,
+                                   or a size that overflows the index types */
+  BSA_ERR_EMPTY_ROW = 4,        /* a query block selects no K block */
+  BSA_ERR_INDEX_RANGE = 5,      /* a global block outside [0, M) */
+  BSA_ERR_BUFFER_TOO_SMALL = 6, /* col_cap < nnz; *nnz_out still holds nnz */
+  BSA_ERR_HIP = 7               /* the HIP runtime reported an error at launch */
+} bsa_status;
+
+typedef enum bsa_pattern_kind {
+  BSA_PATTERN_LOGLINEAR = 0,  /* built-in log-linear rule, [P1] section 3.1 */
+  BSA_PATTERN_BLOCK_MASK = 1  /* user [M, M] block mask, [P2] item 1, [P3] "Block-Sparse" */
+} bsa_pattern_kind;
+
+typedef enum bsa_dtype {
+  BSA_DTYPE_F32 = 0,  /* IEEE binary32 Q/K/V/O */
+  BSA_DTYPE_BF16 = 1  /* bfloat16 Q/K/V/O, float32 accumulation */
+} bsa_dtype;
+
+/*
+ * Pattern descriptor (host memory, read only during the call).
+ *
+ * Notation of [P1] section 3.1: N = seq_len, bs = block_size, M = N / bs,
+ * query block i ("row_i").
+ *
+ * BSA_PATTERN_LOGLINEAR selects, for every query block i,
+ *   local      {i - r, ..., i + r}                 r = local_radius
+ *   log-stride {i - floor(2^k / bs), i + floor(2^k / bs)}  k = 1 .. k_max
+ *   global     the global blocks (default {0, M/2, M-1})
+ * keeping only blocks in [0, M).  [P1] section 3.1 prints r = 1,
+ * k_max = ceil(log2 M) and the anchors {0, M/2, M-1} (worked example N = 4096,
+ * bs = 32, M = 128, k = 1..7, anchors {0, 64, 127}); the anchors are added as
+ * columns of every row, and anchor rows are not made dense.
+ *
+ * BSA_PATTERN_BLOCK_MASK selects block j for query block i iff
+ * mask[i * M + j] != 0.
+ */
+typedef struct bsa_pattern_desc {
+  int32_t kind;                 /* bsa_pattern_kind */
+  int32_t seq_len;              /* N > 0, multiple of block_size */
+  int32_t block_size;           /* bs > 0 */
+  int32_t local_radius;         /* LOGLINEAR: r >= 0; < 0 selects the default 1 */
+  int32_t k_max;                /* LOGLINEAR: >= 0; < 0 selects ceil(log2 M) */
+  int32_t num_global;           /* LOGLINEAR: < 0 selects {0, M/2, M-1};
+                                   >= 0 uses global_blocks[0 .. num_global) */
+  const int32_t* global_blocks; /* LOGLINEAR: host array, each in [0, M) */
+  const uint8_t* mask;          /* BLOCK_MASK: host array, M * M bytes, row-major */
+} bsa_pattern_desc;
+
+/*
+ * bsa_build_pattern -- selected K blocks of every query block, as CSR.
+ *
+ * The per-query-block index table of [P1] section 3.2 (built on the CPU
+ * before launch), encoded as CSR because rows differ in length:
+ *   row_ptr[0] = 0, row_ptr[i + 1] = row_ptr[i] + |S(i)|,
+ *   col_idx[row_ptr[i] .. row_ptr[i + 1]) = S(i) in ascending order, unique.
+ *
+ * desc     host; required.
+ * row_ptr  host, caller-owned int32[M + 1]; may be NULL (not written).
+ * col_idx  host, caller-owned int32[col_cap]; may be NULL to query nnz only.
+ * col_cap  capacity of col_idx in elements (ignored when col_idx is NULL).
+ * nnz_out  host; required; receives nnz = sum_i |S(i)| on BSA_OK and on
+ *          BSA_ERR_BUFFER_TOO_SMALL.
+ *
+ * Errors: BSA_ERR_NULL_POINTER (desc, nnz_out, or mask for BLOCK_MASK, or
+ * global_blocks when num_global > 0), BSA_ERR_INVALID_ARGUMENT (unknown kind),
+ * BSA_ERR_SHAPE (sizes, divisibility, nnz > INT32_MAX), BSA_ERR_INDEX_RANGE
+ * (global block outside [0, M)), BSA_ERR_EMPTY_ROW (a mask row with no block;
+ * [P1] section 5.1 traces NaN outputs to such rows), BSA_ERR_BUFFER_TOO_SMALL.
+ * On error nothing is guaranteed about row_ptr / col_idx contents.
+ *
+ * Host only, synchronous, deterministic, thread-safe (no global state).
+ */
+bsa_status bsa_build_pattern(const bsa_pattern_desc* desc, int32_t* row_ptr, int32_t* col_idx,
+                             int64_t col_cap, int64_t* nnz_out);
+
+/*
+ * bsa_forward -- block-sparse attention forward, one fused kernel launch.
+ *
+ * For every batch b, head h and query block qb, over the key positions of the
+ * K blocks S(qb) = col_idx[row_ptr[qb] .. row_ptr[qb + 1]):
+ *   O[b,h,r,:] = sum_j softmax_j(scale * Q[b,h,r,:] . K[b,h,j,:]) V[b,h,j,:]
+ *   LSE[b,h,r] = ln sum_j exp(scale * Q[b,h,r,:] . K[b,h,j,:])
+ * with the softmax normalised over exactly the selected positions
+ * ([P3] "the O(N^2) bottleneck of long sequences" for the formula, [P1]
+ * section 3.3 for the normalisation over the connected blocks only).
+ * Every block of S(qb) is attended in full (non-causal).
+ *
+ * q, k, v  device, caller-owned, contiguous [batch, heads, seq_len, head_dim]
+ *          of `dtype`, 16-byte aligned.
+ * o        device, caller-owned, same shape and dtype; written.
+ * lse      device, caller-owned float32 [batch, heads, seq_len]; written.
+ *          May be NULL when the log-sum-exp is not wanted.
+ * row_ptr, col_idx  device copies of bsa_build_pattern's output for
+ *          (seq_len, block_size); one pattern serves every batch and head.
+ *          col_idx entries outside [0, M) are skipped by the kernel.
+ * nnz      row_ptr[M] (host copy); must satisfy M <= nnz <= M * M.
+ * scale    > 0 multiplies the scores; <= 0 selects 1 / sqrt(head_dim)
+ *          ([P3] "full call flow").
+ * stream   a hipStream_t, or NULL for the null stream.  The launch is
+ *          enqueued and the call returns without synchronising.
+ *
+ * Supported: dtype BF16 or F32; block_size 32 or 64; head_dim 64 or 128.
+ * All arguments are validated on the host before any HIP call; errors are
+ * BSA_ERR_NULL_POINTER, BSA_ERR_INVALID_ARGUMENT, BSA_ERR_SHAPE, and
+ * BSA_ERR_HIP when the launch itself fails.  NaN/Inf inputs propagate.
+ */
+bsa_status bsa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int32_t batch, int32_t heads, int32_t seq_len, int32_t head_dim,
+                       int32_t block_size, int32_t dtype, const int32_t* row_ptr,
+                       const int32_t* col_idx, int64_t nnz, float scale, void* stream);
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* bsa_status_string(int32_t status);
+
+/* ABI version of this header: bump on any incompatible change. */
+#define BSA_ABI_VERSION 1
+int32_t bsa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSA_H_ */

@@ -1,0 +1,91 @@
+"""The C-ABI library loads, exports every symbol include/bsa.h declares, and
+bsa_forward rejects bad arguments on the host before any HIP call (so these
+run without a GPU)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import block_sparse_attention_csr_amd as bsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsa.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(bsa_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_entry_points():
+    names = _declared_functions()
+    assert {"bsa_build_pattern", "bsa_forward", "bsa_status_string", "bsa_abi_version"} <= set(
+        names)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = bsa._load()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", bsa.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (bsa_\w+)", out))
+    assert set(_declared_functions()) <= exported
+
+
+def test_library_has_gfx950_code_object():
+    # the library built here embeds a device code object for gfx950
+    blob = open(bsa.library_path(), "rb").read()
+    assert b"amdgcn-amd-amdhsa--gfx950" in blob
+
+
+def test_abi_version_and_status_strings():
+    assert bsa.abi_version() == 1
+    for code in range(8):
+        assert bsa.status_string(code).startswith("BSA_")
+    assert bsa.status_string(99) == "BSA_ERR_UNKNOWN"
+
+
+FAKE = 1 << 20  # a 16-byte-aligned non-null pointer value; never dereferenced
+
+
+def _fwd(**over):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=8, N=4096, d=64, bs=32,
+                dtype=1, row_ptr=FAKE, col_idx=FAKE, nnz=1251, scale=0.0, stream=None)
+    args.update(over)
+    lib = bsa._load()
+    return lib.bsa_forward(args["q"], args["k"], args["v"], args["o"], args["lse"], args["B"],
+                           args["H"], args["N"], args["d"], args["bs"], args["dtype"],
+                           args["row_ptr"], args["col_idx"], args["nnz"],
+                           ctypes.c_float(args["scale"]), args["stream"])
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "o", "row_ptr", "col_idx"])
+def test_forward_null_pointer(field):
+    assert _fwd(**{field: None}) == 1
+
+
+@pytest.mark.parametrize("over", [{"d": 96}, {"d": 32}, {"d": 256}, {"bs": 16}, {"bs": 128},
+                                  {"dtype": 2}, {"dtype": -1}, {"q": FAKE + 2},
+                                  {"o": FAKE + 8}, {"scale": float("nan")},
+                                  {"scale": float("inf")}])
+def test_forward_invalid_argument(over):
+    assert _fwd(**over) == 2
+
+
+@pytest.mark.parametrize("over", [{"B": 0}, {"H": -1}, {"N": 4010}, {"N": 0}, {"nnz": 127},
+                                  {"nnz": 128 * 128 + 1}, {"B": 1 << 20, "H": 1 << 12}])
+def test_forward_shape(over):
+    assert _fwd(**over) == 3
+
+
+def test_python_forward_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)
+    rp = torch.zeros(3, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        bsa.forward(q, q, q, rp, rp, 32)

@@ -1,0 +1,140 @@
+"""bsa_build_pattern (C++ host builder, through the C ABI) against the oracle.
+
+CSR output must be bit-exact: same row_ptr, same col_idx, int32.
+"""
+
+import numpy as np
+import pytest
+
+import block_sparse_attention_csr_amd as bsa
+import oracle
+from synthetic_inputs import (WORKLOADS, bernoulli_block_mask, local_global_block_mask,
+                              random_block_mask, workload_block_mask)
+
+
+def _oracle_csr_loglinear(N, bs, **kw):
+    return oracle.csr_from_block_mask(oracle.block_mask_from_sets(
+        oracle.loglinear_block_sets(N, bs, **kw)))
+
+
+def _assert_same(got, want):
+    row_ptr, col_idx = got
+    want_rp, want_ci = want
+    assert row_ptr.dtype == col_idx.dtype  # torch.int32
+    assert str(row_ptr.dtype) == "torch.int32"
+    np.testing.assert_array_equal(row_ptr.numpy(), want_rp)
+    np.testing.assert_array_equal(col_idx.numpy(), want_ci)
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_workload_patterns_bit_exact(name):
+    w = WORKLOADS[name]
+    mask = workload_block_mask(w, seed=0)
+    if mask is None:
+        got = bsa.build_pattern(w.N, w.block_size)
+        want = _oracle_csr_loglinear(w.N, w.block_size)
+    else:
+        got = bsa.build_pattern(w.N, w.block_size, mask=mask)
+        want = oracle.csr_from_block_mask(mask)
+    _assert_same(got, want)
+
+
+def test_worked_example_nnz():
+    row_ptr, col_idx = bsa.build_pattern(4096, 32)
+    assert int(row_ptr[-1]) == col_idx.numel() == 1251
+    assert col_idx[:6].tolist() == [0, 1, 2, 4, 64, 127]
+
+
+def test_local_global_counts():
+    rp, _ = bsa.build_pattern(8192, 64, mask=local_global_block_mask(128))
+    sizes = np.diff(rp.numpy())
+    assert sizes[0] == sizes[-1] == 128
+    assert int(rp[-1]) == 1622
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 6, 7, 8, 100, 1000])
+@pytest.mark.parametrize("bs", [16, 32, 64, 128])
+def test_loglinear_sweep(M, bs):
+    _assert_same(bsa.build_pattern(M * bs, bs), _oracle_csr_loglinear(M * bs, bs))
+
+
+@pytest.mark.parametrize("radius,k_max,globals_", [(0, None, None), (2, None, None),
+                                                   (1, 0, None), (1, 3, None), (1, 40, None),
+                                                   (1, None, []), (1, None, [5, 5, 0]),
+                                                   (3, 12, [1, 2, 3, 4, 5, 6, 7])])
+def test_loglinear_parameters(radius, k_max, globals_):
+    N, bs = 300 * 32, 32
+    got = bsa.build_pattern(N, bs, local_radius=radius, k_max=k_max, global_blocks=globals_)
+    kw = {"local_radius": radius}
+    if k_max is not None:
+        kw["k_max"] = k_max
+    if globals_ is not None:
+        kw["global_blocks"] = globals_
+    if k_max == 0 and radius == 0 and globals_ == []:
+        pytest.skip("empty rows")
+    _assert_same(got, _oracle_csr_loglinear(N, bs, **kw))
+
+
+@pytest.mark.parametrize("seed", range(200))
+def test_random_masks(seed):
+    rng = np.random.default_rng(seed)
+    M = int(rng.integers(1, 70))
+    p = float(rng.uniform(0.02, 1.0))
+    mask = random_block_mask(M, p, seed)
+    # arbitrary nonzero byte values select too
+    mask = mask * rng.integers(1, 256, size=mask.shape).astype(np.uint8)
+    _assert_same(bsa.build_pattern(M * 64, 64, mask=mask),
+                 oracle.csr_from_block_mask(mask))
+
+
+def test_bernoulli_mask_statistics():
+    mask = bernoulli_block_mask(32, seed=0)
+    assert np.all(np.diag(mask) == 1)
+    rp, ci = bsa.build_pattern(2048, 64, mask=mask)
+    assert int(rp[-1]) == int(mask.sum())
+
+
+def _status(excinfo):
+    return excinfo.value.status
+
+
+def test_error_empty_row():
+    mask = np.eye(4, dtype=np.uint8)
+    mask[2, 2] = 0
+    with pytest.raises(bsa.BsaError) as e:
+        bsa.build_pattern(4 * 32, 32, mask=mask)
+    assert _status(e) == 4
+
+
+def test_error_global_out_of_range():
+    with pytest.raises(bsa.BsaError) as e:
+        bsa.build_pattern(256, 32, global_blocks=[8])
+    assert _status(e) == 5
+    with pytest.raises(bsa.BsaError) as e:
+        bsa.build_pattern(256, 32, global_blocks=[-1])
+    assert _status(e) == 5
+
+
+@pytest.mark.parametrize("N,bs", [(100, 32), (0, 32), (64, 0), (-64, 32)])
+def test_error_shape(N, bs):
+    with pytest.raises(bsa.BsaError) as e:
+        bsa.build_pattern(N, bs)
+    assert _status(e) == 3
+
+
+def test_error_buffer_too_small_reports_nnz():
+    import ctypes
+    lib = bsa._load()
+    desc = bsa._desc(4096, 32, None, None, None, None, [])
+    nnz = ctypes.c_int64(-1)
+    buf = (ctypes.c_int32 * 10)()
+    st = lib.bsa_build_pattern(ctypes.byref(desc), None, buf, 10, ctypes.byref(nnz))
+    assert st == 6 and nnz.value == 1251
+    st = lib.bsa_build_pattern(None, None, None, 0, ctypes.byref(nnz))
+    assert st == 1
+    st = lib.bsa_build_pattern(ctypes.byref(desc), None, None, 0, None)
+    assert st == 1
+    desc.kind = 7
+    assert lib.bsa_build_pattern(ctypes.byref(desc), None, None, 0, ctypes.byref(nnz)) == 2
+    desc.kind = 1  # block mask without a mask pointer
+    assert lib.bsa_build_pattern(ctypes.byref(desc), None, None, 0, ctypes.byref(nnz)) == 1
