@@ -55,7 +55,26 @@ def parse_args(argv=None):
                    help="skip the B=32 line of the worked-example shape")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="minimum CPU time for the oracle baseline")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run 5 device-to-device copies of 1 GiB (reference kernel for "
+                        "scaling HBM byte counters) and exit")
     return p.parse_args(argv)
+
+
+def copy_calibration():
+    """Five 1 GiB device copies: each reads 1 GiB and writes 1 GiB of HBM.
+    Profiled with FETCH_SIZE / WRITE_SIZE it gives the counter-to-bytes factor."""
+    import torch
+
+    x = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read_per_copy": 1 << 30,
+                                           "bytes_written_per_copy": 1 << 30, "copies": 5}}))
+    return 0
 
 
 class Case:
@@ -221,6 +240,8 @@ def main(argv=None):
 
     import torch
 
+    if args.copy_calibration:
+        return copy_calibration()
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1

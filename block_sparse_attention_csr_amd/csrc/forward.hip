@@ -118,44 +118,62 @@ struct Tile<__bf16> {
     for (int c = 0; c < D / 16; ++c) q.r[c] = *reinterpret_cast<const u32x4_t*>(p + 16 * c);
   }
 
-  // S^T[key][query] over one 32-key step: the A operand (lane = key, half h)
-  // is K[key][16c + 8h .. +8], read straight from global memory.
+  // K operand of one 32-key step (lane = key, half h): K[key][16c + 8h .. +8],
+  // read straight from global memory into MFMA operand registers.
   template <int D>
-  static __device__ __forceinline__ f32x16_t scores(const QOperand<D>& q, const __bf16* Kstep,
-                                                    int lane) {
+  struct KRegs { u32x4_t r[D / 16]; };
+
+  template <int D>
+  static __device__ __forceinline__ void load_k(KRegs<D>& k, const __bf16* Kstep, int lane) {
     const __bf16* p = Kstep + (size_t)(lane & 31) * D + (lane >> 5) * 8;
-    u32x4_t kr[D / 16];
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) kr[c] = *reinterpret_cast<const u32x4_t*>(p + 16 * c);
+    for (int c = 0; c < D / 16; ++c) k.r[c] = *reinterpret_cast<const u32x4_t*>(p + 16 * c);
+  }
+
+  // S^T[key][query] = sum over features of K[key][f] Q[query][f].
+  template <int D>
+  static __device__ __forceinline__ f32x16_t scores(const QOperand<D>& q, const KRegs<D>& k) {
     f32x16_t s = {};
 #pragma unroll
     for (int c = 0; c < D / 16; ++c)
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kr[c]),
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, k.r[c]),
                                                   __builtin_bit_cast(bf16x8_t, q.r[c]), s, 0, 0,
                                                   0);
     return s;
   }
 
-  // Stage V[32 keys][D] transposed into vt[D][32 + pad].  Lane handles key
-  // pairs (2r, 2r+1) and 8-feature pieces; each 32-bit LDS word holds the
-  // same feature of two adjacent keys.
+  // V rows of one 32-key step in registers.  Lane handles key pairs
+  // (2r, 2r+1), r = lane % 16, and 8-feature pieces (lane / 16) + 4u.
   template <int D>
-  static __device__ __forceinline__ void stage_v(uint16_t* vt, const __bf16* Vstep, int lane) {
-    constexpr int kStride = kKeyStep + kVtPad;
-    constexpr int kUnits = (kKeyStep / 2) * (D / 8);  // (key pair, piece) units
+  struct VRegs { u32x4_t a[D / 32], b[D / 32]; };
+
+  template <int D>
+  static __device__ __forceinline__ void load_v(VRegs<D>& v, const __bf16* Vstep, int lane) {
     const int r = lane & 15;
 #pragma unroll
-    for (int u = 0; u < kUnits / kWave; ++u) {
+    for (int u = 0; u < D / 32; ++u) {
       const int piece = (lane >> 4) + 4 * u;
       const __bf16* src = Vstep + (size_t)(2 * r) * D + piece * 8;
-      const u32x4_t a = *reinterpret_cast<const u32x4_t*>(src);
-      const u32x4_t b = *reinterpret_cast<const u32x4_t*>(src + D);
+      v.a[u] = *reinterpret_cast<const u32x4_t*>(src);
+      v.b[u] = *reinterpret_cast<const u32x4_t*>(src + D);
+    }
+  }
+
+  // Store the step transposed into vt[D][32 + pad]: each 32-bit LDS word
+  // holds one feature of the two adjacent keys (2r, 2r+1).
+  template <int D>
+  static __device__ __forceinline__ void store_vt(uint16_t* vt, const VRegs<D>& v, int lane) {
+    constexpr int kStride = kKeyStep + kVtPad;
+    const int r = lane & 15;
+#pragma unroll
+    for (int u = 0; u < D / 32; ++u) {
+      const int piece = (lane >> 4) + 4 * u;
       uint16_t* dst = vt + (piece * 8) * kStride + 2 * r;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         // feature 2w: low halves of a[w], b[w]; feature 2w+1: high halves.
-        const uint32_t lo = __builtin_amdgcn_perm(b[w], a[w], 0x05040100u);
-        const uint32_t hi = __builtin_amdgcn_perm(b[w], a[w], 0x07060302u);
+        const uint32_t lo = __builtin_amdgcn_perm(v.b[u][w], v.a[u][w], 0x05040100u);
+        const uint32_t hi = __builtin_amdgcn_perm(v.b[u][w], v.a[u][w], 0x07060302u);
         *reinterpret_cast<uint32_t*>(dst + (2 * w) * kStride) = lo;
         *reinterpret_cast<uint32_t*>(dst + (2 * w + 1) * kStride) = hi;
       }
@@ -219,31 +237,50 @@ struct Tile<float> {
   }
 
   template <int D>
-  static __device__ __forceinline__ f32x16_t scores(const QOperand<D>& q, const float* Kstep,
-                                                    int lane) {
+  struct KRegs { f32x4_t r[D / 8]; };
+
+  // Lane (key, h) holds K[key][(D/2) h + c], c = 0 .. D/2-1.
+  template <int D>
+  static __device__ __forceinline__ void load_k(KRegs<D>& k, const float* Kstep, int lane) {
     const float* p = Kstep + (size_t)(lane & 31) * D + (lane >> 5) * (D / 2);
-    f32x16_t s = {};
 #pragma unroll
-    for (int c = 0; c < D / 8; ++c) {
-      const f32x4_t kr = *reinterpret_cast<const f32x4_t*>(p + 4 * c);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        s = __builtin_amdgcn_mfma_f32_32x32x2f32(kr[e], q.r[c][e], s, 0, 0, 0);
-    }
-    return s;
+    for (int c = 0; c < D / 8; ++c) k.r[c] = *reinterpret_cast<const f32x4_t*>(p + 4 * c);
   }
 
   template <int D>
-  static __device__ __forceinline__ void stage_v(float* vt, const float* Vstep, int lane) {
-    constexpr int kStride = kKeyStep + kVtPad;
-    constexpr int kUnits = kKeyStep * (D / 4);
+  static __device__ __forceinline__ f32x16_t scores(const QOperand<D>& q, const KRegs<D>& k) {
+    f32x16_t s = {};
+#pragma unroll
+    for (int c = 0; c < D / 8; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        s = __builtin_amdgcn_mfma_f32_32x32x2f32(k.r[c][e], q.r[c][e], s, 0, 0, 0);
+    return s;
+  }
+
+  // Lane handles key lane % 32 and 4-feature pieces (lane / 32) + 2u.
+  template <int D>
+  struct VRegs { f32x4_t a[D / 8]; };
+
+  template <int D>
+  static __device__ __forceinline__ void load_v(VRegs<D>& v, const float* Vstep, int lane) {
     const int key = lane & 31;
 #pragma unroll
-    for (int u = 0; u < kUnits / kWave; ++u) {
+    for (int u = 0; u < D / 8; ++u) {
       const int piece = (lane >> 5) + 2 * u;
-      const f32x4_t a = *reinterpret_cast<const f32x4_t*>(Vstep + (size_t)key * D + piece * 4);
+      v.a[u] = *reinterpret_cast<const f32x4_t*>(Vstep + (size_t)key * D + piece * 4);
+    }
+  }
+
+  template <int D>
+  static __device__ __forceinline__ void store_vt(float* vt, const VRegs<D>& v, int lane) {
+    constexpr int kStride = kKeyStep + kVtPad;
+    const int key = lane & 31;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) vt[(piece * 4 + e) * kStride + key] = a[e];
+    for (int u = 0; u < D / 8; ++u) {
+      const int piece = (lane >> 5) + 2 * u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vt[(piece * 4 + e) * kStride + key] = v.a[u][e];
     }
   }
 
@@ -304,7 +341,7 @@ __global__ __launch_bounds__(kWave * (BS / kQRows) * kMaxKeySplit) void bsa_fwd_
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int qg = wave % QW;
   const int ks = wave / QW;
   const int KS = p.key_split;
@@ -330,17 +367,48 @@ __global__ __launch_bounds__(kWave * (BS / kQRows) * kMaxKeySplit) void bsa_fwd_
   float lsum = 0.f;      // running sum over this lane half's keys
   const float c2 = p.scale_log2;
 
+  // This wave's blocks are CSR entries rs + ks, rs + ks + KS, ...; each block
+  // is BS / 32 steps of 32 keys.  Software pipeline: the K and V registers of
+  // step s+1 are loaded while step s computes, and col_idx is read two blocks
+  // ahead into scalar registers.
   const int rs = p.row_ptr[qb];
   const int re = p.row_ptr[qb + 1];
-  for (int t = rs + ks; t < re; t += KS) {
-    const int j = p.col_idx[t];
-    if (j < 0 || j >= p.M) continue;
+  const int nblk = (re - rs > ks) ? (re - rs - ks + KS - 1) / KS : 0;
+  auto block_col = [&](int b) -> int { return p.col_idx[rs + ks + KS * b]; };
+  auto key_of = [&](int j) -> int {  // first key row of block j, or -1 if out of range
+    return (j >= 0 && j < p.M) ? j * BS : -1;
+  };
+  typename Ops::template KRegs<D> kn;
+  typename Ops::template VRegs<D> vn;
+  int key_next = nblk > 0 ? key_of(block_col(0)) : -1;  // block b
+  int col_next2 = nblk > 1 ? block_col(1) : -1;         // block b + 1 (raw column)
+  if (nblk > 0) {
+    const size_t k0 = (size_t)(key_next < 0 ? 0 : key_next) * D;
+    Ops::template load_k<D>(kn, K + k0, lane);
+    Ops::template load_v<D>(vn, V + k0, lane);
+  }
+
+  for (int b = 0; b < nblk; ++b) {
+    const int key_cur = key_next;
+    key_next = key_of(col_next2);
+    col_next2 = (b + 2 < nblk) ? block_col(b + 2) : -1;
 #pragma unroll
     for (int st = 0; st < kSteps; ++st) {
-      const size_t key0 = (size_t)j * BS + st * kKeyStep;
+      const typename Ops::template KRegs<D> kc = kn;
+      const typename Ops::template VRegs<D> vc = vn;
+      // prefetch the next step: the rest of this block, else the next block
+      int pre = -1;
+      if (st + 1 < kSteps) pre = key_cur < 0 ? 0 : key_cur + (st + 1) * kKeyStep;
+      else if (b + 1 < nblk) pre = key_next < 0 ? 0 : key_next;
+      if (pre >= 0) {
+        Ops::template load_k<D>(kn, K + (size_t)pre * D, lane);
+        Ops::template load_v<D>(vn, V + (size_t)pre * D, lane);
+      }
+      if (key_cur < 0) continue;
+
+      f32x16_t s = Ops::template scores<D>(qop, kc);
       wave_lds_fence();
-      Ops::template stage_v<D>(vt, V + key0 * D, lane);
-      f32x16_t s = Ops::template scores<D>(qop, K + key0 * D, lane);
+      Ops::template store_vt<D>(vt, vc, lane);
 
       float mx = s[0];
 #pragma unroll
