@@ -79,6 +79,9 @@ def _load():
     lib.bsa_forward.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, i64,
                                 ctypes.c_float, vp]
     lib.bsa_forward.restype = i32
+    lib.bsa_forward_ex.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp,
+                                   i64, ctypes.c_float, i32, i32, vp]
+    lib.bsa_forward_ex.restype = i32
     lib.bsa_status_string.argtypes = [i32]
     lib.bsa_status_string.restype = ctypes.c_char_p
     lib.bsa_abi_version.argtypes = []
@@ -158,7 +161,8 @@ def _dtype_code(t):
 
 
 def forward(q, k, v, row_ptr, col_idx, block_size: int, scale: float | None = None, *,
-            out=None, lse=None, nnz: int | None = None, stream=None):
+            out=None, lse=None, nnz: int | None = None, stream=None, group: int = 0,
+            key_split: int = 0):
     """Block-sparse attention forward on the GPU.
 
     q, k, v: CUDA tensors [B, H, N, d] (bfloat16 or float32), contiguous.
@@ -166,7 +170,8 @@ def forward(q, k, v, row_ptr, col_idx, block_size: int, scale: float | None = No
     Returns (o [B, H, N, d] same dtype, lse [B, H, N] float32).  The launch is
     enqueued on the current stream (or ``stream``) and not synchronised.
     ``nnz`` (host int) avoids reading row_ptr back; by default it is
-    col_idx.numel().
+    col_idx.numel().  ``group`` / ``key_split`` force a workgroup shape
+    (bsa_forward_ex); 0 / 0 lets the library choose.
     """
     import torch
 
@@ -192,10 +197,14 @@ def forward(q, k, v, row_ptr, col_idx, block_size: int, scale: float | None = No
         nnz = col_idx.numel()
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    st = _load().bsa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                             lse.data_ptr(), B, H, N, d, int(block_size), _dtype_code(q),
-                             row_ptr.data_ptr(), col_idx.data_ptr(), int(nnz),
-                             0.0 if scale is None else float(scale), stream.cuda_stream)
+    lib = _load()
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N,
+            d, int(block_size), _dtype_code(q), row_ptr.data_ptr(), col_idx.data_ptr(),
+            int(nnz), 0.0 if scale is None else float(scale))
+    if group or key_split:
+        st = lib.bsa_forward_ex(*args, int(group), int(key_split), stream.cuda_stream)
+    else:
+        st = lib.bsa_forward(*args, stream.cuda_stream)
     if st != BSA_OK:
         raise BsaError(st, "bsa_forward")
     return out, lse

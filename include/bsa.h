@@ -137,6 +137,25 @@ bsa_status bsa_forward(const void* q, const void* k, const void* v, void* o, flo
                        int32_t block_size, int32_t dtype, const int32_t* row_ptr,
                        const int32_t* col_idx, int64_t nnz, float scale, void* stream);
 
+/*
+ * bsa_forward_ex -- bsa_forward with an explicit workgroup shape.
+ *
+ * Same computation, arguments and errors as bsa_forward, plus:
+ * group      query blocks sharing one workgroup's K/V tiles: 1, 2 or 4;
+ * key_split  wave sets that split each query block's CSR row (>= 1), merged
+ *            through LDS before the store;
+ * group == key_split == 0 selects the shape bsa_forward would use.  A shape
+ * needing more than 8 waves (block_size / 32 * group * key_split) or more
+ * LDS than a workgroup may use returns BSA_ERR_INVALID_ARGUMENT.  Every shape
+ * computes the same result up to floating-point summation order; this entry
+ * point exists to tune and to test the shapes.
+ */
+bsa_status bsa_forward_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int32_t batch, int32_t heads, int32_t seq_len, int32_t head_dim,
+                          int32_t block_size, int32_t dtype, const int32_t* row_ptr,
+                          const int32_t* col_idx, int64_t nnz, float scale, int32_t group,
+                          int32_t key_split, void* stream);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* bsa_status_string(int32_t status);
 

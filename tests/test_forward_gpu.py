@@ -226,3 +226,32 @@ def test_nan_propagates_only_to_rows_that_see_it():
             assert np.isnan(rows).all(), qb
         else:
             assert np.isfinite(rows).all(), qb
+
+
+SHAPES = [(1, 1), (1, 2), (1, 4), (1, 8), (2, 1), (2, 2), (2, 4), (4, 1), (4, 2)]
+
+
+@pytest.mark.parametrize("group,key_split", SHAPES)
+@pytest.mark.parametrize("dt,bs,d", [(dt, bs, d) for dt in ("bf16", "f32") for bs in (32, 64)
+                                     for d in (64, 128)])
+def test_every_workgroup_shape(dt, bs, d, group, key_split):
+    """bsa_forward_ex: every (group, key_split) computes the oracle's result,
+    on a ragged case (M = 11 query blocks is a multiple of no group size)."""
+    if (bs // 32) * group * key_split > 8:
+        pytest.skip("more than 8 waves per workgroup")
+    dtype = torch.bfloat16 if dt == "bf16" else torch.float32
+    B, H, M = 2, 3, 11
+    N = bs * M
+    q, k, v = make_qkv(B, H, N, d, dtype, 17)
+    mask = random_block_mask(M, 0.35, 17)
+    dev = torch.device("cuda")
+    rp, ci = bsa.build_pattern(N, bs, mask=mask)
+    try:
+        o, lse = bsa.forward(q.to(dev), k.to(dev), v.to(dev), rp.to(dev), ci.to(dev), bs,
+                             group=group, key_split=key_split)
+    except bsa.BsaError as e:
+        assert e.status == 2
+        pytest.skip(f"shape needs more LDS than a workgroup has: {e}")
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.block_sparse_attention(_f64(q), _f64(k), _f64(v), mask, bs)
+    _compare(_f64(o), _f64(lse), o_ref, lse_ref, dtype, f"{dt} bs{bs} d{d} G{group} KS{key_split}")
