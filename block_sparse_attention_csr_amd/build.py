@@ -26,7 +26,9 @@ CXX = os.environ.get("CXX", "g++")
 
 # Packed fp32 VALU instructions are switched off for all device code.
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
-             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             # MFMA accumulators in ordinary VGPRs: no AGPR copies around each block
+             "-mllvm", "-amdgpu-mfma-vgpr-form=1", "-Wno-inline-asm"]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
 
 

@@ -82,7 +82,6 @@ struct FwdParams {
   int32_t num_wg;     // batch * heads * ceil(M / group)
   int32_t group;      // G: query blocks per workgroup
   int32_t key_split;  // KS: key-slice wave sets per workgroup
-  int32_t nbuf;       // LDS entry buffers per key slice (1 or 2)
   float scale_log2;   // scale * log2(e)
 };
 
@@ -132,40 +131,23 @@ struct TileLayout {
   static constexpr int kEntryBytes = 2 * kTileBytes;  // K tile then V tile
   static constexpr int kCopies = kEntryBytes / (kWave * 16);  // 1 KB parts per entry
 
-  static __device__ __forceinline__ int swz(int r) { return (r >> 1) & (kChunksPerRow - 1); }
-  static __device__ __forceinline__ int chunk_offset(int r, int c) {
-    return r * kRowBytes + ((c ^ swz(r)) << 4);
-  }
-};
-
-// Register staging of one entry (K tile then V tile of key block `key0`).
-// The entry is cut into 1 KB parts; part c is staged by wave (c % SW) of the
-// key slice, lane i holding the 16-byte chunk that LDS slot 64 c + i gets
-// under the swizzle.
-template <typename T, int BS, int D, int SW>
-struct Stage {
-  using L = TileLayout<T, BS, D>;
-  static_assert(L::kCopies % SW == 0, "entry parts must split evenly over the slice waves");
-  static constexpr int kParts = L::kCopies / SW;  // parts per wave
-  u32x4_t r[kParts];
-
-  __device__ __forceinline__ void load(const T* K, const T* V, int key0, int ws, int lane) {
-    constexpr int kSlotsPerTile = L::kTileBytes / 16;
-#pragma unroll
-    for (int c = 0; c < kParts; ++c) {
-      const int slot = (ws + c * SW) * kWave + lane;
-      const bool is_v = slot >= kSlotsPerTile;
-      const int s = is_v ? slot - kSlotsPerTile : slot;
-      const int row = s / L::kChunksPerRow;
-      const int chunk = (s % L::kChunksPerRow) ^ L::swz(row);
-      const T* src = (is_v ? V : K) + (size_t)(key0 + row) * D + chunk * (16 / (int)sizeof(T));
-      r[c] = *reinterpret_cast<const u32x4_t*>(src);
+  // XOR key of row r: a bit-reversed row index, chosen so that (a) 16 rows
+  // read at the same chunk hit 16 different 16-byte bank groups and (b) the
+  // transpose reads (4 consecutive rows x 4 consecutive chunks) do too.  It
+  // depends on r mod 16 only, so per-lane offsets computed for rows 0..15
+  // hold for every row at a multiple of 16 further on.
+  static __device__ __forceinline__ int swz(int r) {
+    if constexpr (kChunksPerRow == 8) {  // 128-byte rows: two rows per 256-byte bank line
+      const int t = (r >> 1) & 7;
+      return ((t & 1) << 2) | (t & 2) | ((t >> 2) & 1);
+    } else {
+      const int t = r & 15;
+      const int rev = ((t & 1) << 3) | ((t & 2) << 1) | ((t & 4) >> 1) | ((t & 8) >> 3);
+      return rev & (kChunksPerRow - 1);
     }
   }
-  __device__ __forceinline__ void store(unsigned char* entry, int ws, int lane) const {
-#pragma unroll
-    for (int c = 0; c < kParts; ++c)
-      *reinterpret_cast<u32x4_t*>(entry + ((ws + c * SW) * kWave + lane) * 16) = r[c];
+  static __device__ __forceinline__ int chunk_offset(int r, int c) {
+    return r * kRowBytes + ((c ^ swz(r)) << 4);
   }
 };
 
@@ -186,19 +168,47 @@ struct Ops<__bf16> {
     for (int c = 0; c < D / 16; ++c) q.r[c] = *reinterpret_cast<const u32x4_t*>(p + 16 * c);
   }
 
-  // S^T for 32-key step st: A operand (lane = key, half h) = K[key][16c + 8h .. +8].
+  // Per-lane LDS byte offsets of the operand reads, relative to the LDS base
+  // of the slice's buffer 0 (plus that base).  Valid for every 32-key step
+  // and 16-key sub-step: those move by multiples of 16 rows.
+  template <int BS, int D>
+  struct Offsets {
+    int k[D / 16];     // K chunk 2c + h of key row lane % 32
+    int v[2][D / 32];  // transpose-read address, rows +0 / +8, feature tile dt
+    __device__ __forceinline__ void init(int lane, int base) {
+      using L = TileLayout<__bf16, BS, D>;
+      const int h = lane >> 5;
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) k[c] = base + L::chunk_offset(lane & 31, 2 * c + h);
+      // In each 16-lane group, lane 4k + q addresses the 4 features
+      // (feature0 + 4q ..) of key row k; the hardware returns to lane i
+      // feature0 + i of rows k = 0..3.
+      const int g4 = lane >> 4;
+      const int i = lane & 15;
+      const int row = 4 * (g4 >> 1) + (i >> 2);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const int feature = dt * 32 + 16 * (g4 & 1) + 4 * (i & 3);
+        const int half = (feature & 7) * 2;
+        v[0][dt] = base + L::kTileBytes + L::chunk_offset(row, feature >> 3) + half;
+        v[1][dt] = base + L::kTileBytes + L::chunk_offset(row + 8, feature >> 3) + half;
+      }
+    }
+  };
+
+  // S^T for 32-key step st of the entry at byte `entry` (a constant) past
+  // the offsets' base: A operand (lane = key, half h) = K[key][16c + 8h .. +8].
   template <int BS, int D>
   static __device__ __forceinline__ f32x16_t scores(const QOperand<D>& q,
-                                                    const unsigned char* ktile, int st,
-                                                    int lane) {
+                                                    const Offsets<BS, D>& off,
+                                                    LDS_PTR(unsigned char) lds, int entry,
+                                                    int st) {
     using L = TileLayout<__bf16, BS, D>;
-    const int key = st * kKeyStep + (lane & 31);
-    const int h = lane >> 5;
     f32x16_t s = {};
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
-      const u32x4_t k =
-          *reinterpret_cast<const u32x4_t*>(ktile + L::chunk_offset(key, 2 * c + h));
+      const u32x4_t k = *(LDS_PTR(const u32x4_t))(lds + off.k[c] + entry +
+                                                  st * kKeyStep * L::kRowBytes);
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, k),
                                                   __builtin_bit_cast(bf16x8_t, q.r[c]), s, 0, 0,
                                                   0);
@@ -208,27 +218,20 @@ struct Ops<__bf16> {
 
   // V^T operand of step st, 16-key sub-step sc, feature tile dt: lane
   // (feature = 32 dt + lane % 32, half h) holds V[key][feature] for keys
-  // kappa(h, j) = 32 st + 16 sc + 8 (j / 4) + 4 h + j % 4, j = 0..7, read with
-  // two transpose loads.  In each 16-lane group, lane 4k + q addresses the 4
-  // features (feature0 + 4q ..) of key row k; the hardware returns to lane i
-  // feature0 + i of rows k = 0..3.
+  // kappa(h, j) = 32 st + 16 sc + 8 (j / 4) + 4 h + j % 4, j = 0..7: two
+  // transpose loads, rows +0 and +8.
   template <int BS, int D>
-  static __device__ __forceinline__ u32x4_t v_operand(const unsigned char* vtile, int st, int sc,
-                                                      int dt, int lane) {
+  static __device__ __forceinline__ u32x4_t v_operand(const Offsets<BS, D>& off,
+                                                      LDS_PTR(unsigned char) lds, int entry,
+                                                      int st, int sc, int dt) {
     using L = TileLayout<__bf16, BS, D>;
-    const int g4 = lane >> 4;
-    const int h = g4 >> 1;
-    const int i = lane & 15;
-    const int row = st * kKeyStep + 16 * sc + 4 * h + (i >> 2);
-    const int feature = dt * 32 + 16 * (g4 & 1) + 4 * (i & 3);
-    const int chunk = feature >> 3;
-    const int half = (feature & 7) * 2;
+    const int rows = (st * kKeyStep + 16 * sc) * L::kRowBytes;
     const u32x2_t lo = __builtin_bit_cast(
         u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                     (LDS_PTR(s16x4_t))(vtile + L::chunk_offset(row, chunk) + half)));
+                     (LDS_PTR(s16x4_t))(lds + off.v[0][dt] + entry + rows)));
     const u32x2_t hi = __builtin_bit_cast(
         u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                     (LDS_PTR(s16x4_t))(vtile + L::chunk_offset(row + 8, chunk) + half)));
+                     (LDS_PTR(s16x4_t))(lds + off.v[1][dt] + entry + rows)));
     return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
   }
 
@@ -236,7 +239,8 @@ struct Ops<__bf16> {
   template <int BS, int D>
   static __device__ __forceinline__ float accumulate(f32x16_t (&o)[D / 32],
                                                      const f32x16_t (&p)[BS / kKeyStep],
-                                                     const unsigned char* vtile, int lane) {
+                                                     const Offsets<BS, D>& off,
+                                                     LDS_PTR(unsigned char) lds, int entry) {
     float sum = 0.f;
     const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
@@ -256,7 +260,7 @@ struct Ops<__bf16> {
         const u32x4_t pb = {w4[0], w4[1], w4[2], w4[3]};
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
-          const u32x4_t va = v_operand<BS, D>(vtile, st, sc, dt, lane);
+          const u32x4_t va = v_operand<BS, D>(off, lds, entry, st, sc, dt);
           o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, va),
                                                           __builtin_bit_cast(bf16x8_t, pb),
                                                           o[dt], 0, 0, 0);
@@ -290,17 +294,28 @@ struct Ops<float> {
   }
 
   template <int BS, int D>
+  struct Offsets {
+    int lane;
+    int base;
+    __device__ __forceinline__ void init(int l, int b) {
+      lane = l;
+      base = b;
+    }
+  };
+
+  template <int BS, int D>
   static __device__ __forceinline__ f32x16_t scores(const QOperand<D>& q,
-                                                    const unsigned char* ktile, int st,
-                                                    int lane) {
+                                                    const Offsets<BS, D>& off,
+                                                    LDS_PTR(unsigned char) lds, int entry,
+                                                    int st) {
     using L = TileLayout<float, BS, D>;
-    const int key = st * kKeyStep + (lane & 31);
-    const int h = lane >> 5;
+    const int key = st * kKeyStep + (off.lane & 31);
+    const int h = off.lane >> 5;
     f32x16_t s = {};
 #pragma unroll
     for (int c = 0; c < D / 8; ++c) {
-      const f32x4_t k =
-          *reinterpret_cast<const f32x4_t*>(ktile + L::chunk_offset(key, (D / 8) * h + c));
+      const f32x4_t k = *(LDS_PTR(const f32x4_t))(lds + off.base + entry +
+                                                   L::chunk_offset(key, (D / 8) * h + c));
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         s = __builtin_amdgcn_mfma_f32_32x32x2f32(k[e], q.r[c][e], s, 0, 0, 0);
@@ -313,9 +328,10 @@ struct Ops<float> {
   template <int BS, int D>
   static __device__ __forceinline__ float accumulate(f32x16_t (&o)[D / 32],
                                                      const f32x16_t (&p)[BS / kKeyStep],
-                                                     const unsigned char* vtile, int lane) {
+                                                     const Offsets<BS, D>& off,
+                                                     LDS_PTR(unsigned char) lds, int entry) {
     using L = TileLayout<float, BS, D>;
-    const int h = lane >> 5;
+    const int h = off.lane >> 5;
     float sum = 0.f;
 #pragma unroll
     for (int st = 0; st < BS / kKeyStep; ++st) {
@@ -323,12 +339,13 @@ struct Ops<float> {
       for (int i = 0; i < 16; ++i) sum += p[st][i];
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const int feature = dt * 32 + (lane & 31);
+        const int feature = dt * 32 + (off.lane & 31);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int row = st * kKeyStep + 8 * (i / 4) + 4 * h + (i % 4);
-          const float va = *reinterpret_cast<const float*>(
-              vtile + L::chunk_offset(row, feature >> 2) + (feature & 3) * 4);
+          const float va = *(LDS_PTR(const float))(lds + off.base + entry + L::kTileBytes +
+                                                   L::chunk_offset(row, feature >> 2) +
+                                                   (feature & 3) * 4);
           o[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(va, p[st][i], o[dt], 0, 0, 0);
         }
       }
@@ -350,50 +367,79 @@ constexpr int partial_bytes() {
   return (D / 32) * 16 * kWave * 4 + 2 * kWave * 4;
 }
 
-template <typename T, int BS, int D>
-size_t lds_bytes(int group, int key_split, int nbuf, int M) {
+// Compile-time shape of one kernel instantiation.
+template <typename T, int BS, int D, int G, int KS>
+struct Cfg {
   using L = TileLayout<T, BS, D>;
-  constexpr int QW = BS / kQRows;
-  const size_t tiles = (size_t)nbuf * key_split * L::kEntryBytes;
-  const size_t merge = (size_t)QW * group * (key_split - 1) * partial_bytes<D>();
-  const size_t words = (size_t)(group + 1) * ((M + 31) / 32);
-  return (tiles > merge ? tiles : merge) + 4 * words;
-}
-
-// Iterator over the set bits of the union bitmap, in ascending block order.
-struct BitIter {
-  const uint32_t* words;
-  int nwords;
-  int w;
-  uint32_t bits;
-  __device__ __forceinline__ int next() {
-    while (bits == 0) {
-      if (++w >= nwords) return -1;
-      bits = (uint32_t)uniform((int)words[w]);
-    }
-    const int j = w * 32 + __builtin_ctz(bits);
-    bits &= bits - 1;
-    return j;
-  }
+  static constexpr int QW = BS / kQRows;  // query waves per query block
+  static constexpr int SW = QW * G;       // waves per key slice
+  static constexpr int W = SW * KS;       // waves per workgroup
+  static constexpr int kEntry = L::kEntryBytes;
+  static constexpr int kSliceBytes = KS * kEntry;  // one buffer for every slice
+  static_assert(L::kCopies % SW == 0, "entry parts must split evenly over a slice's waves");
+  static constexpr int kParts = L::kCopies / SW;  // 1 KB copies per wave per entry
+  // Three tile buffers (prefetch distance 2) while they leave room for three
+  // workgroups per CU, else two (prefetch distance 1).
+  static constexpr int NB = 3 * kSliceBytes <= 48 * 1024 ? 3 : 2;
+  // Shapes whose buffers do not fit a workgroup's LDS are not instantiated.
+  static constexpr bool kValid = NB * kSliceBytes + 1024 <= 160 * 1024 &&
+                                 (KS - 1) * SW * partial_bytes<D>() <= kSliceBytes;
 };
 
-template <typename T, int BS, int D, int G>
-__global__ __launch_bounds__(kWave* kMaxWaves) void bsa_fwd_kernel(FwdParams p) {
-  using L = TileLayout<T, BS, D>;
+// s_waitcnt: vector-memory count <= n and LDS/scalar count == 0.
+template <int n>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  // gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]
+  __builtin_amdgcn_s_waitcnt((n & 0xF) | (0x7 << 4) | (0x0 << 8) | ((n >> 4) << 14));
+}
+
+// Direct-to-LDS copy of 16 bytes per lane: lane i reads sbase + voff (its
+// own offset) and the data lands at LDS byte address m0 + 16 i.  Written as
+// asm so that the compiler does not add waits for these copies in front of
+// LDS reads of other buffers; the kernel waits for them itself (s_waitcnt
+// vmcnt before the barrier that publishes a buffer).  The asm has no register
+// outputs.  It sets M0, which nothing else in these kernels uses.
+__device__ __forceinline__ void lds_dma16(const void* sbase, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(m0)
+               : "memory", "m0");
+}
+
+// Workgroup barrier without a memory fence: the caller has already waited for
+// the memory operations the barrier publishes.  The empty asm statements keep
+// the compiler from moving memory accesses across it.
+__device__ __forceinline__ void raw_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <typename T, int BS, int D, int G, int KS>
+__global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_kernel(FwdParams p) {
+  using C = Cfg<T, BS, D, G, KS>;
+  using L = typename C::L;
   using O = Ops<T>;
-  constexpr int QW = BS / kQRows;
+  constexpr int QW = C::QW;
+  constexpr int SW = C::SW;
+  constexpr int NB = C::NB;
   constexpr int KSTEPS = BS / kKeyStep;
-  constexpr int SW = QW * G;  // waves per key slice
-  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+
+  // K/V tile buffers: separate LDS objects so that the compiler can tell a
+  // copy in flight into one buffer from the reads of another.
+  __shared__ __attribute__((aligned(16))) unsigned char buf0[C::kSliceBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char buf1[C::kSliceBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char buf2[NB == 3 ? C::kSliceBytes : 16];
+  extern __shared__ __attribute__((aligned(16))) int32_t dyn[];  // entry list | bitmaps
+  __shared__ int32_t union_size;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = uniform(threadIdx.x / kWave);
-  const int KS = p.key_split;
-  const int qg = wave % QW;          // 32-row query group within the block
-  const int g = (wave / QW) % G;     // query block within the workgroup
-  const int ks = wave / SW;          // key slice
-  const int slice_waves = SW;
-  const int ws = wave % SW;          // wave index within its key slice
+  const int qg = wave % QW;        // 32-row query group within the block
+  const int g = (wave / QW) % G;   // query block within the workgroup
+  const int ks = wave / SW;        // key slice
+  const int ws = wave % SW;        // wave index within its key slice
 
   const int M = p.M;
   const int ngroups = (M + G - 1) / G;
@@ -407,124 +453,184 @@ __global__ __launch_bounds__(kWave* kMaxWaves) void bsa_fwd_kernel(FwdParams p) 
   const T* K = static_cast<const T*>(p.k) + head;
   const T* V = static_cast<const T*>(p.v) + head;
 
-  // ---- LDS: tile buffers [KS][kNumBuf][entry] | union bitmap | row bitmaps [G]
-  const int MW = (M + 31) / 32;
-  const int NB = p.nbuf;
-  size_t tiles = (size_t)NB * KS * L::kEntryBytes;
-  const size_t merge = (size_t)slice_waves * (KS - 1) * partial_bytes<D>();
-  if (merge > tiles) tiles = merge;
-  uint32_t* bitmap = reinterpret_cast<uint32_t*>(lds + tiles);
-  for (int i = threadIdx.x; i < (G + 1) * MW; i += blockDim.x) bitmap[i] = 0;
-  __syncthreads();
-  if (has_rows && qg == 0 && ks == 0) {
-    const int rs = p.row_ptr[qb];
-    const int re = p.row_ptr[qb + 1];
-    for (int t = rs + lane; t < re; t += kWave) {
-      const int j = p.col_idx[t];
-      if (j >= 0 && j < M) {
-        atomicOr(&bitmap[j >> 5], 1u << (j & 31));
-        atomicOr(&bitmap[(1 + g) * MW + (j >> 5)], 1u << (j & 31));
-      }
-    }
-  }
-
-  // Q operand in registers while the bitmaps settle.
   typename O::template QOperand<D> qop;
   const int q0 = (has_rows ? qb : 0) * BS + qg * kQRows;
   O::template load_q<D>(qop, Q + (size_t)q0 * D, lane);
-  __syncthreads();
 
-  int U = 0;  // union size
-  for (int w = lane; w < MW; w += kWave) U += __builtin_popcount(bitmap[w]);
-  for (int off = 32; off > 0; off >>= 1) U += __shfl_xor(U, off);
-  U = uniform(U);
-  const int niter = (U + KS - 1) / KS;  // same trip count for every wave
-
-  // This slice's entries are union entries ks, ks + KS, ...
-  BitIter it{bitmap, MW, -1, 0};
-  auto next_entry = [&]() -> int {  // next column of this slice, or -1
-    int j = -1;
-    for (int s = 0; s < KS; ++s) {
-      const int x = it.next();
-      if (s == ks) j = x;
+  // ---- entry list: the workgroup's CSR row (G == 1) or the sorted union of
+  // its G rows (G > 1), in LDS; per-row bitmaps say which entries a wave uses.
+  const int MW = (M + 31) / 32;
+  int32_t* list = dyn;                                        // [M]
+  uint32_t* bitmap = reinterpret_cast<uint32_t*>(dyn + M);    // [(G + 1) * MW] (G > 1)
+  const uint32_t* my_row = bitmap + (1 + g) * MW;
+  int U;
+  if constexpr (G == 1) {
+    const int rs = p.row_ptr[grp];
+    const int re = p.row_ptr[grp + 1];
+    U = re - rs;
+    if (wave == 0)
+      for (int t = lane; t < U; t += kWave) list[t] = p.col_idx[rs + t];
+    __syncthreads();
+  } else {
+    for (int i = threadIdx.x; i < (G + 1) * MW; i += blockDim.x) bitmap[i] = 0;
+    __syncthreads();
+    if (has_rows && qg == 0 && ks == 0) {
+      const int rs = p.row_ptr[qb];
+      const int re = p.row_ptr[qb + 1];
+      for (int t = rs + lane; t < re; t += kWave) {
+        const int j = p.col_idx[t];
+        if (j >= 0 && j < M) {
+          atomicOr(&bitmap[j >> 5], 1u << (j & 31));
+          atomicOr(&bitmap[(1 + g) * MW + (j >> 5)], 1u << (j & 31));
+        }
+      }
     }
-    return j;
+    __syncthreads();
+    if (wave == 0) {  // ascending list of the union's blocks
+      int base = 0;
+      for (int w0 = 0; w0 < MW; w0 += kWave) {
+        const int w = w0 + lane;
+        uint32_t bits = w < MW ? bitmap[w] : 0u;
+        const int cnt = __builtin_popcount(bits);
+        int incl = cnt;
+        for (int off = 1; off < kWave; off <<= 1) {
+          const int t = __shfl_up(incl, off);
+          if (lane >= off) incl += t;
+        }
+        int pos = base + incl - cnt;
+        while (bits != 0u) {
+          list[pos++] = w * 32 + __builtin_ctz(bits);
+          bits &= bits - 1;
+        }
+        base += __shfl(incl, kWave - 1);
+      }
+      if (lane == 0) union_size = base;
+    }
+    __syncthreads();
+    U = uniform(union_size);
+  }
+  // Slice ks takes list entries ks, ks + KS, ...; every wave runs niter steps.
+  const int niter = (U + KS - 1) / KS;
+  auto entry_block = [&](int i) -> int {  // block of this slice's step i, or -1
+    const int t = i * KS + ks;
+    return t < U ? uniform(list[t]) : -1;
   };
-  unsigned char* slice_buf = lds + (size_t)ks * NB * L::kEntryBytes;
-  Stage<T, BS, D, SW> stage;
-  auto stage_load = [&](int j) {  // a missing entry stages block 0 (never used)
-    stage.load(K, V, (j < 0 ? 0 : j) * BS, ws, lane);
+  auto selected = [&](int j) -> bool {
+    if (j < 0 || j >= M || !has_rows) return false;
+    if constexpr (G == 1) return true;
+    return ((((uint32_t)uniform((int)my_row[j >> 5])) >> (j & 31)) & 1u) != 0;
   };
+
+  // ---- direct-to-LDS copies.  Part c of this wave is part ws + c*SW of the
+  // entry (1 KB: slots 64 (ws + c SW) .. +64); lane i fetches the 16-byte
+  // global chunk the swizzle places in its slot.
+  constexpr int kPartsPerTile = L::kCopies / 2;
+  int dma_off[C::kParts];
+#pragma unroll
+  for (int c = 0; c < C::kParts; ++c) {
+    const int part = (ws + c * SW) % kPartsPerTile;
+    const int slot = part * kWave + lane;
+    const int row = slot / L::kChunksPerRow;
+    const int chunk = (slot % L::kChunksPerRow) ^ L::swz(row);
+    dma_off[c] = row * L::kRowBytes + chunk * 16;
+  }
+  auto issue = [&](int j, unsigned char* buf) {
+    const int key0 = (j < 0 || j >= M ? 0 : j) * BS;  // a missing entry copies block 0 (unused)
+    const uint32_t dst = (uint32_t)(uintptr_t)(LDS_PTR(unsigned char))buf + ks * C::kEntry;
+#pragma unroll
+    for (int c = 0; c < C::kParts; ++c) {
+      const int part = ws + c * SW;
+      const T* base = (part < kPartsPerTile ? K : V) + (size_t)key0 * D;
+      lds_dma16(base, (uint32_t)dma_off[c], dst + part * kWave * 16);
+    }
+  };
+
+  typename O::template Offsets<BS, D> off;
+  off.init(lane, ks * C::kEntry);
 
   f32x16_t o[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16_t{};
   float m2 = -INFINITY;  // exponent offset (log2 domain) for this lane's query
   float lsum = 0.f;      // sum of exponentials over this lane half's keys
+  bool first = true;     // no block computed yet by this wave
   const float c2 = p.scale_log2;
-  const uint32_t* my_row = bitmap + (1 + g) * MW;
-  // Pipeline (two buffers): entry i computes from LDS buffer i % 2 while
-  // entry i+1 goes registers -> LDS buffer (i+1) % 2 and entry i+2 goes
-  // global -> registers.  With one buffer, entry i+1 is written to LDS after a
-  // second barrier that ends entry i's reads.
-  int j_cur = next_entry();
-  int j_next = next_entry();
-  stage_load(j_cur);
-  stage.store(slice_buf, ws, lane);
-  if (niter > 1) stage_load(j_next);
-  auto advance = [&](int i, unsigned char* dst) {
-    if (i + 1 < niter) stage.store(dst, ws, lane);
-    j_cur = j_next;
-    j_next = next_entry();
-    if (i + 2 < niter) stage_load(j_next);
-  };
-  for (int i = 0; i < niter; ++i) {
-    const int j = j_cur;
-    __syncthreads();  // entry i is in LDS; with two buffers nobody reads entry i-1 any more
-    if (NB == 2) advance(i, slice_buf + ((i + 1) & 1) * L::kEntryBytes);
-    const bool mine = j >= 0 && has_rows &&
-                      ((((uint32_t)uniform((int)my_row[j >> 5])) >> (j & 31)) & 1u) != 0;
-    if (mine) {
-      const unsigned char* ktile = slice_buf + (NB == 2 ? (i & 1) : 0) * L::kEntryBytes;
-      const unsigned char* vtile = ktile + L::kTileBytes;
-      f32x16_t s[KSTEPS];
-#pragma unroll
-      for (int st = 0; st < KSTEPS; ++st)
-        s[st] = O::template scores<BS, D>(qop, ktile, st, lane);
 
-      float mx = s[0][0];
+  auto compute = [&](unsigned char* buf) {
+    LDS_PTR(unsigned char) tile = (LDS_PTR(unsigned char))buf;
+    f32x16_t sc[KSTEPS];
 #pragma unroll
-      for (int st = 0; st < KSTEPS; ++st)
+    for (int st = 0; st < KSTEPS; ++st) sc[st] = O::template scores<BS, D>(qop, off, tile, 0, st);
+    float mx = sc[0][0];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[st][r]);
-      mx = halves_max(mx) * c2;
-      if (__builtin_amdgcn_ballot_w64(mx > m2 + kLazyRescale) != 0) {
-        const float m_new = fmaxf(m2, mx);
-        const float alpha = fast_exp2(m2 - m_new);
-        m2 = m_new;
-        lsum *= alpha;
+    for (int st = 0; st < KSTEPS; ++st)
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
-      }
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[st][r]);
+    mx = halves_max(mx) * c2;
+    if (first) {  // O and l are still zero: no rescale
+      m2 = mx;
+      first = false;
+    } else if (__builtin_amdgcn_ballot_w64(mx > m2 + kLazyRescale) != 0) {
+      const float m_new = fmaxf(m2, mx);
+      const float alpha = fast_exp2(m2 - m_new);
+      m2 = m_new;
+      lsum *= alpha;
 #pragma unroll
-      for (int st = 0; st < KSTEPS; ++st)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[st][r] = fast_exp2(fmaf(s[st][r], c2, -m2));
-      lsum += O::template accumulate<BS, D>(o, s, vtile, lane);
+      for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
     }
-    if (NB == 1) {
-      __syncthreads();  // entry i is no longer read
-      advance(i, slice_buf);
-    }
+#pragma unroll
+    for (int st = 0; st < KSTEPS; ++st)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[st][r] = fast_exp2(fmaf(sc[st][r], c2, -m2));
+    lsum += O::template accumulate<BS, D>(o, sc, off, tile, 0);
+  };
+
+  // ---- pipeline: entry i computes from buffer i % NB while the copies of
+  // entries up to i + NB - 1 are in flight.  Before the barrier that starts
+  // entry i each wave waits for its own copies of entry i (the later entries'
+  // copies may stay in flight) and for its LDS reads of entry i-1; after it,
+  // every wave's copies of entry i have landed and buffer (i-1) % NB is free.
+  int jq[NB];  // blocks of steps i .. i + NB - 1
+#pragma unroll
+  for (int e = 0; e < NB; ++e) jq[e] = entry_block(e);
+  // The Q loads were issued long ago; waiting for them here, before the first
+  // copy, tells the compiler they are complete (it does not see the copies
+  // and would otherwise wait on the vector-memory counter inside the loop).
+  wait_vm_lgkm0<0>();
+  issue(jq[0], buf0);
+  if (NB == 3) issue(jq[1], buf1);
+  auto buffer = [&](auto b_c) -> unsigned char* {
+    constexpr int b = decltype(b_c)::value;
+    if constexpr (b == 0) return buf0;
+    else if constexpr (b == 1) return buf1;
+    else return buf2;
+  };
+  auto step = [&](int i, auto b_c) {
+    constexpr int b = decltype(b_c)::value;
+    if (NB == 3 && i + 1 < niter) wait_vm_lgkm0<C::kParts>();
+    else wait_vm_lgkm0<0>();
+    raw_barrier();
+    const int j = jq[0];
+#pragma unroll
+    for (int e = 0; e + 1 < NB; ++e) jq[e] = jq[e + 1];
+    jq[NB - 1] = entry_block(i + NB);
+    if (i + NB - 1 < niter) issue(jq[NB - 2], buffer(std::integral_constant<int, (b + NB - 1) % NB>{}));
+    if (selected(j)) compute(buffer(b_c));
+  };
+  for (int i = 0; i < niter; i += NB) {
+    step(i, std::integral_constant<int, 0>{});
+    if (i + 1 < niter) step(i + 1, std::integral_constant<int, 1>{});
+    if constexpr (NB == 3)
+      if (i + 2 < niter) step(i + 2, std::integral_constant<int, 2>{});
   }
 
   // ---- merge the key slices: slices 1..KS-1 publish (O, m, l); slice 0 merges
-  if (KS > 1) {
-    __syncthreads();  // tile buffers are free
-    float* part = reinterpret_cast<float*>(lds);
+  if constexpr (KS > 1) {
+    __syncthreads();  // every copy and read of the tile buffers is over
+    float* part = reinterpret_cast<float*>(buf0);
     constexpr int kPartFloats = partial_bytes<D>() / 4;
     if (ks > 0) {
-      float* mine = part + (size_t)((ks - 1) * slice_waves + ws) * kPartFloats;
+      float* mine = part + (size_t)((ks - 1) * SW + ws) * kPartFloats;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -535,7 +641,7 @@ __global__ __launch_bounds__(kWave* kMaxWaves) void bsa_fwd_kernel(FwdParams p) 
     __syncthreads();
     if (ks > 0) return;
     for (int w = 1; w < KS; ++w) {
-      const float* other = part + (size_t)((w - 1) * slice_waves + ws) * kPartFloats;
+      const float* other = part + (size_t)((w - 1) * SW + ws) * kPartFloats;
       const float mo = other[(D / 32) * 16 * kWave + lane];
       const float lo = other[(D / 32) * 16 * kWave + kWave + lane];
       const float m_new = fmaxf(m2, mo);
@@ -571,78 +677,108 @@ __global__ __launch_bounds__(kWave* kMaxWaves) void bsa_fwd_kernel(FwdParams p) 
   }
 }
 
-template <typename T, int BS, int D, int G>
+// Dynamic LDS: entry list (M ints) and, for G > 1, G + 1 bitmaps.
+size_t dynamic_lds_bytes(int group, int M) {
+  const size_t words = group > 1 ? (size_t)(group + 1) * ((M + 31) / 32) : 0;
+  return 4 * ((size_t)M + words);
+}
+
+template <typename T, int BS, int D, int G, int KS>
+constexpr size_t static_lds_bytes() {  // 0 for a shape that is not instantiated
+  using C = Cfg<T, BS, D, G, KS>;
+  return C::kValid ? (size_t)C::NB * C::kSliceBytes + 16 : 0;
+}
+
+template <typename T, int BS, int D, int G, int KS>
 bsa_status launch(const FwdParams& p, hipStream_t stream) {
-  constexpr int QW = BS / kQRows;
-  const size_t lds = lds_bytes<T, BS, D>(G, p.key_split, p.nbuf, p.M);
-  if (lds > 64 * 1024) {
+  using C = Cfg<T, BS, D, G, KS>;
+  if constexpr (!C::kValid) {
+    return BSA_ERR_INVALID_ARGUMENT;
+  } else {
+  const size_t dyn = dynamic_lds_bytes(G, p.M);
+  if (dyn + static_lds_bytes<T, BS, D, G, KS>() > kMaxLds) return BSA_ERR_INVALID_ARGUMENT;
+  if (dyn + static_lds_bytes<T, BS, D, G, KS>() > 64 * 1024) {
     static bool raised = false;  // one attribute call per instantiation
     if (!raised) {
-      if (hipFuncSetAttribute(reinterpret_cast<const void*>(&bsa_fwd_kernel<T, BS, D, G>),
+      if (hipFuncSetAttribute(reinterpret_cast<const void*>(&bsa_fwd_kernel<T, BS, D, G, KS>),
                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                              static_cast<int>(kMaxLds)) != hipSuccess)
+                              static_cast<int>(kMaxLds - static_lds_bytes<T, BS, D, G, KS>())) !=
+          hipSuccess)
         return BSA_ERR_HIP;
       raised = true;
     }
   }
-  const dim3 block(kWave * QW * G * p.key_split);
+  const dim3 block(kWave * C::W);
   const dim3 grid(p.num_wg);
-  hipLaunchKernelGGL((bsa_fwd_kernel<T, BS, D, G>), grid, block, lds, stream, p);
+  hipLaunchKernelGGL((bsa_fwd_kernel<T, BS, D, G, KS>), grid, block, dyn, stream, p);
   return hipGetLastError() == hipSuccess ? BSA_OK : BSA_ERR_HIP;
+  }
+}
+
+// Static LDS of a shape, or 0 when the shape is not instantiated.
+template <typename T, int BS, int D>
+size_t shape_lds(int group, int key_split) {
+  if (group == 1 && key_split == 1) return static_lds_bytes<T, BS, D, 1, 1>();
+  if (group == 1 && key_split == 2) return static_lds_bytes<T, BS, D, 1, 2>();
+  if (group == 1 && key_split == 4) return static_lds_bytes<T, BS, D, 1, 4>();
+  if (group == 2 && key_split == 1) return static_lds_bytes<T, BS, D, 2, 1>();
+  if (group == 4 && key_split == 1) return static_lds_bytes<T, BS, D, 4, 1>();
+  return 0;
 }
 
 template <typename T, int BS, int D>
-bsa_status launch_group(const FwdParams& p, hipStream_t stream) {
-  switch (p.group) {
-    case 1: return launch<T, BS, D, 1>(p, stream);
-    case 2: return launch<T, BS, D, 2>(p, stream);
-    case 4: return launch<T, BS, D, 4>(p, stream);
-    default: return BSA_ERR_INVALID_ARGUMENT;
-  }
+bsa_status launch_shape(const FwdParams& p, hipStream_t stream) {
+  if (p.group == 1 && p.key_split == 1) return launch<T, BS, D, 1, 1>(p, stream);
+  if (p.group == 1 && p.key_split == 2) return launch<T, BS, D, 1, 2>(p, stream);
+  if (p.group == 1 && p.key_split == 4) return launch<T, BS, D, 1, 4>(p, stream);
+  if (p.group == 2 && p.key_split == 1) return launch<T, BS, D, 2, 1>(p, stream);
+  if (p.group == 4 && p.key_split == 1) return launch<T, BS, D, 4, 1>(p, stream);
+  return BSA_ERR_INVALID_ARGUMENT;
 }
 
 template <typename T>
 bsa_status dispatch(const FwdParams& p, int bs, int d, hipStream_t stream) {
-  if (bs == 32 && d == 64) return launch_group<T, 32, 64>(p, stream);
-  if (bs == 32 && d == 128) return launch_group<T, 32, 128>(p, stream);
-  if (bs == 64 && d == 64) return launch_group<T, 64, 64>(p, stream);
-  if (bs == 64 && d == 128) return launch_group<T, 64, 128>(p, stream);
+  if (bs == 32 && d == 64) return launch_shape<T, 32, 64>(p, stream);
+  if (bs == 32 && d == 128) return launch_shape<T, 32, 128>(p, stream);
+  if (bs == 64 && d == 64) return launch_shape<T, 64, 64>(p, stream);
+  if (bs == 64 && d == 128) return launch_shape<T, 64, 128>(p, stream);
   return BSA_ERR_INVALID_ARGUMENT;
 }
 
-size_t lds_for(int dtype, int bs, int d, int group, int ks, int nbuf, int M) {
+// Total LDS of a shape for (dtype, bs, d), or 0 when it is not instantiated.
+size_t lds_for(int dtype, int bs, int d, int group, int ks, int M) {
+  size_t st = 0;
   if (dtype == BSA_DTYPE_F32) {
-    if (bs == 32) return d == 64 ? lds_bytes<float, 32, 64>(group, ks, nbuf, M)
-                                 : lds_bytes<float, 32, 128>(group, ks, nbuf, M);
-    return d == 64 ? lds_bytes<float, 64, 64>(group, ks, nbuf, M)
-                   : lds_bytes<float, 64, 128>(group, ks, nbuf, M);
+    if (bs == 32) st = d == 64 ? shape_lds<float, 32, 64>(group, ks) : shape_lds<float, 32, 128>(group, ks);
+    else st = d == 64 ? shape_lds<float, 64, 64>(group, ks) : shape_lds<float, 64, 128>(group, ks);
+  } else {
+    if (bs == 32) st = d == 64 ? shape_lds<__bf16, 32, 64>(group, ks) : shape_lds<__bf16, 32, 128>(group, ks);
+    else st = d == 64 ? shape_lds<__bf16, 64, 64>(group, ks) : shape_lds<__bf16, 64, 128>(group, ks);
   }
-  if (bs == 32) return d == 64 ? lds_bytes<__bf16, 32, 64>(group, ks, nbuf, M)
-                               : lds_bytes<__bf16, 32, 128>(group, ks, nbuf, M);
-  return d == 64 ? lds_bytes<__bf16, 64, 64>(group, ks, nbuf, M)
-                 : lds_bytes<__bf16, 64, 128>(group, ks, nbuf, M);
+  return st == 0 ? 0 : st + dynamic_lds_bytes(group, M);
 }
 
 // Workgroup shape.  Large grids: G query blocks per workgroup share their K/V
 // tiles (4 blocks of 32 rows, or 2 of 64).  Grids too small to give every
 // SIMD ~4 waves: one query block per workgroup and the CSR row split over KS
-// key-slice wave sets instead.  Two LDS entry buffers when they fit in
-// kMaxLds, else one.
-void choose_shape(int64_t bhm, int bs, int d, int dtype, int M, int* group, int* key_split,
-                  int* nbuf) {
+// key-slice wave sets instead.
+void choose_shape(int64_t bhm, int bs, int d, int dtype, int M, int* group, int* key_split) {
   constexpr int64_t kTargetWaves = 4 * 4 * 256;
   const int qw = bs / kQRows;
-  auto fits = [&](int g, int ks, int nb) { return lds_for(dtype, bs, d, g, ks, nb, M) <= kMaxLds; };
+  auto fits = [&](int g, int ks) {
+    const size_t b = lds_for(dtype, bs, d, g, ks, M);
+    return b != 0 && b <= kMaxLds;
+  };
   int g = 1, ks = 1;
   if (bhm * qw >= 2 * kTargetWaves) {
     g = bs == 32 ? 4 : 2;
+    if (!fits(g, 1)) g = 1;
   } else {
-    while (qw * ks * 2 <= kMaxWaves && bhm * qw * ks < kTargetWaves && fits(1, ks * 2, 2))
+    while (ks < 4 && qw * ks * 2 <= kMaxWaves && bhm * qw * ks < kTargetWaves && fits(1, ks * 2))
       ks *= 2;
   }
   *group = g;
   *key_split = ks;
-  *nbuf = fits(g, ks, 2) ? 2 : 1;
 }
 
 }  // namespace
@@ -681,18 +817,15 @@ bsa_status forward_impl(const void* q, const void* k, const void* v, void* o, fl
   p.N = seq_len;
   if (group == 0 && key_split == 0) {
     choose_shape((int64_t)batch * heads * M, block_size, head_dim, dtype, (int)M, &p.group,
-                 &p.key_split, &p.nbuf);
+                 &p.key_split);
   } else {
     const int qw = block_size / kQRows;
-    if ((group != 1 && group != 2 && group != 4) || key_split < 1 ||
-        qw * group * key_split > kMaxWaves)
-      return BSA_ERR_INVALID_ARGUMENT;
+    if (qw * group * key_split > kMaxWaves) return BSA_ERR_INVALID_ARGUMENT;
     p.group = group;
     p.key_split = key_split;
-    p.nbuf = lds_for(dtype, block_size, head_dim, group, key_split, 2, (int)M) <= kMaxLds ? 2 : 1;
   }
-  if (lds_for(dtype, block_size, head_dim, p.group, p.key_split, p.nbuf, (int)M) > kMaxLds)
-    return BSA_ERR_INVALID_ARGUMENT;
+  const size_t lds = lds_for(dtype, block_size, head_dim, p.group, p.key_split, (int)M);
+  if (lds == 0 || lds > kMaxLds) return BSA_ERR_INVALID_ARGUMENT;
   const int64_t ngroups = (M + p.group - 1) / p.group;
   const int64_t num_wg = (int64_t)batch * heads * ngroups;
   if (num_wg > INT32_MAX) return BSA_ERR_SHAPE;
