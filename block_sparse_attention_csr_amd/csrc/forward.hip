@@ -511,14 +511,30 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
   }
   // Slice ks takes list entries ks, ks + KS, ...; every wave runs niter steps.
   const int niter = (U + KS - 1) / KS;
-  auto entry_block = [&](int i) -> int {  // block of this slice's step i, or -1
-    const int t = i * KS + ks;
-    return t < U ? uniform(list[t]) : -1;
-  };
-  auto selected = [&](int j) -> bool {
-    if (j < 0 || j >= M || !has_rows) return false;
-    if constexpr (G == 1) return true;
-    return ((((uint32_t)uniform((int)my_row[j >> 5])) >> (j & 31)) & 1u) != 0;
+  // The list is read 64 entries at a time into one VGPR (lane l holds entry
+  // base + l) with a ballot of which of them this wave's row selects, so a
+  // step needs one v_readlane and a scalar bit test, not an LDS round trip.
+  int chunk_base = -64;
+  int chunk = -1;
+  uint64_t chunk_mine = 0;
+  auto entry_at = [&](int step, bool& mine) -> int {  // block of this slice's step, or -1
+    const int t = step * KS + ks;
+    if (t >= U) {
+      mine = false;
+      return -1;
+    }
+    if ((t & ~(kWave - 1)) != chunk_base) {
+      chunk_base = t & ~(kWave - 1);
+      const int idx = chunk_base + lane;
+      chunk = idx < U ? list[idx] : -1;
+      bool sel = chunk >= 0 && chunk < M && has_rows;
+      if constexpr (G > 1)
+        sel = sel && ((my_row[chunk >> 5] >> (chunk & 31)) & 1u) != 0;
+      chunk_mine = __builtin_amdgcn_ballot_w64(sel);
+    }
+    const int l = t - chunk_base;
+    mine = ((chunk_mine >> l) & 1ull) != 0;
+    return __builtin_amdgcn_readlane(chunk, l);
   };
 
   // ---- direct-to-LDS copies.  Part c of this wave is part ws + c*SW of the
@@ -590,9 +606,10 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
   // entry i each wave waits for its own copies of entry i (the later entries'
   // copies may stay in flight) and for its LDS reads of entry i-1; after it,
   // every wave's copies of entry i have landed and buffer (i-1) % NB is free.
-  int jq[NB];  // blocks of steps i .. i + NB - 1
+  int jq[NB];   // blocks of steps i .. i + NB - 1
+  bool mq[NB];  // whether this wave computes them
 #pragma unroll
-  for (int e = 0; e < NB; ++e) jq[e] = entry_block(e);
+  for (int e = 0; e < NB; ++e) jq[e] = entry_at(e, mq[e]);
   // The Q loads were issued long ago; waiting for them here, before the first
   // copy, tells the compiler they are complete (it does not see the copies
   // and would otherwise wait on the vector-memory counter inside the loop).
@@ -610,12 +627,15 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
     if (NB == 3 && i + 1 < niter) wait_vm_lgkm0<C::kParts>();
     else wait_vm_lgkm0<0>();
     raw_barrier();
-    const int j = jq[0];
+    const bool mine = mq[0];
 #pragma unroll
-    for (int e = 0; e + 1 < NB; ++e) jq[e] = jq[e + 1];
-    jq[NB - 1] = entry_block(i + NB);
+    for (int e = 0; e + 1 < NB; ++e) {
+      jq[e] = jq[e + 1];
+      mq[e] = mq[e + 1];
+    }
+    jq[NB - 1] = entry_at(i + NB, mq[NB - 1]);
     if (i + NB - 1 < niter) issue(jq[NB - 2], buffer(std::integral_constant<int, (b + NB - 1) % NB>{}));
-    if (selected(j)) compute(buffer(b_c));
+    if (mine) compute(buffer(b_c));
   };
   for (int i = 0; i < niter; i += NB) {
     step(i, std::integral_constant<int, 0>{});
