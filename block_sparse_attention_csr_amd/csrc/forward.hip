@@ -17,10 +17,10 @@
 //    and banded patterns select mostly the same K blocks, so the tile traffic
 //    out of L2 drops by the reuse factor.  Every wave computes only the
 //    blocks its own row selects (a bit test on its row bitmap).
-//  * K/V tiles are software-pipelined through registers: while union entry u
-//    computes, entry u+1 is written from registers into the other LDS
-//    buffer and entry u+2 is loaded from global memory (16-byte loads).
-//    16-byte chunks are XOR-swizzled per row pair to spread LDS banks.
+//  * The union's K/V blocks stream through a ring of NB LDS buffers with
+//    direct-to-LDS copies (global_load_lds_dwordx4), NB - 1 entries ahead of
+//    the compute.  16-byte chunks are XOR-swizzled per row to spread LDS
+//    banks.
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (keys = MFMA rows, queries =
 //    MFMA columns): each lane holds the scores of ONE query, so row max and
 //    row sum are in-lane plus one v_permlane32_swap between the lane halves.
@@ -106,7 +106,7 @@ __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirs
 __device__ __forceinline__ float halves_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float halves_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
@@ -581,7 +581,7 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
 #pragma unroll
     for (int st = 0; st < KSTEPS; ++st)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[st][r]);
+      for (int r = 0; r < 16; ++r) mx = __builtin_elementwise_maximum(mx, sc[st][r]);
     mx = halves_max(mx) * c2;
     if (first) {  // O and l are still zero: no rescale
       m2 = mx;
@@ -779,23 +779,23 @@ size_t lds_for(int dtype, int bs, int d, int group, int ks, int M) {
 }
 
 // Workgroup shape.  Large grids: G query blocks per workgroup share their K/V
-// tiles (4 blocks of 32 rows, or 2 of 64).  Grids too small to give every
-// SIMD ~4 waves: one query block per workgroup and the CSR row split over KS
-// key-slice wave sets instead.
+// tiles (4 blocks of 32 rows, or 2 of 64).  Smaller grids: one query block
+// per workgroup, which has the shortest critical path; only grids with fewer
+// query blocks than CUs also split each CSR row over KS key-slice wave sets.
 void choose_shape(int64_t bhm, int bs, int d, int dtype, int M, int* group, int* key_split) {
-  constexpr int64_t kTargetWaves = 4 * 4 * 256;
+  constexpr int64_t kCus = 256;
+  constexpr int64_t kLargeGrid = 8 * 4 * kCus;  // 8 query waves per SIMD
   const int qw = bs / kQRows;
   auto fits = [&](int g, int ks) {
     const size_t b = lds_for(dtype, bs, d, g, ks, M);
     return b != 0 && b <= kMaxLds;
   };
   int g = 1, ks = 1;
-  if (bhm * qw >= 2 * kTargetWaves) {
+  if (bhm * qw >= kLargeGrid) {
     g = bs == 32 ? 4 : 2;
     if (!fits(g, 1)) g = 1;
   } else {
-    while (ks < 4 && qw * ks * 2 <= kMaxWaves && bhm * qw * ks < kTargetWaves && fits(1, ks * 2))
-      ks *= 2;
+    while (ks < 4 && qw * ks * 2 <= kMaxWaves && bhm * ks < kCus && fits(1, ks * 2)) ks *= 2;
   }
   *group = g;
   *key_split = ks;
