@@ -235,36 +235,34 @@ struct Ops<__bf16> {
     return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
   }
 
-  // O^T += V^T P^T over one block; returns the sum of the bf16-rounded P.
+  // O^T += V^T P^T over 32-key step st of the entry; returns the sum of the
+  // bf16-rounded P (the weights the product uses).
   template <int BS, int D>
-  static __device__ __forceinline__ float accumulate(f32x16_t (&o)[D / 32],
-                                                     const f32x16_t (&p)[BS / kKeyStep],
+  static __device__ __forceinline__ float accumulate(f32x16_t (&o)[D / 32], const f32x16_t& p,
                                                      const Offsets<BS, D>& off,
-                                                     LDS_PTR(unsigned char) lds, int entry) {
+                                                     LDS_PTR(unsigned char) lds, int entry,
+                                                     int st) {
     float sum = 0.f;
     const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-    for (int st = 0; st < BS / kKeyStep; ++st) {
+    for (int sc = 0; sc < 2; ++sc) {
+      // The four packed words are built as separate scalars: reading dot2
+      // operands out of a 128-bit vector miscompiles (every v_dot2c read
+      // the first word).
+      uint32_t w4[4];
 #pragma unroll
-      for (int sc = 0; sc < 2; ++sc) {
-        // The four packed words are built as separate scalars: reading dot2
-        // operands out of a 128-bit vector miscompiles (every v_dot2c read
-        // the first word).
-        uint32_t w4[4];
+      for (int w = 0; w < 4; ++w) {
+        w4[w] = pack_bf16x2(p[8 * sc + 2 * w], p[8 * sc + 2 * w + 1]);
+        sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w4[w]), ones, sum,
+                                              false);
+      }
+      const u32x4_t pb = {w4[0], w4[1], w4[2], w4[3]};
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          w4[w] = pack_bf16x2(p[st][8 * sc + 2 * w], p[st][8 * sc + 2 * w + 1]);
-          sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w4[w]), ones, sum,
-                                                false);
-        }
-        const u32x4_t pb = {w4[0], w4[1], w4[2], w4[3]};
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          const u32x4_t va = v_operand<BS, D>(off, lds, entry, st, sc, dt);
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, va),
-                                                          __builtin_bit_cast(bf16x8_t, pb),
-                                                          o[dt], 0, 0, 0);
-        }
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const u32x4_t va = v_operand<BS, D>(off, lds, entry, st, sc, dt);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, va),
+                                                        __builtin_bit_cast(bf16x8_t, pb), o[dt],
+                                                        0, 0, 0);
       }
     }
     return sum;
@@ -326,28 +324,25 @@ struct Ops<float> {
   // Instruction i of a 32-key step contracts the keys held in accumulator
   // register i: key 8 (i / 4) + 4 h + i % 4 for lane half h.
   template <int BS, int D>
-  static __device__ __forceinline__ float accumulate(f32x16_t (&o)[D / 32],
-                                                     const f32x16_t (&p)[BS / kKeyStep],
+  static __device__ __forceinline__ float accumulate(f32x16_t (&o)[D / 32], const f32x16_t& p,
                                                      const Offsets<BS, D>& off,
-                                                     LDS_PTR(unsigned char) lds, int entry) {
+                                                     LDS_PTR(unsigned char) lds, int entry,
+                                                     int st) {
     using L = TileLayout<float, BS, D>;
     const int h = off.lane >> 5;
     float sum = 0.f;
 #pragma unroll
-    for (int st = 0; st < BS / kKeyStep; ++st) {
+    for (int i = 0; i < 16; ++i) sum += p[i];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sum += p[st][i];
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const int feature = dt * 32 + (off.lane & 31);
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        const int feature = dt * 32 + (off.lane & 31);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int row = st * kKeyStep + 8 * (i / 4) + 4 * h + (i % 4);
-          const float va = *(LDS_PTR(const float))(lds + off.base + entry + L::kTileBytes +
-                                                   L::chunk_offset(row, feature >> 2) +
-                                                   (feature & 3) * 4);
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(va, p[st][i], o[dt], 0, 0, 0);
-        }
+      for (int i = 0; i < 16; ++i) {
+        const int row = st * kKeyStep + 8 * (i / 4) + 4 * h + (i % 4);
+        const float va = *(LDS_PTR(const float))(lds + off.base + entry + L::kTileBytes +
+                                                 L::chunk_offset(row, feature >> 2) +
+                                                 (feature & 3) * 4);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(va, p[i], o[dt], 0, 0, 0);
       }
     }
     return sum;
@@ -572,33 +567,35 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
   bool first = true;     // no block computed yet by this wave
   const float c2 = p.scale_log2;
 
+  // One entry: all S^T tiles are issued first; each 32-key step then runs its
+  // softmax (VALU) while the MFMAs of the later steps are still in flight,
+  // and its P.V while the next step's softmax runs.
   auto compute = [&](unsigned char* buf) {
     LDS_PTR(unsigned char) tile = (LDS_PTR(unsigned char))buf;
     f32x16_t sc[KSTEPS];
 #pragma unroll
     for (int st = 0; st < KSTEPS; ++st) sc[st] = O::template scores<BS, D>(qop, off, tile, 0, st);
-    float mx = sc[0][0];
 #pragma unroll
-    for (int st = 0; st < KSTEPS; ++st)
+    for (int st = 0; st < KSTEPS; ++st) {
+      float mx = sc[st][0];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = __builtin_elementwise_maximum(mx, sc[st][r]);
-    mx = halves_max(mx) * c2;
-    if (first) {  // O and l are still zero: no rescale
-      m2 = mx;
-      first = false;
-    } else if (__builtin_amdgcn_ballot_w64(mx > m2 + kLazyRescale) != 0) {
-      const float m_new = fmaxf(m2, mx);
-      const float alpha = fast_exp2(m2 - m_new);
-      m2 = m_new;
-      lsum *= alpha;
+      for (int r = 1; r < 16; ++r) mx = __builtin_elementwise_maximum(mx, sc[st][r]);
+      mx = halves_max(mx) * c2;
+      if (first) {  // O and l are still zero: no rescale
+        m2 = mx;
+        first = false;
+      } else if (__builtin_amdgcn_ballot_w64(mx > m2 + kLazyRescale) != 0) {
+        const float m_new = fmaxf(m2, mx);
+        const float alpha = fast_exp2(m2 - m_new);
+        m2 = m_new;
+        lsum *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
-    }
-#pragma unroll
-    for (int st = 0; st < KSTEPS; ++st)
+        for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) sc[st][r] = fast_exp2(fmaf(sc[st][r], c2, -m2));
-    lsum += O::template accumulate<BS, D>(o, sc, off, tile, 0);
+      lsum += O::template accumulate<BS, D>(o, sc[st], off, tile, 0, st);
+    }
   };
 
   // ---- pipeline: entry i computes from buffer i % NB while the copies of
