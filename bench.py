@@ -55,6 +55,11 @@ def parse_args(argv=None):
                    help="skip the B=32 line of the worked-example shape")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="minimum CPU time for the oracle baseline")
+    p.add_argument("--no-ceilings", action="store_true",
+                   help="skip the measured dense-GEMM and copy ceilings")
+    p.add_argument("--causal", action="store_true",
+                   help="time the causal forward (keys after each query hidden; the pattern "
+                        "built causal) instead of the plain one")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run 5 device-to-device copies of 1 GiB (reference kernel for "
                         "scaling HBM byte counters) and exit")
@@ -80,13 +85,15 @@ def copy_calibration():
 class Case:
     """Inputs, cached pattern and preallocated outputs of one workload."""
 
-    def __init__(self, name, seed, device):
+    def __init__(self, name, seed, device, causal=False):
+        import numpy as np
         import torch
 
         import block_sparse_attention_csr_amd as bsa
         from synthetic_inputs import WORKLOADS, make_qkv, workload_block_mask
 
         self.bsa = bsa
+        self.causal = causal
         self.w = w = WORKLOADS[name]
         self.mask = workload_block_mask(w, seed)
         q, k, v = make_qkv(w.B, w.H, w.N, w.d, w.torch_dtype, seed)
@@ -100,17 +107,26 @@ class Case:
         self.step()
         torch.cuda.synchronize()
         self.first_step_ms = (time.perf_counter() - t0) * 1e3
-        self.nnz = self.cache.get(w.N, w.block_size, mask=self.mask)[2]
-        self.flops = 4.0 * w.block_size ** 2 * w.d * self.nnz * w.B * w.H
+        self.nnz = self.cache.get(w.N, w.block_size, mask=self.mask, causal=causal)[2]
+        # Selected (query, key) pairs: a whole block pair is bs^2 of them; with
+        # causal masking a diagonal block keeps bs (bs + 1) / 2.
+        pairs = float(w.block_size ** 2 * self.nnz)
+        if causal:
+            rp, ci = bsa.build_pattern(w.N, w.block_size, mask=self.mask, causal=True)
+            rows = np.repeat(np.arange(w.M), np.diff(rp.numpy()))
+            diag = int((ci.numpy() == rows).sum())
+            pairs -= diag * (w.block_size ** 2 - w.block_size * (w.block_size + 1) // 2)
+        self.flops = 4.0 * w.d * pairs * w.B * w.H
         elt = 2 if w.dtype == "bf16" else 4
         # compulsory traffic: Q, K, V read once, O written once, LSE written once
         self.compulsory_bytes = 4.0 * w.B * w.H * w.N * w.d * elt + 4.0 * w.B * w.H * w.N
 
     def step(self):
         w = self.w
-        row_ptr, col_idx, nnz = self.cache.get(w.N, w.block_size, mask=self.mask)
+        row_ptr, col_idx, nnz = self.cache.get(w.N, w.block_size, mask=self.mask,
+                                               causal=self.causal)
         self.bsa.forward(self.q, self.k, self.v, row_ptr, col_idx, w.block_size,
-                         out=self.out, lse=self.lse, nnz=nnz)
+                         out=self.out, lse=self.lse, nnz=nnz, causal=self.causal)
 
 
 def time_eager(case, steps):
@@ -230,6 +246,75 @@ def cpu_baseline(workload: str, seed: int, min_seconds: float):
     }
 
 
+def practical_ceilings():
+    """Measured ceilings on this GPU beside the published peaks: a dense bf16
+    GEMM through torch (hipBLASLt) and a 1 GiB device-to-device copy."""
+    import torch
+
+    n = 8192
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    start.record()
+    for _ in range(reps):
+        torch.matmul(a, b)
+    end.record()
+    torch.cuda.synchronize()
+    gemm = 2.0 * n ** 3 * reps / (start.elapsed_time(end) * 1e-3) / 1e12
+    del a, b
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    start.record()
+    for _ in range(5):
+        dst.copy_(src)
+    end.record()
+    torch.cuda.synchronize()
+    copy = 2.0 * (1 << 30) * 5 / (start.elapsed_time(end) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"dense_bf16_gemm_tflops": round(gemm, 1),
+            "dense_bf16_gemm": "torch.matmul 8192^3 bf16, 10 reps",
+            "device_copy_gbps": round(copy, 1),
+            "device_copy": "1 GiB copy, read + write bytes, 5 reps"}
+
+
+def side_line(name, args, device, causal):
+    """A graph-timed line for another workload (the saturating B = 32 shape,
+    or its causal forward) reported beside the headline."""
+    import torch
+
+    sat = Case(name, args.seed, device, causal=causal)
+    for _ in range(5):
+        sat.step()
+    sat_steps = max(10, min(100, args.steps // 10))
+    s_graph, s_evt = time_graph(sat, sat_steps) if not args.no_graph else (None, None)
+    s_launch = time_events_per_launch(sat, sat_steps)
+    s_step = s_graph if s_graph is not None else time_eager(sat, sat_steps)
+    s_kernel = s_evt if s_evt is not None else s_launch
+    s_traffic = None if causal else load_traffic(name)
+    line = {
+        "value": round(sat.flops / s_step / 1e12, 3),
+        "unit": "TFLOP/s",
+        "ms_per_step": s_step * 1e3,
+        "pct_bf16_mfma_peak": round(100.0 * sat.flops / s_step / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "kernel_us": s_kernel * 1e6,
+        "mfma_achieved_tflops": round(sat.flops / s_kernel / 1e12, 3),
+        "compulsory_hbm_gbps": round(sat.compulsory_bytes / s_kernel / 1e9, 1),
+        "traffic": s_traffic,
+        "traffic_over_algorithmic": None if s_traffic is None
+        else round(s_traffic / sat.compulsory_bytes, 3),
+    }
+    if causal:
+        line["flop_counting"] = "selected (query, key) pairs: diagonal blocks count bs(bs+1)/2"
+    del sat
+    torch.cuda.empty_cache()
+    return line
+
+
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
@@ -248,7 +333,7 @@ def main(argv=None):
     device = torch.device("cuda:0")
     torch.cuda.set_device(device)
 
-    case = Case(args.workload, args.seed, device)
+    case = Case(args.workload, args.seed, device, causal=args.causal)
     w = case.w
     for _ in range(args.warmup):
         case.step()
@@ -281,7 +366,7 @@ def main(argv=None):
     else:
         roof = {"bound": "mfma", "achieved": round(tflops, 3), "peak": peak_flops,
                 "unit": "TFLOP/s", "frac": round(tflops / peak_flops, 4)}
-    traffic = load_traffic(args.workload)
+    traffic = None if args.causal else load_traffic(args.workload)
     roof.update({
         "traffic": traffic,
         "kernel": "bsa_fwd_kernel",
@@ -311,7 +396,7 @@ def main(argv=None):
         "config": {
             "workload": w.name, "description": w.description, "B": w.B, "H": w.H, "N": w.N,
             "d": w.d, "block_size": w.block_size, "nnz_per_head": case.nnz,
-            "pattern": w.pattern, "parallelism": "single GPU",
+            "pattern": w.pattern, "causal": bool(args.causal), "parallelism": "single GPU",
             "timing": "HIP graph of K launches" if graph_s is not None else "eager",
         },
         "pct_bf16_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
@@ -320,31 +405,17 @@ def main(argv=None):
         "roofline": roof,
     }
 
-    if not args.no_saturating and args.workload == "worked_example":
+    if not args.no_saturating and args.workload == "worked_example" and not args.causal:
         del case
         torch.cuda.empty_cache()
-        sat = Case("worked_example_b32", args.seed, device)
-        for _ in range(5):
-            sat.step()
-        sat_steps = max(10, min(100, args.steps // 10))
-        s_graph, s_evt = time_graph(sat, sat_steps) if not args.no_graph else (None, None)
-        s_launch = time_events_per_launch(sat, sat_steps)
-        s_step = s_graph if s_graph is not None else time_eager(sat, sat_steps)
-        s_kernel = s_evt if s_evt is not None else s_launch
-        s_traffic = load_traffic("worked_example_b32")
-        result["saturating_worked_example_b32"] = {
-            "value": round(sat.flops / s_step / 1e12, 3),
-            "unit": "TFLOP/s",
-            "ms_per_step": s_step * 1e3,
-            "pct_bf16_mfma_peak": round(100.0 * sat.flops / s_step / 1e12 / PEAK_BF16_TFLOPS, 2),
-            "kernel_us": s_kernel * 1e6,
-            "mfma_achieved_tflops": round(sat.flops / s_kernel / 1e12, 3),
-            "compulsory_hbm_gbps": round(sat.compulsory_bytes / s_kernel / 1e9, 1),
-            "traffic": s_traffic,
-            "traffic_over_algorithmic": None if s_traffic is None
-            else round(s_traffic / sat.compulsory_bytes, 3),
-        }
-        del sat
+        # The same shape with B = 32 fills the GPU; then its causal forward.
+        result["saturating_worked_example_b32"] = side_line("worked_example_b32", args, device,
+                                                            causal=False)
+        result["causal_worked_example_b32"] = side_line("worked_example_b32", args, device,
+                                                        causal=True)
+
+    if not args.no_ceilings:
+        result["practical_ceilings"] = practical_ceilings()
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.workload, args.seed, args.cpu_seconds)

@@ -21,7 +21,7 @@ import numpy as np
 
 __all__ = [
     "BsaError", "build_pattern", "forward", "status_string", "abi_version", "library_path",
-    "PatternCache", "BSA_OK",
+    "PatternCache", "BSA_OK", "stack_head_patterns",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -30,6 +30,10 @@ _LIB_PATH = os.path.join(_PKG, "libbsa.so")
 BSA_OK = 0
 _PATTERN_LOGLINEAR = 0
 _PATTERN_BLOCK_MASK = 1
+_PATTERN_DILATED = 2
+_PATTERN_BIGBIRD = 3
+FORWARD_CAUSAL = 1
+FORWARD_PATTERN_PER_HEAD = 2
 _DTYPE_F32 = 0
 _DTYPE_BF16 = 1
 
@@ -52,6 +56,11 @@ class _PatternDesc(ctypes.Structure):
         ("num_global", ctypes.c_int32),
         ("global_blocks", ctypes.POINTER(ctypes.c_int32)),
         ("mask", ctypes.POINTER(ctypes.c_uint8)),
+        ("causal", ctypes.c_int32),
+        ("window", ctypes.c_int32),
+        ("dilation", ctypes.c_int32),
+        ("num_random", ctypes.c_int32),
+        ("seed", ctypes.c_uint64),
     ]
 
 
@@ -80,7 +89,7 @@ def _load():
                                 ctypes.c_float, vp]
     lib.bsa_forward.restype = i32
     lib.bsa_forward_ex.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp,
-                                   i64, ctypes.c_float, i32, i32, vp]
+                                   i64, ctypes.c_float, i32, i32, i32, vp]
     lib.bsa_forward_ex.restype = i32
     lib.bsa_status_string.argtypes = [i32]
     lib.bsa_status_string.restype = ctypes.c_char_p
@@ -98,7 +107,8 @@ def abi_version() -> int:
     return int(_load().bsa_abi_version())
 
 
-def _desc(seq_len, block_size, mask, local_radius, k_max, global_blocks, keep):
+def _desc(seq_len, block_size, kind, mask, local_radius, k_max, global_blocks, causal, window,
+          dilation, num_random, seed, keep):
     d = _PatternDesc()
     d.seq_len = int(seq_len)
     d.block_size = int(block_size)
@@ -107,34 +117,52 @@ def _desc(seq_len, block_size, mask, local_radius, k_max, global_blocks, keep):
     d.num_global = -1
     d.global_blocks = None
     d.mask = None
-    if mask is not None:
-        d.kind = _PATTERN_BLOCK_MASK
+    d.causal = 1 if causal else 0
+    d.window = 0 if window is None else int(window)
+    d.dilation = 1 if dilation is None else int(dilation)
+    d.num_random = 0 if num_random is None else int(num_random)
+    d.seed = 0 if seed is None else int(seed) & ((1 << 64) - 1)
+    if kind is None:
+        kind = "mask" if mask is not None else "loglinear"
+    codes = {"loglinear": _PATTERN_LOGLINEAR, "mask": _PATTERN_BLOCK_MASK,
+             "dilated": _PATTERN_DILATED, "bigbird": _PATTERN_BIGBIRD}
+    if kind not in codes:
+        raise ValueError(f"unknown pattern kind {kind!r}; one of {sorted(codes)}")
+    d.kind = codes[kind]
+    if kind == "mask":
+        if mask is None:
+            raise ValueError("kind 'mask' needs a mask")
         m = np.ascontiguousarray(np.asarray(mask) != 0, dtype=np.uint8)
         keep.append(m)
         d.mask = m.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))
-    else:
-        d.kind = _PATTERN_LOGLINEAR
-        if global_blocks is not None:
-            g = np.ascontiguousarray(np.asarray(global_blocks, dtype=np.int32).reshape(-1))
-            keep.append(g)
-            d.num_global = int(g.size)
-            d.global_blocks = g.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    elif global_blocks is not None:
+        g = np.ascontiguousarray(np.asarray(global_blocks, dtype=np.int32).reshape(-1))
+        keep.append(g)
+        d.num_global = int(g.size)
+        d.global_blocks = g.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
     return d
 
 
 def build_pattern(seq_len: int, block_size: int, *, mask=None, local_radius=None, k_max=None,
-                  global_blocks=None):
+                  global_blocks=None, causal: bool = False, kind: str | None = None,
+                  window: int | None = None, dilation: int | None = None,
+                  num_random: int | None = None, seed: int | None = None):
     """CSR (row_ptr int32[M+1], col_idx int32[nnz]) as CPU torch tensors.
 
-    Without ``mask``: the log-linear rule (defaults: radius 1,
-    k_max = ceil(log2 M), globals {0, M/2, M-1}).  With ``mask`` ([M, M],
-    nonzero = selected): that block mask.  Raises BsaError on a bad pattern.
+    ``kind``: "loglinear" (default without ``mask``: radius 1,
+    k_max = ceil(log2 M), globals {0, M/2, M-1}), "mask" (default with
+    ``mask``: an [M, M] array, nonzero = selected), "dilated" (``window``,
+    ``dilation``, optional ``global_blocks``) or "bigbird" (``local_radius``,
+    ``global_blocks``, ``num_random`` per row drawn from ``seed``).
+    ``causal`` drops blocks after each query block.  Raises BsaError on a bad
+    pattern.
     """
     import torch
 
     lib = _load()
     keep = []
-    desc = _desc(seq_len, block_size, mask, local_radius, k_max, global_blocks, keep)
+    desc = _desc(seq_len, block_size, kind, mask, local_radius, k_max, global_blocks, causal,
+                 window, dilation, num_random, seed, keep)
     nnz = ctypes.c_int64(0)
     st = lib.bsa_build_pattern(ctypes.byref(desc), None, None, 0, ctypes.byref(nnz))
     if st != BSA_OK:
@@ -150,6 +178,23 @@ def build_pattern(seq_len: int, block_size: int, *, mask=None, local_radius=None
     return torch.from_numpy(row_ptr), torch.from_numpy(col_idx[:nnz.value].copy())
 
 
+def stack_head_patterns(patterns):
+    """One CSR per head -> (row_ptr int32[H*(M+1)], col_idx int32[nnz]) for the
+    per-head forward: head h's row offsets are shifted by the entries of the
+    heads before it, so that they index the one concatenated col_idx."""
+    import torch
+
+    rps, cis = [], []
+    base = 0
+    for row_ptr, col_idx in patterns:
+        rps.append(row_ptr.to(torch.int64) + base)
+        cis.append(col_idx)
+        base += int(col_idx.numel())
+    if base > 2**31 - 1:
+        raise ValueError("per-head patterns exceed int32 offsets")
+    return torch.cat(rps).to(torch.int32), torch.cat(cis).to(torch.int32)
+
+
 def _dtype_code(t):
     import torch
 
@@ -162,7 +207,7 @@ def _dtype_code(t):
 
 def forward(q, k, v, row_ptr, col_idx, block_size: int, scale: float | None = None, *,
             out=None, lse=None, nnz: int | None = None, stream=None, group: int = 0,
-            key_split: int = 0):
+            key_split: int = 0, causal: bool = False, per_head: bool = False):
     """Block-sparse attention forward on the GPU.
 
     q, k, v: CUDA tensors [B, H, N, d] (bfloat16 or float32), contiguous.
@@ -171,7 +216,9 @@ def forward(q, k, v, row_ptr, col_idx, block_size: int, scale: float | None = No
     enqueued on the current stream (or ``stream``) and not synchronised.
     ``nnz`` (host int) avoids reading row_ptr back; by default it is
     col_idx.numel().  ``group`` / ``key_split`` force a workgroup shape
-    (bsa_forward_ex); 0 / 0 lets the library choose.
+    (bsa_forward_ex); 0 / 0 lets the library choose.  ``causal`` hides keys
+    after each query position; ``per_head`` takes row_ptr as [H, M + 1]
+    offsets into one col_idx (see ``stack_head_patterns``).
     """
     import torch
 
@@ -201,8 +248,9 @@ def forward(q, k, v, row_ptr, col_idx, block_size: int, scale: float | None = No
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N,
             d, int(block_size), _dtype_code(q), row_ptr.data_ptr(), col_idx.data_ptr(),
             int(nnz), 0.0 if scale is None else float(scale))
-    if group or key_split:
-        st = lib.bsa_forward_ex(*args, int(group), int(key_split), stream.cuda_stream)
+    flags = (FORWARD_CAUSAL if causal else 0) | (FORWARD_PATTERN_PER_HEAD if per_head else 0)
+    if group or key_split or flags:
+        st = lib.bsa_forward_ex(*args, flags, int(group), int(key_split), stream.cuda_stream)
     else:
         st = lib.bsa_forward(*args, stream.cuda_stream)
     if st != BSA_OK:
@@ -221,19 +269,16 @@ class PatternCache:
         self.device = device
         self._cache = {}
 
-    def get(self, seq_len: int, block_size: int, *, mask=None, local_radius=None, k_max=None,
-            global_blocks=None):
-        if mask is not None:
-            mkey = np.ascontiguousarray(np.asarray(mask) != 0, dtype=np.uint8).tobytes()
-        else:
-            mkey = None
-        gkey = None if global_blocks is None else tuple(int(g) for g in global_blocks)
-        key = (seq_len, block_size, mkey, local_radius, k_max, gkey)
+    def get(self, seq_len: int, block_size: int, *, mask=None, **options):
+        """(row_ptr, col_idx, nnz) on the device; ``options`` as for build_pattern."""
+        mkey = (None if mask is None else
+                np.ascontiguousarray(np.asarray(mask) != 0, dtype=np.uint8).tobytes())
+        okey = tuple(sorted((k, tuple(int(g) for g in v) if k == "global_blocks" and v is not None
+                             else v) for k, v in options.items()))
+        key = (seq_len, block_size, mkey, okey)
         hit = self._cache.get(key)
         if hit is None:
-            row_ptr, col_idx = build_pattern(seq_len, block_size, mask=mask,
-                                             local_radius=local_radius, k_max=k_max,
-                                             global_blocks=global_blocks)
+            row_ptr, col_idx = build_pattern(seq_len, block_size, mask=mask, **options)
             hit = (row_ptr.to(self.device, non_blocking=False),
                    col_idx.to(self.device, non_blocking=False), int(col_idx.numel()))
             self._cache[key] = hit

@@ -82,6 +82,9 @@ struct FwdParams {
   int32_t num_wg;     // batch * heads * ceil(M / group)
   int32_t group;      // G: query blocks per workgroup
   int32_t key_split;  // KS: key-slice wave sets per workgroup
+  int32_t heads;      // H
+  int32_t causal;     // hide keys after each query position
+  int32_t row_stride; // row_ptr entries per head: M + 1 (one pattern per head) or 0
   float scale_log2;   // scale * log2(e)
 };
 
@@ -411,7 +414,7 @@ __device__ __forceinline__ void raw_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <typename T, int BS, int D, int G, int KS>
+template <typename T, int BS, int D, int G, int KS, bool CAUSAL>
 __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_kernel(FwdParams p) {
   using C = Cfg<T, BS, D, G, KS>;
   using L = typename C::L;
@@ -443,6 +446,8 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
   const int bh = wg / ngroups;
   const int qb = grp * G + g;
   const bool has_rows = qb < M;
+  constexpr bool causal = CAUSAL;
+  const int32_t* const row_ptr = p.row_ptr + (size_t)(bh % p.heads) * p.row_stride;
   const size_t head = (size_t)bh * p.N * D;
   const T* Q = static_cast<const T*>(p.q) + head;
   const T* K = static_cast<const T*>(p.k) + head;
@@ -460,8 +465,8 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
   const uint32_t* my_row = bitmap + (1 + g) * MW;
   int U;
   if constexpr (G == 1) {
-    const int rs = p.row_ptr[grp];
-    const int re = p.row_ptr[grp + 1];
+    const int rs = row_ptr[grp];
+    const int re = row_ptr[grp + 1];
     U = re - rs;
     if (wave == 0)
       for (int t = lane; t < U; t += kWave) list[t] = p.col_idx[rs + t];
@@ -470,11 +475,11 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
     for (int i = threadIdx.x; i < (G + 1) * MW; i += blockDim.x) bitmap[i] = 0;
     __syncthreads();
     if (has_rows && qg == 0 && ks == 0) {
-      const int rs = p.row_ptr[qb];
-      const int re = p.row_ptr[qb + 1];
+      const int rs = row_ptr[qb];
+      const int re = row_ptr[qb + 1];
       for (int t = rs + lane; t < re; t += kWave) {
         const int j = p.col_idx[t];
-        if (j >= 0 && j < M) {
+        if (j >= 0 && j < M && (!causal || j <= qb)) {
           atomicOr(&bitmap[j >> 5], 1u << (j & 31));
           atomicOr(&bitmap[(1 + g) * MW + (j >> 5)], 1u << (j & 31));
         }
@@ -522,7 +527,7 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
       chunk_base = t & ~(kWave - 1);
       const int idx = chunk_base + lane;
       chunk = idx < U ? list[idx] : -1;
-      bool sel = chunk >= 0 && chunk < M && has_rows;
+      bool sel = chunk >= 0 && chunk < M && has_rows && (!causal || chunk <= qb);
       if constexpr (G > 1)
         sel = sel && ((my_row[chunk >> 5] >> (chunk & 31)) & 1u) != 0;
       chunk_mine = __builtin_amdgcn_ballot_w64(sel);
@@ -570,13 +575,24 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
   // One entry: all S^T tiles are issued first; each 32-key step then runs its
   // softmax (VALU) while the MFMAs of the later steps are still in flight,
   // and its P.V while the next step's softmax runs.
-  auto compute = [&](unsigned char* buf) {
+  // `diag`: the entry is this wave's own query block under causal masking.
+  // Its 32-key steps after the wave's 32 rows are skipped, the step level
+  // with them is masked above the diagonal (the keys after each query).
+  auto compute = [&](unsigned char* buf, bool diag) {
     LDS_PTR(unsigned char) tile = (LDS_PTR(unsigned char))buf;
     f32x16_t sc[KSTEPS];
 #pragma unroll
     for (int st = 0; st < KSTEPS; ++st) sc[st] = O::template scores<BS, D>(qop, off, tile, 0, st);
 #pragma unroll
     for (int st = 0; st < KSTEPS; ++st) {
+      if (diag && st > qg) continue;
+      if (diag && st == qg) {
+        const int qrow = lane & 31;
+        const int h = lane >> 5;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (8 * (r / 4) + 4 * h + (r % 4) > qrow) sc[st][r] = -INFINITY;
+      }
       float mx = sc[st][0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) mx = __builtin_elementwise_maximum(mx, sc[st][r]);
@@ -625,6 +641,7 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
     else wait_vm_lgkm0<0>();
     raw_barrier();
     const bool mine = mq[0];
+    const bool diag = causal && jq[0] == qb;
 #pragma unroll
     for (int e = 0; e + 1 < NB; ++e) {
       jq[e] = jq[e + 1];
@@ -632,7 +649,7 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
     }
     jq[NB - 1] = entry_at(i + NB, mq[NB - 1]);
     if (i + NB - 1 < niter) issue(jq[NB - 2], buffer(std::integral_constant<int, (b + NB - 1) % NB>{}));
-    if (mine) compute(buffer(b_c));
+    if (mine) compute(buffer(b_c), diag);
   };
   for (int i = 0; i < niter; i += NB) {
     step(i, std::integral_constant<int, 0>{});
@@ -706,8 +723,8 @@ constexpr size_t static_lds_bytes() {  // 0 for a shape that is not instantiated
   return C::kValid ? (size_t)C::NB * C::kSliceBytes + 16 : 0;
 }
 
-template <typename T, int BS, int D, int G, int KS>
-bsa_status launch(const FwdParams& p, hipStream_t stream) {
+template <typename T, int BS, int D, int G, int KS, bool CAUSAL>
+bsa_status launch_kernel(const FwdParams& p, hipStream_t stream) {
   using C = Cfg<T, BS, D, G, KS>;
   if constexpr (!C::kValid) {
     return BSA_ERR_INVALID_ARGUMENT;
@@ -717,7 +734,7 @@ bsa_status launch(const FwdParams& p, hipStream_t stream) {
   if (dyn + static_lds_bytes<T, BS, D, G, KS>() > 64 * 1024) {
     static bool raised = false;  // one attribute call per instantiation
     if (!raised) {
-      if (hipFuncSetAttribute(reinterpret_cast<const void*>(&bsa_fwd_kernel<T, BS, D, G, KS>),
+      if (hipFuncSetAttribute(reinterpret_cast<const void*>(&bsa_fwd_kernel<T, BS, D, G, KS, CAUSAL>),
                               hipFuncAttributeMaxDynamicSharedMemorySize,
                               static_cast<int>(kMaxLds - static_lds_bytes<T, BS, D, G, KS>())) !=
           hipSuccess)
@@ -727,9 +744,15 @@ bsa_status launch(const FwdParams& p, hipStream_t stream) {
   }
   const dim3 block(kWave * C::W);
   const dim3 grid(p.num_wg);
-  hipLaunchKernelGGL((bsa_fwd_kernel<T, BS, D, G, KS>), grid, block, dyn, stream, p);
+  hipLaunchKernelGGL((bsa_fwd_kernel<T, BS, D, G, KS, CAUSAL>), grid, block, dyn, stream, p);
   return hipGetLastError() == hipSuccess ? BSA_OK : BSA_ERR_HIP;
   }
+}
+
+template <typename T, int BS, int D, int G, int KS>
+bsa_status launch(const FwdParams& p, hipStream_t stream) {
+  return p.causal != 0 ? launch_kernel<T, BS, D, G, KS, true>(p, stream)
+                       : launch_kernel<T, BS, D, G, KS, false>(p, stream);
 }
 
 // Static LDS of a shape, or 0 when the shape is not instantiated.
@@ -805,8 +828,8 @@ namespace {
 bsa_status forward_impl(const void* q, const void* k, const void* v, void* o, float* lse,
                         int32_t batch, int32_t heads, int32_t seq_len, int32_t head_dim,
                         int32_t block_size, int32_t dtype, const int32_t* row_ptr,
-                        const int32_t* col_idx, int64_t nnz, float scale, int32_t group,
-                        int32_t key_split, void* stream) {
+                        const int32_t* col_idx, int64_t nnz, float scale, int32_t flags,
+                        int32_t group, int32_t key_split, void* stream) {
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || row_ptr == nullptr ||
       col_idx == nullptr)
     return BSA_ERR_NULL_POINTER;
@@ -815,8 +838,12 @@ bsa_status forward_impl(const void* q, const void* k, const void* v, void* o, fl
   if (head_dim != 64 && head_dim != 128) return BSA_ERR_INVALID_ARGUMENT;
   if (batch <= 0 || heads <= 0 || seq_len <= 0 || seq_len % block_size != 0) return BSA_ERR_SHAPE;
   if (!(scale == scale) || std::isinf(scale)) return BSA_ERR_INVALID_ARGUMENT;
+  if ((flags & ~(BSA_FORWARD_CAUSAL | BSA_FORWARD_PATTERN_PER_HEAD)) != 0)
+    return BSA_ERR_INVALID_ARGUMENT;
+  const bool per_head = (flags & BSA_FORWARD_PATTERN_PER_HEAD) != 0;
   const int64_t M = seq_len / block_size;
-  if (nnz < M || nnz > M * M) return BSA_ERR_SHAPE;
+  const int64_t patterns = per_head ? heads : 1;
+  if (nnz < patterns * M || nnz > patterns * M * M) return BSA_ERR_SHAPE;
   if ((int64_t)batch * heads * seq_len > INT32_MAX) return BSA_ERR_SHAPE;  // LSE/row indices
   const uintptr_t align = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
                           reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(o);
@@ -832,6 +859,9 @@ bsa_status forward_impl(const void* q, const void* k, const void* v, void* o, fl
   p.col_idx = col_idx;
   p.M = static_cast<int32_t>(M);
   p.N = seq_len;
+  p.heads = heads;
+  p.causal = (flags & BSA_FORWARD_CAUSAL) != 0 ? 1 : 0;
+  p.row_stride = per_head ? static_cast<int32_t>(M + 1) : 0;
   if (group == 0 && key_split == 0) {
     choose_shape((int64_t)batch * heads * M, block_size, head_dim, dtype, (int)M, &p.group,
                  &p.key_split);
@@ -864,15 +894,15 @@ extern "C" bsa_status bsa_forward(const void* q, const void* k, const void* v, v
                                   const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz,
                                   float scale, void* stream) {
   return forward_impl(q, k, v, o, lse, batch, heads, seq_len, head_dim, block_size, dtype,
-                      row_ptr, col_idx, nnz, scale, 0, 0, stream);
+                      row_ptr, col_idx, nnz, scale, 0, 0, 0, stream);
 }
 
 extern "C" bsa_status bsa_forward_ex(const void* q, const void* k, const void* v, void* o,
                                      float* lse, int32_t batch, int32_t heads, int32_t seq_len,
                                      int32_t head_dim, int32_t block_size, int32_t dtype,
                                      const int32_t* row_ptr, const int32_t* col_idx,
-                                     int64_t nnz, float scale, int32_t group,
+                                     int64_t nnz, float scale, int32_t flags, int32_t group,
                                      int32_t key_split, void* stream) {
   return forward_impl(q, k, v, o, lse, batch, heads, seq_len, head_dim, block_size, dtype,
-                      row_ptr, col_idx, nnz, scale, group, key_split, stream);
+                      row_ptr, col_idx, nnz, scale, flags, group, key_split, stream);
 }

@@ -8,6 +8,14 @@
 // before the launch; it is stored here as CSR (row_ptr / col_idx) because the
 // number of selected blocks differs from row to row.
 //
+// Further kinds: a dilated sliding window and BigBird's local + global +
+// random blocks (the pattern configuration examples of the Ascend CANN
+// SparseFlashAttention article; BigBird also in section 2.2 of the log-linear
+// page).  The random blocks come from SplitMix64 used as a counter-based
+// generator (output n of the sequence started at `seed` is mix(seed + n * g),
+// g = 0x9e3779b97f4a7c15), so any row can be drawn on its own.  With
+// `causal`, blocks after the query block are dropped.
+//
 // Each row is assembled as a short candidate list (O(log M) entries for the
 // rule), sorted and deduplicated; a mask row is scanned in order.
 
@@ -26,12 +34,70 @@ int ceil_log2_int(int64_t m) {
 }
 
 struct Rule {
+  int32_t kind = BSA_PATTERN_LOGLINEAR;
   int32_t M = 0;
   int32_t bs = 0;
   int32_t radius = 1;
   int32_t k_max = 0;
+  int32_t window = 0;
+  int32_t dilation = 1;
+  int32_t num_random = 0;
+  uint64_t seed = 0;
   std::vector<int32_t> globals;
 };
+
+// Output n (n >= 1) of SplitMix64 started at state `seed`.
+uint64_t splitmix64_at(uint64_t seed, uint64_t n) {
+  uint64_t z = seed + n * 0x9e3779b97f4a7c15ull;
+  z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+  z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+  return z ^ (z >> 31);
+}
+
+void sort_unique(std::vector<int32_t>& row) {
+  std::sort(row.begin(), row.end());
+  row.erase(std::unique(row.begin(), row.end()), row.end());
+}
+
+// Dilated window: {i + dilation * t, |t| <= window} and the globals.
+void dilated_row(const Rule& r, int32_t i, std::vector<int32_t>& row) {
+  row.clear();
+  for (int64_t t = -int64_t{r.window}; t <= r.window; ++t) {
+    const int64_t j = int64_t{i} + t * r.dilation;
+    if (j >= 0 && j < r.M) row.push_back(static_cast<int32_t>(j));
+  }
+  for (int32_t g : r.globals) row.push_back(g);
+  sort_unique(row);
+}
+
+// BigBird: local {i - r .. i + r}, the globals, then num_random new blocks:
+// candidate c is splitmix64_at(seed, i * 2^32 + c + 1) mod M, skipping blocks
+// already in the row, until num_random are added, the row is full or
+// 64 M + 1024 candidates have been drawn.
+void bigbird_row(const Rule& r, int32_t i, std::vector<int32_t>& row) {
+  row.clear();
+  for (int64_t j = int64_t{i} - r.radius; j <= int64_t{i} + r.radius; ++j)
+    if (j >= 0 && j < r.M) row.push_back(static_cast<int32_t>(j));
+  for (int32_t g : r.globals) row.push_back(g);
+  sort_unique(row);
+  std::vector<char> in(static_cast<size_t>(r.M), 0);
+  for (int32_t j : row) in[static_cast<size_t>(j)] = 1;
+  int32_t added = 0;
+  int64_t have = static_cast<int64_t>(row.size());
+  // At most 64 M + 1024 candidates (a bound the draw never reaches in practice:
+  // it keeps the loop finite whatever the generator's residues).
+  const uint64_t cap = 64 * static_cast<uint64_t>(r.M) + 1024;
+  for (uint64_t c = 0; added < r.num_random && have < r.M && c < cap; ++c) {
+    const uint64_t n = (static_cast<uint64_t>(i) << 32) + c + 1;
+    const int32_t j = static_cast<int32_t>(splitmix64_at(r.seed, n) % static_cast<uint64_t>(r.M));
+    if (in[static_cast<size_t>(j)]) continue;
+    in[static_cast<size_t>(j)] = 1;
+    row.push_back(j);
+    ++added;
+    ++have;
+  }
+  sort_unique(row);
+}
 
 // Candidate blocks of one query block under the log-linear rule, ascending
 // and unique, written into `row` (cleared first).
@@ -50,8 +116,7 @@ void loglinear_row(const Rule& r, int32_t i, std::vector<int32_t>& row) {
     add(int64_t{i} + stride);
   }
   for (int32_t g : r.globals) add(g);
-  std::sort(row.begin(), row.end());
-  row.erase(std::unique(row.begin(), row.end()), row.end());
+  sort_unique(row);
 }
 
 }  // namespace
@@ -59,28 +124,40 @@ void loglinear_row(const Rule& r, int32_t i, std::vector<int32_t>& row) {
 extern "C" bsa_status bsa_build_pattern(const bsa_pattern_desc* desc, int32_t* row_ptr,
                                         int32_t* col_idx, int64_t col_cap, int64_t* nnz_out) {
   if (desc == nullptr || nnz_out == nullptr) return BSA_ERR_NULL_POINTER;
-  if (desc->kind != BSA_PATTERN_LOGLINEAR && desc->kind != BSA_PATTERN_BLOCK_MASK)
+  if (desc->kind != BSA_PATTERN_LOGLINEAR && desc->kind != BSA_PATTERN_BLOCK_MASK &&
+      desc->kind != BSA_PATTERN_DILATED && desc->kind != BSA_PATTERN_BIGBIRD)
     return BSA_ERR_INVALID_ARGUMENT;
   if (desc->seq_len <= 0 || desc->block_size <= 0 || desc->seq_len % desc->block_size != 0)
     return BSA_ERR_SHAPE;
   const int32_t M = desc->seq_len / desc->block_size;
 
   Rule rule;
-  if (desc->kind == BSA_PATTERN_LOGLINEAR) {
-    rule.M = M;
-    rule.bs = desc->block_size;
+  rule.kind = desc->kind;
+  rule.M = M;
+  rule.bs = desc->block_size;
+  if (desc->kind == BSA_PATTERN_BLOCK_MASK) {
+    if (desc->mask == nullptr) return BSA_ERR_NULL_POINTER;
+  } else {
     rule.radius = desc->local_radius < 0 ? 1 : desc->local_radius;
     rule.k_max = desc->k_max < 0 ? ceil_log2_int(M) : desc->k_max;
+    if (desc->kind == BSA_PATTERN_DILATED) {
+      if (desc->window < 0 || desc->dilation < 1) return BSA_ERR_INVALID_ARGUMENT;
+      rule.window = desc->window;
+      rule.dilation = desc->dilation;
+    }
+    if (desc->kind == BSA_PATTERN_BIGBIRD) {
+      if (desc->num_random < 0) return BSA_ERR_INVALID_ARGUMENT;
+      rule.num_random = desc->num_random;
+      rule.seed = desc->seed;
+    }
     if (desc->num_global < 0) {
-      rule.globals = {0, M / 2, M - 1};
+      if (desc->kind == BSA_PATTERN_LOGLINEAR) rule.globals = {0, M / 2, M - 1};
     } else {
       if (desc->num_global > 0 && desc->global_blocks == nullptr) return BSA_ERR_NULL_POINTER;
       rule.globals.assign(desc->global_blocks, desc->global_blocks + desc->num_global);
     }
     for (int32_t g : rule.globals)
       if (g < 0 || g >= M) return BSA_ERR_INDEX_RANGE;
-  } else if (desc->mask == nullptr) {
-    return BSA_ERR_NULL_POINTER;
   }
 
   // Pass 1 counts, pass 2 (when col_idx is given and large enough) fills.
@@ -97,12 +174,18 @@ extern "C" bsa_status bsa_build_pattern(const bsa_pattern_desc* desc, int32_t* r
     for (int32_t i = 0; i < M; ++i) {
       if (desc->kind == BSA_PATTERN_LOGLINEAR) {
         loglinear_row(rule, i, row);
+      } else if (desc->kind == BSA_PATTERN_DILATED) {
+        dilated_row(rule, i, row);
+      } else if (desc->kind == BSA_PATTERN_BIGBIRD) {
+        bigbird_row(rule, i, row);
       } else {
         row.clear();
         const uint8_t* mrow = desc->mask + static_cast<int64_t>(i) * M;
         for (int32_t j = 0; j < M; ++j)
           if (mrow[j] != 0) row.push_back(j);
       }
+      if (desc->causal != 0)
+        row.erase(std::upper_bound(row.begin(), row.end(), i), row.end());
       if (row.empty()) return BSA_ERR_EMPTY_ROW;
       if (pass == 1) std::copy(row.begin(), row.end(), col_idx + pos);
       pos += static_cast<int64_t>(row.size());

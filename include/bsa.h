@@ -36,7 +36,9 @@ typedef enum bsa_status {
 
 typedef enum bsa_pattern_kind {
   BSA_PATTERN_LOGLINEAR = 0,  /* built-in log-linear rule, [P1] section 3.1 */
-  BSA_PATTERN_BLOCK_MASK = 1  /* user [M, M] block mask, [P2] item 1, [P3] "Block-Sparse" */
+  BSA_PATTERN_BLOCK_MASK = 1, /* user [M, M] block mask, [P2] item 1, [P3] "Block-Sparse" */
+  BSA_PATTERN_DILATED = 2,    /* dilated sliding window, [P3] pattern configuration examples */
+  BSA_PATTERN_BIGBIRD = 3     /* local + global + random blocks, [P1] section 2.2, [P3] same */
 } bsa_pattern_kind;
 
 typedef enum bsa_dtype {
@@ -48,30 +50,52 @@ typedef enum bsa_dtype {
  * Pattern descriptor (host memory, read only during the call).
  *
  * Notation of [P1] section 3.1: N = seq_len, bs = block_size, M = N / bs,
- * query block i ("row_i").
+ * query block i ("row_i").  Every kind keeps only blocks in [0, M).
  *
  * BSA_PATTERN_LOGLINEAR selects, for every query block i,
  *   local      {i - r, ..., i + r}                 r = local_radius
  *   log-stride {i - floor(2^k / bs), i + floor(2^k / bs)}  k = 1 .. k_max
  *   global     the global blocks (default {0, M/2, M-1})
- * keeping only blocks in [0, M).  [P1] section 3.1 prints r = 1,
- * k_max = ceil(log2 M) and the anchors {0, M/2, M-1} (worked example N = 4096,
- * bs = 32, M = 128, k = 1..7, anchors {0, 64, 127}); the anchors are added as
- * columns of every row, and anchor rows are not made dense.
+ * [P1] section 3.1 prints r = 1, k_max = ceil(log2 M) and the anchors
+ * {0, M/2, M-1} (worked example N = 4096, bs = 32, M = 128, k = 1..7, anchors
+ * {0, 64, 127}); the anchors are added as columns of every row, and anchor
+ * rows are not made dense.  [P1] section 6.1's seven anchors are a
+ * seven-entry global_blocks list.
  *
  * BSA_PATTERN_BLOCK_MASK selects block j for query block i iff
  * mask[i * M + j] != 0.
+ *
+ * BSA_PATTERN_DILATED selects {i + dilation * t : t = -window .. window} and
+ * the global blocks (default: none).
+ *
+ * BSA_PATTERN_BIGBIRD selects the local blocks {i - r .. i + r}, the global
+ * blocks (default: none) and num_random further blocks drawn for row i:
+ * candidate c = 0, 1, 2, ... is block x_c mod M, where x_c is output number
+ * (i * 2^32 + c + 1) of SplitMix64 started at state `seed` (state advances by
+ * 0x9e3779b97f4a7c15; output mixes with the shifts 30, 27, 31 and the
+ * multipliers 0xbf58476d1ce4e5b9, 0x94d049bb133111eb); candidates already in
+ * the row are skipped, and the draw stops after num_random new blocks, when
+ * the row holds all M blocks, or after 64 M + 1024 candidates.  Global
+ * blocks are columns only.
+ *
+ * causal != 0 then drops every block j > i from row i (the diagonal block
+ * stays; inside it the causal forward masks the later keys).
  */
 typedef struct bsa_pattern_desc {
   int32_t kind;                 /* bsa_pattern_kind */
   int32_t seq_len;              /* N > 0, multiple of block_size */
   int32_t block_size;           /* bs > 0 */
-  int32_t local_radius;         /* LOGLINEAR: r >= 0; < 0 selects the default 1 */
+  int32_t local_radius;         /* LOGLINEAR, BIGBIRD: r >= 0; < 0 selects the default 1 */
   int32_t k_max;                /* LOGLINEAR: >= 0; < 0 selects ceil(log2 M) */
-  int32_t num_global;           /* LOGLINEAR: < 0 selects {0, M/2, M-1};
+  int32_t num_global;           /* < 0 selects the kind's default global blocks;
                                    >= 0 uses global_blocks[0 .. num_global) */
-  const int32_t* global_blocks; /* LOGLINEAR: host array, each in [0, M) */
+  const int32_t* global_blocks; /* host array, each in [0, M) */
   const uint8_t* mask;          /* BLOCK_MASK: host array, M * M bytes, row-major */
+  int32_t causal;               /* != 0: keep only blocks j <= i */
+  int32_t window;               /* DILATED: window >= 0 (in steps of `dilation`) */
+  int32_t dilation;             /* DILATED: dilation >= 1 */
+  int32_t num_random;           /* BIGBIRD: random blocks per row, >= 0 */
+  uint64_t seed;                /* BIGBIRD: generator seed */
 } bsa_pattern_desc;
 
 /*
@@ -90,7 +114,8 @@ typedef struct bsa_pattern_desc {
  *          BSA_ERR_BUFFER_TOO_SMALL.
  *
  * Errors: BSA_ERR_NULL_POINTER (desc, nnz_out, or mask for BLOCK_MASK, or
- * global_blocks when num_global > 0), BSA_ERR_INVALID_ARGUMENT (unknown kind),
+ * global_blocks when num_global > 0), BSA_ERR_INVALID_ARGUMENT (unknown kind,
+ * window < 0, dilation < 1, num_random < 0),
  * BSA_ERR_SHAPE (sizes, divisibility, nnz > INT32_MAX), BSA_ERR_INDEX_RANGE
  * (global block outside [0, M)), BSA_ERR_EMPTY_ROW (a mask row with no block;
  * [P1] section 5.1 traces NaN outputs to such rows), BSA_ERR_BUFFER_TOO_SMALL.
@@ -137,30 +162,46 @@ bsa_status bsa_forward(const void* q, const void* k, const void* v, void* o, flo
                        int32_t block_size, int32_t dtype, const int32_t* row_ptr,
                        const int32_t* col_idx, int64_t nnz, float scale, void* stream);
 
+/* Flags of bsa_forward_ex. */
+typedef enum bsa_forward_flags {
+  /* Causal: query row r sees only keys at positions <= r.  Pattern blocks
+   * j > i are skipped, the diagonal block is masked inside.  Every row must
+   * reach its own block (bsa_build_pattern with causal set keeps it whenever
+   * the row selects it).  A row with no visible key gets O = 0 and
+   * LSE = -inf. */
+  BSA_FORWARD_CAUSAL = 1,
+  /* One pattern per head: row_ptr holds heads * (M + 1) entries, head h's
+   * rows at row_ptr[h * (M + 1) ..], each an offset into the one col_idx
+   * array (nnz entries in all); every batch uses the same per-head patterns. */
+  BSA_FORWARD_PATTERN_PER_HEAD = 2
+} bsa_forward_flags;
+
 /*
- * bsa_forward_ex -- bsa_forward with an explicit workgroup shape.
+ * bsa_forward_ex -- bsa_forward with flags and an explicit workgroup shape.
  *
  * Same computation, arguments and errors as bsa_forward, plus:
+ * flags      a bitwise OR of bsa_forward_flags (0: exactly bsa_forward);
  * group      query blocks sharing one workgroup's K/V tiles: 1, 2 or 4;
  * key_split  wave sets that split each query block's CSR row (>= 1), merged
  *            through LDS before the store;
  * group == key_split == 0 selects the shape bsa_forward would use.  A shape
  * needing more than 8 waves (block_size / 32 * group * key_split) or more
- * LDS than a workgroup may use returns BSA_ERR_INVALID_ARGUMENT.  Every shape
- * computes the same result up to floating-point summation order; this entry
- * point exists to tune and to test the shapes.
+ * LDS than a workgroup may use returns BSA_ERR_INVALID_ARGUMENT, as do
+ * unknown flags.  With BSA_FORWARD_PATTERN_PER_HEAD, nnz is the total over
+ * the heads and must satisfy heads * M <= nnz <= heads * M * M.  Every shape
+ * computes the same result up to floating-point summation order.
  */
 bsa_status bsa_forward_ex(const void* q, const void* k, const void* v, void* o, float* lse,
                           int32_t batch, int32_t heads, int32_t seq_len, int32_t head_dim,
                           int32_t block_size, int32_t dtype, const int32_t* row_ptr,
-                          const int32_t* col_idx, int64_t nnz, float scale, int32_t group,
-                          int32_t key_split, void* stream);
+                          const int32_t* col_idx, int64_t nnz, float scale, int32_t flags,
+                          int32_t group, int32_t key_split, void* stream);
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* bsa_status_string(int32_t status);
 
 /* ABI version of this header: bump on any incompatible change. */
-#define BSA_ABI_VERSION 1
+#define BSA_ABI_VERSION 2
 int32_t bsa_abi_version(void);
 
 #ifdef __cplusplus

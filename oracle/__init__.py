@@ -9,8 +9,9 @@ nothing from it.
 It is deliberately plain and slow:
 
 * ``oracle.pattern`` -- the block-selection rules written out step by step
-  (log-linear rule, local+global token mask and its block conversion) and the
-  CSR encoding of a block mask, in Python integers.
+  (log-linear rule, local+global token mask and its block conversion, dilated
+  window, BigBird with its counter-based draw, causal filtering) and the CSR
+  encoding of a block mask, in Python integers.
 * ``oracle.attention`` -- dense softmax attention in float64 with an explicit
   block mask expanded to tokens, one query block at a time.
 
@@ -37,6 +38,10 @@ docstring; none is "parity unpinned".
 from .pattern import (
     ceil_log2,
     loglinear_block_sets,
+    dilated_block_sets,
+    bigbird_block_sets,
+    causal_block_sets,
+    splitmix64_at,
     block_mask_from_sets,
     csr_from_block_mask,
     block_mask_from_csr,
@@ -48,6 +53,10 @@ from .attention import block_sparse_attention_head, block_sparse_attention
 __all__ = [
     "ceil_log2",
     "loglinear_block_sets",
+    "dilated_block_sets",
+    "bigbird_block_sets",
+    "causal_block_sets",
+    "splitmix64_at",
     "block_mask_from_sets",
     "csr_from_block_mask",
     "block_mask_from_csr",

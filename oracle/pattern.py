@@ -16,12 +16,34 @@ Readings of the pages taken here (each one is also listed in the design notes):
   lists them in the set of K blocks each token connects to).
 * The selected set of a row is a set: duplicates collapse, CSR columns ascend.
 
+Further rules (the pattern configuration examples of the Ascend CANN
+SparseFlashAttention article: a sliding window with dilation and BigBird's
+local + global + random blocks; BigBird also in [P1] section 2.2):
+
+* Dilated window: S(i) = {i + dilation * t : |t| <= window} in [0, M), plus the
+  global blocks given.
+* BigBird: local {i - r .. i + r}, the global blocks given (columns only, as
+  for the log-linear anchors) and ``num_random`` further blocks.  The pages
+  name no generator; the draw is SplitMix64 (Steele, Lea and Flood, "Fast
+  splittable pseudorandom number generators", 2014, in the form of Vigna's
+  reference code) read as a counter-based generator: output n of the
+  sequence started at ``seed``.  Candidate c of row i is output
+  i * 2**32 + c + 1 modulo M; blocks already in the row are skipped; the draw
+  stops after ``num_random`` new blocks, a full row, or 64 M + 1024
+  candidates.
+* Causal: row i keeps only blocks j <= i.
+
 Pins (tests/test_oracle.py): the hand-derived rows and row-size histogram of
 the page's worked example N=4096, block 32 (tests/golden/), the hand-derived
 tiny case, a closed-form offset description of every log-linear row, the
 O(log M) row bound, own-block membership and symmetry; the ±4 block band that
 the page's ±256-token window produces at block 64 (closed form 2080/4096
-coverage); CSR round trips.
+coverage); CSR round trips; SplitMix64's published first outputs from seed 0;
+a dilated window of dilation 1 equal to a plain band, hand-derived dilated
+rows; BigBird row contents (local and global blocks present, exactly
+``num_random`` others, a full row when more are asked than exist), seed
+dependence and the uniformity of the draw; causal filtering against the
+lower triangle.
 """
 
 from __future__ import annotations
@@ -82,6 +104,84 @@ def loglinear_block_sets(seq_len: int, block_size: int, *, local_radius: int = 1
             selected.add(int(g))
         sets.append(selected)
     return sets
+
+
+_GOLDEN = 0x9E3779B97F4A7C15
+_MASK64 = (1 << 64) - 1
+
+
+def splitmix64_at(seed: int, n: int) -> int:
+    """Output number n (n >= 1) of SplitMix64 started at state ``seed``.
+
+    The generator adds the golden-ratio constant 0x9e3779b97f4a7c15 to its
+    state per step and returns a mix of the new state: xor-shift 30, multiply
+    by 0xbf58476d1ce4e5b9, xor-shift 27, multiply by 0x94d049bb133111eb,
+    xor-shift 31 (all modulo 2**64).  After n steps the state is
+    seed + n * golden, so any output can be formed directly.
+    """
+    z = (seed + n * _GOLDEN) & _MASK64
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & _MASK64
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & _MASK64
+    return z ^ (z >> 31)
+
+
+def dilated_block_sets(seq_len: int, block_size: int, *, window: int, dilation: int,
+                       global_blocks=()) -> list[set[int]]:
+    """Dilated sliding window over blocks: {i + dilation * t : |t| <= window}."""
+    if block_size <= 0 or seq_len <= 0 or seq_len % block_size != 0:
+        raise ValueError("seq_len must be a positive multiple of block_size")
+    if window < 0 or dilation < 1:
+        raise ValueError("window >= 0 and dilation >= 1 required")
+    M = seq_len // block_size
+    sets = []
+    for i in range(M):
+        selected = set()
+        for t in range(-window, window + 1):
+            j = i + dilation * t
+            if 0 <= j < M:
+                selected.add(j)
+        for g in global_blocks:
+            if not 0 <= g < M:
+                raise ValueError(f"global block {g} outside [0, {M})")
+            selected.add(int(g))
+        sets.append(selected)
+    return sets
+
+
+def bigbird_block_sets(seq_len: int, block_size: int, *, num_random: int, seed: int,
+                       local_radius: int = 1, global_blocks=()) -> list[set[int]]:
+    """Local + global + random blocks per row (see the module notes for the draw)."""
+    if block_size <= 0 or seq_len <= 0 or seq_len % block_size != 0:
+        raise ValueError("seq_len must be a positive multiple of block_size")
+    if num_random < 0:
+        raise ValueError("num_random >= 0 required")
+    M = seq_len // block_size
+    sets = []
+    for i in range(M):
+        selected = set()
+        for j in range(i - local_radius, i + local_radius + 1):
+            if 0 <= j < M:
+                selected.add(j)
+        for g in global_blocks:
+            if not 0 <= g < M:
+                raise ValueError(f"global block {g} outside [0, {M})")
+            selected.add(int(g))
+        added = 0
+        c = 0
+        while added < num_random and len(selected) < M and c < 64 * M + 1024:
+            j = splitmix64_at(seed, (i << 32) + c + 1) % M
+            c += 1
+            if j in selected:
+                continue
+            selected.add(j)
+            added += 1
+        sets.append(selected)
+    return sets
+
+
+def causal_block_sets(sets: list[set[int]]) -> list[set[int]]:
+    """Row i keeps only blocks j <= i."""
+    return [{j for j in s if j <= i} for i, s in enumerate(sets)]
 
 
 def block_mask_from_sets(sets: list[set[int]]) -> np.ndarray:

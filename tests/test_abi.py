@@ -44,7 +44,7 @@ def test_library_has_gfx950_code_object():
 
 
 def test_abi_version_and_status_strings():
-    assert bsa.abi_version() == 1
+    assert bsa.abi_version() == 2
     for code in range(8):
         assert bsa.status_string(code).startswith("BSA_")
     assert bsa.status_string(99) == "BSA_ERR_UNKNOWN"
@@ -89,3 +89,31 @@ def test_python_forward_rejects_cpu_tensors():
     rp = torch.zeros(3, dtype=torch.int32)
     with pytest.raises(ValueError):
         bsa.forward(q, q, q, rp, rp, 32)
+
+
+def _fwd_ex(flags, **over):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=8, N=4096, d=64, bs=32,
+                dtype=1, row_ptr=FAKE, col_idx=FAKE, nnz=1251, scale=0.0, stream=None)
+    args.update(over)
+    lib = bsa._load()
+    return lib.bsa_forward_ex(args["q"], args["k"], args["v"], args["o"], args["lse"], args["B"],
+                              args["H"], args["N"], args["d"], args["bs"], args["dtype"],
+                              args["row_ptr"], args["col_idx"], args["nnz"],
+                              ctypes.c_float(args["scale"]), flags, 0, 0, args["stream"])
+
+
+@pytest.mark.parametrize("flags", [4, 8, -1, 1 << 30])
+def test_forward_ex_unknown_flags(flags):
+    assert _fwd_ex(flags) == 2
+
+
+def test_forward_ex_per_head_nnz_range():
+    # 8 heads of M = 128: nnz must lie in [8 * 128, 8 * 128 * 128]
+    assert _fwd_ex(2, nnz=8 * 128 - 1) == 3
+    assert _fwd_ex(2, nnz=8 * 128 * 128 + 1) == 3
+    assert _fwd_ex(3, nnz=1251, q=None) == 1
+
+
+def test_forward_ex_bad_shape_flags_combination():
+    assert _fwd_ex(1, d=96) == 2
+    assert _fwd_ex(1, N=4010) == 3

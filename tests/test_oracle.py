@@ -309,3 +309,133 @@ def test_oracle_imports_nothing_from_the_library():
         if name.endswith(".py"):
             src = open(os.path.join(root, name)).read()
             assert not re.search(r"block_sparse_attention_csr_amd|synthetic_inputs", src), name
+
+
+# ----------------------------------------------------------------------------- further rules
+
+
+def test_splitmix64_published_outputs():
+    # First three outputs of the SplitMix64 reference generator started at 0.
+    assert [oracle.splitmix64_at(0, n) for n in (1, 2, 3)] == [
+        0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]
+
+
+@pytest.mark.parametrize("M,w", [(1, 0), (7, 1), (16, 3), (33, 5)])
+def test_dilated_dilation_one_is_a_band(M, w):
+    sets = oracle.dilated_block_sets(M * 32, 32, window=w, dilation=1)
+    for i, s in enumerate(sets):
+        assert s == {j for j in range(M) if abs(i - j) <= w}
+
+
+def test_dilated_hand_derived():
+    # M = 10, window 2, dilation 3: i + 3t for t = -2..2, kept inside [0, 10).
+    sets = oracle.dilated_block_sets(640, 64, window=2, dilation=3)
+    assert sets[0] == {0, 3, 6}
+    assert sets[4] == {1, 4, 7}
+    assert sets[9] == {3, 6, 9}
+    with_g = oracle.dilated_block_sets(640, 64, window=1, dilation=4, global_blocks=[0, 9])
+    assert with_g[5] == {0, 1, 5, 9}
+    with pytest.raises(ValueError):
+        oracle.dilated_block_sets(640, 64, window=-1, dilation=1)
+    with pytest.raises(ValueError):
+        oracle.dilated_block_sets(640, 64, window=1, dilation=0)
+
+
+@pytest.mark.parametrize("M,r,g,nr", [(32, 1, [0], 3), (16, 0, [], 5), (8, 1, [0, 7], 100),
+                                      (64, 2, [0, 63], 0)])
+def test_bigbird_row_contents(M, r, g, nr):
+    sets = oracle.bigbird_block_sets(M * 64, 64, num_random=nr, seed=12345, local_radius=r,
+                                     global_blocks=g)
+    for i, s in enumerate(sets):
+        base = {j for j in range(i - r, i + r + 1) if 0 <= j < M} | set(g)
+        assert base <= s
+        assert len(s) == len(base) + min(nr, M - len(base))
+        assert all(0 <= j < M for j in s)
+
+
+def test_bigbird_seed_dependence_and_uniform_draw():
+    M = 64
+    a = oracle.bigbird_block_sets(M * 32, 32, num_random=3, seed=1, local_radius=0)
+    b = oracle.bigbird_block_sets(M * 32, 32, num_random=3, seed=1, local_radius=0)
+    c = oracle.bigbird_block_sets(M * 32, 32, num_random=3, seed=2, local_radius=0)
+    assert a == b and a != c
+    # Random picks over many rows spread over all offsets i - j (mod M).
+    big = oracle.bigbird_block_sets(512 * 32, 32, num_random=8, seed=7, local_radius=0)
+    counts = np.zeros(512)
+    for i, s in enumerate(big):
+        for j in s - {i}:
+            counts[(j - i) % 512] += 1
+    expected = counts.sum() / 511
+    chi2 = ((counts[1:] - expected) ** 2 / expected).sum()
+    assert chi2 < 511 + 6 * math.sqrt(2 * 511)  # 511 degrees of freedom, 6 sigma
+
+
+def test_causal_block_sets_is_the_lower_triangle():
+    sets = loglinear_block_sets(4096, 32)
+    causal = oracle.causal_block_sets(sets)
+    full = block_mask_from_sets(sets)
+    assert (block_mask_from_sets(causal) == np.tril(full)).all()
+    assert all(i in s for i, s in enumerate(causal))
+
+
+# ----------------------------------------------------------------------------- causal / per head
+
+
+def _causal_textbook(q, k, v, scale):
+    N = q.shape[0]
+    out = np.zeros_like(q)
+    lse = np.zeros(N)
+    for r in range(N):
+        s = np.array([scale * float(np.dot(q[r], k[j])) for j in range(r + 1)])
+        m = s.max()
+        p = np.exp(s - m)
+        out[r] = (p[:, None] * v[: r + 1]).sum(axis=0) / p.sum()
+        lse[r] = m + math.log(p.sum())
+    return out, lse
+
+
+def test_causal_all_ones_equals_causal_sdpa_and_textbook():
+    rng = np.random.default_rng(3)
+    N, d, bs = 96, 16, 32
+    q, k, v = (rng.standard_normal((N, d)) for _ in range(3))
+    o, lse = block_sparse_attention_head(q, k, v, np.ones((3, 3)), bs, causal=True)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        *(torch.from_numpy(x)[None, None] for x in (q, k, v)), is_causal=True)[0, 0].numpy()
+    assert np.abs(o - ref).max() < 1e-12
+    o2, lse2 = _causal_textbook(q, k, v, 1 / math.sqrt(d))
+    assert np.abs(o - o2).max() < 1e-12 and np.abs(lse - lse2).max() < 1e-12
+
+
+def test_causal_zero_query_uniform_over_visible_keys():
+    rng = np.random.default_rng(4)
+    N, d, bs = 128, 8, 32
+    mask = np.array([[1, 0, 0, 0], [1, 1, 0, 0], [0, 1, 1, 0], [1, 0, 1, 1]], np.uint8)
+    v = rng.standard_normal((N, d))
+    o, lse = block_sparse_attention_head(np.zeros((N, d)), rng.standard_normal((N, d)), v, mask,
+                                         bs, causal=True)
+    for r in range(N):
+        qb = r // bs
+        keys = [j for j in range(N) if mask[qb, j // bs] and j <= r]
+        assert abs(lse[r] - math.log(len(keys))) < 1e-12
+        assert np.abs(o[r] - v[keys].mean(axis=0)).max() < 1e-12
+
+
+def test_causal_row_without_visible_keys():
+    # Query block 0 selects only block 1: with causal masking nothing is left.
+    rng = np.random.default_rng(5)
+    q, k, v = (rng.standard_normal((64, 8)) for _ in range(3))
+    o, lse = block_sparse_attention_head(q, k, v, np.array([[0, 1], [1, 1]]), 32, causal=True)
+    assert (o[:32] == 0).all() and np.isneginf(lse[:32]).all()
+    assert np.isfinite(o[32:]).all() and np.isfinite(lse[32:]).all()
+
+
+def test_per_head_masks_equal_separate_calls():
+    rng = np.random.default_rng(6)
+    B, H, N, d, bs = 2, 3, 128, 8, 32
+    q, k, v = (rng.standard_normal((B, H, N, d)) for _ in range(3))
+    masks = np.stack([random_block_mask(4, 0.5, s) for s in range(H)])
+    o, lse = block_sparse_attention(q, k, v, masks, bs)
+    for b in range(B):
+        for h in range(H):
+            o1, l1 = block_sparse_attention_head(q[b, h], k[b, h], v[b, h], masks[h], bs)
+            assert (o[b, h] == o1).all() and (lse[b, h] == l1).all()

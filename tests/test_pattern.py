@@ -125,7 +125,7 @@ def test_error_shape(N, bs):
 def test_error_buffer_too_small_reports_nnz():
     import ctypes
     lib = bsa._load()
-    desc = bsa._desc(4096, 32, None, None, None, None, [])
+    desc = bsa._desc(4096, 32, None, None, None, None, None, False, None, None, None, None, [])
     nnz = ctypes.c_int64(-1)
     buf = (ctypes.c_int32 * 10)()
     st = lib.bsa_build_pattern(ctypes.byref(desc), None, buf, 10, ctypes.byref(nnz))
@@ -138,3 +138,101 @@ def test_error_buffer_too_small_reports_nnz():
     assert lib.bsa_build_pattern(ctypes.byref(desc), None, None, 0, ctypes.byref(nnz)) == 2
     desc.kind = 1  # block mask without a mask pointer
     assert lib.bsa_build_pattern(ctypes.byref(desc), None, None, 0, ctypes.byref(nnz)) == 1
+
+
+# ----------------------------------------------------------------------------- further kinds
+
+
+def _sets_from_csr(rp, ci):
+    rp, ci = rp.numpy(), ci.numpy()
+    return [set(int(j) for j in ci[rp[i]:rp[i + 1]]) for i in range(len(rp) - 1)]
+
+
+def _check_sorted_unique(rp, ci):
+    rp, ci = rp.numpy(), ci.numpy()
+    for i in range(len(rp) - 1):
+        row = ci[rp[i]:rp[i + 1]]
+        assert (np.diff(row) > 0).all()
+
+
+@pytest.mark.parametrize("M,bs,w,dil,g", [(10, 64, 2, 3, None), (128, 32, 4, 1, [0, 127]),
+                                          (64, 64, 3, 5, [32]), (1, 32, 0, 1, None),
+                                          (200, 32, 7, 11, [0, 199])])
+def test_dilated_matches_oracle(M, bs, w, dil, g):
+    rp, ci = bsa.build_pattern(M * bs, bs, kind="dilated", window=w, dilation=dil,
+                               global_blocks=g)
+    ref = oracle.dilated_block_sets(M * bs, bs, window=w, dilation=dil, global_blocks=g or ())
+    assert _sets_from_csr(rp, ci) == ref
+    _check_sorted_unique(rp, ci)
+
+
+@pytest.mark.parametrize("M,bs,r,g,nr,seed", [(32, 64, 1, [0], 3, 0), (128, 32, 1, None, 5, 42),
+                                              (8, 32, 1, [0, 7], 100, 7),
+                                              (512, 64, 2, [0, 511], 4, 2**63 + 5),
+                                              (3, 32, 0, None, 1, 1)])
+def test_bigbird_matches_oracle(M, bs, r, g, nr, seed):
+    rp, ci = bsa.build_pattern(M * bs, bs, kind="bigbird", local_radius=r, global_blocks=g,
+                               num_random=nr, seed=seed)
+    ref = oracle.bigbird_block_sets(M * bs, bs, num_random=nr, seed=seed, local_radius=r,
+                                    global_blocks=g or ())
+    assert _sets_from_csr(rp, ci) == ref
+    _check_sorted_unique(rp, ci)
+
+
+@pytest.mark.parametrize("kind", ["loglinear", "mask", "dilated", "bigbird"])
+def test_causal_matches_oracle(kind):
+    N, bs = 4096, 32
+    M = N // bs
+    if kind == "loglinear":
+        sets = oracle.loglinear_block_sets(N, bs)
+        kw = {}
+    elif kind == "mask":
+        m = random_block_mask(M, 0.3, 9)
+        sets = [set(np.nonzero(m[i])[0].tolist()) for i in range(M)]
+        kw = {"mask": m}
+    elif kind == "dilated":
+        sets = oracle.dilated_block_sets(N, bs, window=3, dilation=2, global_blocks=[0])
+        kw = {"window": 3, "dilation": 2, "global_blocks": [0]}
+    else:
+        sets = oracle.bigbird_block_sets(N, bs, num_random=3, seed=11, global_blocks=[0])
+        kw = {"num_random": 3, "seed": 11, "global_blocks": [0]}
+    rp, ci = bsa.build_pattern(N, bs, kind=kind, causal=True, **kw)
+    assert _sets_from_csr(rp, ci) == oracle.causal_block_sets(sets)
+
+
+def test_causal_row_losing_every_block_is_an_empty_row():
+    m = np.zeros((4, 4), np.uint8)
+    m[:, 3] = 1  # every row selects only the last block
+    with pytest.raises(bsa.BsaError) as e:
+        bsa.build_pattern(128, 32, mask=m, causal=True)
+    assert e.value.status == 4
+
+
+@pytest.mark.parametrize("kw,status", [({"kind": "dilated", "window": -1, "dilation": 1}, 2),
+                                       ({"kind": "dilated", "window": 1, "dilation": 0}, 2),
+                                       ({"kind": "bigbird", "num_random": -1, "seed": 0}, 2),
+                                       ({"kind": "dilated", "window": 1, "dilation": 1,
+                                         "global_blocks": [128]}, 5),
+                                       ({"kind": "bigbird", "num_random": 1, "seed": 0,
+                                         "global_blocks": [-1]}, 5)])
+def test_new_kinds_reject_bad_input(kw, status):
+    with pytest.raises(bsa.BsaError) as e:
+        bsa.build_pattern(4096, 32, **kw)
+    assert e.value.status == status
+
+
+def test_seven_anchor_loglinear_matches_oracle():
+    M = 128
+    anchors = [0, 21, 42, 64, 85, 106, 127]
+    rp, ci = bsa.build_pattern(M * 32, 32, global_blocks=anchors)
+    assert _sets_from_csr(rp, ci) == oracle.loglinear_block_sets(M * 32, 32, global_blocks=anchors)
+
+
+def test_stack_head_patterns_offsets():
+    a = bsa.build_pattern(1024, 32)
+    b = bsa.build_pattern(1024, 32, kind="dilated", window=2, dilation=2)
+    rp, ci = bsa.stack_head_patterns([a, b])
+    M = 32
+    assert rp.numel() == 2 * (M + 1) and ci.numel() == a[1].numel() + b[1].numel()
+    assert (rp[:M + 1] == a[0]).all() and (rp[M + 1:] == b[0] + a[1].numel()).all()
+    assert (ci[:a[1].numel()] == a[1]).all() and (ci[a[1].numel():] == b[1]).all()
