@@ -14,6 +14,7 @@ It is deliberately plain and slow:
   encoding of a block mask, in Python integers.
 * ``oracle.attention`` -- dense softmax attention in float64 with an explicit
   block mask expanded to tokens, one query block at a time.
+* ``oracle.backward`` -- the plain gradients dQ, dK, dV of that forward.
 
 Sources (web pages; cited by title and section):
 
@@ -49,6 +50,7 @@ from .pattern import (
     token_mask_to_block_mask,
 )
 from .attention import block_sparse_attention_head, block_sparse_attention
+from .backward import block_sparse_attention_backward_head, block_sparse_attention_backward
 
 __all__ = [
     "ceil_log2",
@@ -64,4 +66,6 @@ __all__ = [
     "token_mask_to_block_mask",
     "block_sparse_attention_head",
     "block_sparse_attention",
+    "block_sparse_attention_backward_head",
+    "block_sparse_attention_backward",
 ]

@@ -439,3 +439,60 @@ def test_per_head_masks_equal_separate_calls():
         for h in range(H):
             o1, l1 = block_sparse_attention_head(q[b, h], k[b, h], v[b, h], masks[h], bs)
             assert (o[b, h] == o1).all() and (lse[b, h] == l1).all()
+
+
+# ----------------------------------------------------------------------------- backward
+
+
+def _loss(q, k, v, g, mask, bs, causal):
+    o, _ = block_sparse_attention_head(q, k, v, mask, bs, causal=causal)
+    return float((g * o).sum())
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_finite_differences(causal):
+    rng = np.random.default_rng(8)
+    N, d, bs = 24, 3, 8
+    mask = np.array([[1, 0, 1], [1, 1, 0], [0, 1, 1]], np.uint8)
+    q, k, v, g = (rng.standard_normal((N, d)) for _ in range(4))
+    dq, dk, dv, _ = oracle.block_sparse_attention_backward_head(q, k, v, g, mask, bs,
+                                                                causal=causal)
+    eps = 1e-6
+    for x, grad in ((q, dq), (k, dk), (v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            x0 = x[idx]
+            x[idx] = x0 + eps
+            lp = _loss(q, k, v, g, mask, bs, causal)
+            x[idx] = x0 - eps
+            lm = _loss(q, k, v, g, mask, bs, causal)
+            x[idx] = x0
+            num[idx] = (lp - lm) / (2 * eps)
+        assert np.abs(num - grad).max() < 1e-7 * max(1.0, np.abs(grad).max())
+
+
+def _sdpa_grads(q, k, v, g, attn_mask=None, is_causal=False):
+    ts = [torch.from_numpy(x).clone().requires_grad_(True) for x in (q, k, v)]
+    o = torch.nn.functional.scaled_dot_product_attention(
+        *(t[None, None] for t in ts), attn_mask=attn_mask, is_causal=is_causal)[0, 0]
+    (o * torch.from_numpy(g)).sum().backward()
+    return [t.grad.numpy() for t in ts], o.detach().numpy()
+
+
+@pytest.mark.parametrize("kind", ["ones", "causal", "mask"])
+def test_backward_matches_sdpa_autograd(kind):
+    rng = np.random.default_rng(9)
+    N, d, bs = 128, 16, 32
+    q, k, v, g = (rng.standard_normal((N, d)) for _ in range(4))
+    if kind == "mask":
+        mask = random_block_mask(4, 0.5, 3)
+        token = torch.from_numpy(np.kron(mask, np.ones((bs, bs))) != 0)
+        (gq, gk, gv), o = _sdpa_grads(q, k, v, g, attn_mask=token)
+    else:
+        mask = np.ones((4, 4), np.uint8)
+        (gq, gk, gv), o = _sdpa_grads(q, k, v, g, is_causal=kind == "causal")
+    dq, dk, dv, dvec = oracle.block_sparse_attention_backward_head(q, k, v, g, mask, bs,
+                                                                   causal=kind == "causal")
+    for a, b in ((dq, gq), (dk, gk), (dv, gv)):
+        assert np.abs(a - b).max() < 1e-12 * max(1.0, np.abs(b).max())
+    assert np.abs(dvec - (g * o).sum(axis=1)).max() < 1e-12
