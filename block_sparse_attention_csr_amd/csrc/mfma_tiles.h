@@ -1,0 +1,351 @@
+// Shared device code of the forward and backward kernels for gfx950:
+// vector types, the LDS tile layout of K/V (or Q/dO) blocks, the MFMA
+// operand loaders and products on those tiles, and the copy/barrier
+// primitives of the LDS pipelines.
+//
+// MFMA layouts (v_mfma_f32_32x32x16_bf16): accumulator lane l, register i
+// holds row 8 (i / 4) + 4 (l / 32) + i % 4, column l % 32.  A product
+// X^T = R C^T keeps the rows R of a tile (keys, or queries) as MFMA rows read
+// from LDS and the 32 rows C a wave owns in registers as the B operand, so
+// every lane holds one column (one query, or one key).  A product
+// Y^T = T^T X packs X's accumulator (bf16) as the B operand directly, with the
+// matching key order kappa(h, j) = 16 sc + 8 (j / 4) + 4 h + j % 4 taken on
+// the A side through transposing LDS reads of tile T.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <type_traits>
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+#define LDS_PTR(T) __attribute__((address_space(3))) T*
+
+
+constexpr int kWave = 64;
+constexpr int kQRows = 32;        // query rows per wave
+constexpr int kKeyStep = 32;      // keys per MFMA step
+constexpr int kNumXcd = 8;
+
+// Workgroups are dispatched round-robin over the XCDs.  Give each XCD a
+// contiguous range of workgroups so that the query blocks of one head
+// (which read overlapping K/V blocks) share one L2.
+__device__ __forceinline__ int xcd_remap(int x, int G) {
+  const int per = (G + kNumXcd - 1) / kNumXcd;
+  int tall = G % kNumXcd;
+  if (tall == 0) tall = kNumXcd;
+  const int xcd = x % kNumXcd;
+  const int local = x / kNumXcd;
+  if (xcd < tall) return xcd * per + local;
+  return tall * per + (xcd - tall) * (per - 1) + local;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Max (or sum) of a per-lane value with the lane 32 apart.
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2_t f = {lo, hi};
+  bf16x2_t b = __builtin_convertvector(f, bf16x2_t);  // round to nearest even
+  return __builtin_bit_cast(uint32_t, b);
+}
+
+// ---------------------------------------------------------------- tile layout
+// A K or V tile is BS rows of D elements, row-major in LDS, in 16-byte
+// chunks; chunk c of row r sits at position c ^ swz(r).
+template <typename T, int BS, int D>
+struct TileLayout {
+  static constexpr int kRowBytes = D * (int)sizeof(T);
+  static constexpr int kChunksPerRow = kRowBytes / 16;
+  static constexpr int kTileBytes = BS * kRowBytes;
+  static constexpr int kEntryBytes = 2 * kTileBytes;  // K tile then V tile
+  static constexpr int kCopies = kEntryBytes / (kWave * 16);  // 1 KB parts per entry
+
+  // XOR key of row r: a bit-reversed row index, chosen so that (a) 16 rows
+  // read at the same chunk hit 16 different 16-byte bank groups and (b) the
+  // transpose reads (4 consecutive rows x 4 consecutive chunks) do too.  It
+  // depends on r mod 16 only, so per-lane offsets computed for rows 0..15
+  // hold for every row at a multiple of 16 further on.
+  static __device__ __forceinline__ int swz(int r) {
+    if constexpr (kChunksPerRow == 8) {  // 128-byte rows: two rows per 256-byte bank line
+      const int t = (r >> 1) & 7;
+      return ((t & 1) << 2) | (t & 2) | ((t >> 2) & 1);
+    } else {
+      const int t = r & 15;
+      const int rev = ((t & 1) << 3) | ((t & 2) << 1) | ((t & 4) >> 1) | ((t & 8) >> 3);
+      return rev & (kChunksPerRow - 1);
+    }
+  }
+  static __device__ __forceinline__ int chunk_offset(int r, int c) {
+    return r * kRowBytes + ((c ^ swz(r)) << 4);
+  }
+};
+
+template <typename T>
+struct Ops;
+
+// ---------------------------------------------------------------- bf16
+template <>
+struct Ops<__bf16> {
+  template <int D>
+  struct QOperand { u32x4_t r[D / 16]; };
+
+  // Lane (query = lane % 32, half h = lane / 32) holds Q[query][16c + 8h .. +8].
+  template <int D>
+  static __device__ __forceinline__ void load_q(QOperand<D>& q, const __bf16* Q, int lane) {
+    const __bf16* p = Q + (size_t)(lane & 31) * D + (lane >> 5) * 8;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) q.r[c] = *reinterpret_cast<const u32x4_t*>(p + 16 * c);
+  }
+
+  // Per-lane LDS byte offsets of the operand reads, relative to the LDS base
+  // of the slice's buffer 0 (plus that base).  Valid for every 32-key step
+  // and 16-key sub-step: those move by multiples of 16 rows.
+  template <int BS, int D>
+  struct Offsets {
+    int k[D / 16];     // K chunk 2c + h of key row lane % 32
+    int v[2][D / 32];  // transpose-read address, rows +0 / +8, feature tile dt
+    __device__ __forceinline__ void init(int lane, int base) {
+      using L = TileLayout<__bf16, BS, D>;
+      const int h = lane >> 5;
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) k[c] = base + L::chunk_offset(lane & 31, 2 * c + h);
+      // In each 16-lane group, lane 4k + q addresses the 4 features
+      // (feature0 + 4q ..) of key row k; the hardware returns to lane i
+      // feature0 + i of rows k = 0..3.
+      const int g4 = lane >> 4;
+      const int i = lane & 15;
+      const int row = 4 * (g4 >> 1) + (i >> 2);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const int feature = dt * 32 + 16 * (g4 & 1) + 4 * (i & 3);
+        const int half = (feature & 7) * 2;
+        v[0][dt] = base + L::kTileBytes + L::chunk_offset(row, feature >> 3) + half;
+        v[1][dt] = base + L::kTileBytes + L::chunk_offset(row + 8, feature >> 3) + half;
+      }
+    }
+  };
+
+  // S^T for 32-key step st of the entry at byte `entry` (a constant) past
+  // the offsets' base: A operand (lane = key, half h) = K[key][16c + 8h .. +8].
+  template <int BS, int D>
+  static __device__ __forceinline__ f32x16_t scores(const QOperand<D>& q,
+                                                    const Offsets<BS, D>& off,
+                                                    LDS_PTR(unsigned char) lds, int entry,
+                                                    int st) {
+    using L = TileLayout<__bf16, BS, D>;
+    f32x16_t s = {};
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      const u32x4_t k = *(LDS_PTR(const u32x4_t))(lds + off.k[c] + entry +
+                                                  st * kKeyStep * L::kRowBytes);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, k),
+                                                  __builtin_bit_cast(bf16x8_t, q.r[c]), s, 0, 0,
+                                                  0);
+    }
+    return s;
+  }
+
+  // V^T operand of step st, 16-key sub-step sc, feature tile dt: lane
+  // (feature = 32 dt + lane % 32, half h) holds V[key][feature] for keys
+  // kappa(h, j) = 32 st + 16 sc + 8 (j / 4) + 4 h + j % 4, j = 0..7: two
+  // transpose loads, rows +0 and +8.
+  template <int BS, int D>
+  static __device__ __forceinline__ u32x4_t v_operand(const Offsets<BS, D>& off,
+                                                      LDS_PTR(unsigned char) lds, int entry,
+                                                      int st, int sc, int dt) {
+    using L = TileLayout<__bf16, BS, D>;
+    const int rows = (st * kKeyStep + 16 * sc) * L::kRowBytes;
+    const u32x2_t lo = __builtin_bit_cast(
+        u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                     (LDS_PTR(s16x4_t))(lds + off.v[0][dt] + entry + rows)));
+    const u32x2_t hi = __builtin_bit_cast(
+        u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                     (LDS_PTR(s16x4_t))(lds + off.v[1][dt] + entry + rows)));
+    return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+  }
+
+  // O^T += V^T P^T over 32-key step st of the entry; returns the sum of the
+  // bf16-rounded P (the weights the product uses).
+  template <int BS, int D>
+  static __device__ __forceinline__ float accumulate(f32x16_t (&o)[D / 32], const f32x16_t& p,
+                                                     const Offsets<BS, D>& off,
+                                                     LDS_PTR(unsigned char) lds, int entry,
+                                                     int st) {
+    float sum = 0.f;
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int sc = 0; sc < 2; ++sc) {
+      // The four packed words are built as separate scalars: reading dot2
+      // operands out of a 128-bit vector miscompiles (every v_dot2c read
+      // the first word).
+      uint32_t w4[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        w4[w] = pack_bf16x2(p[8 * sc + 2 * w], p[8 * sc + 2 * w + 1]);
+        sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w4[w]), ones, sum,
+                                              false);
+      }
+      const u32x4_t pb = {w4[0], w4[1], w4[2], w4[3]};
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const u32x4_t va = v_operand<BS, D>(off, lds, entry, st, sc, dt);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, va),
+                                                        __builtin_bit_cast(bf16x8_t, pb), o[dt],
+                                                        0, 0, 0);
+      }
+    }
+    return sum;
+  }
+
+  // Lane holds O^T[d = 32 dt + 8 g + 4 h + e][query], e = 0..3.
+  static __device__ __forceinline__ void store_o4(__bf16* dst, float a, float b, float c,
+                                                  float d) {
+    u32x2_t w = {pack_bf16x2(a, b), pack_bf16x2(c, d)};
+    *reinterpret_cast<u32x2_t*>(dst) = w;
+  }
+};
+
+// ---------------------------------------------------------------- fp32
+template <>
+struct Ops<float> {
+  template <int D>
+  struct QOperand { f32x4_t r[D / 8]; };
+
+  // v_mfma_f32_32x32x2_f32 contracts 2 features per instruction, one per lane
+  // half.  Lane (query, h) holds Q[query][(D/2) h + c], c = 0 .. D/2-1.
+  template <int D>
+  static __device__ __forceinline__ void load_q(QOperand<D>& q, const float* Q, int lane) {
+    const float* p = Q + (size_t)(lane & 31) * D + (lane >> 5) * (D / 2);
+#pragma unroll
+    for (int c = 0; c < D / 8; ++c) q.r[c] = *reinterpret_cast<const f32x4_t*>(p + 4 * c);
+  }
+
+  template <int BS, int D>
+  struct Offsets {
+    int lane;
+    int base;
+    __device__ __forceinline__ void init(int l, int b) {
+      lane = l;
+      base = b;
+    }
+  };
+
+  template <int BS, int D>
+  static __device__ __forceinline__ f32x16_t scores(const QOperand<D>& q,
+                                                    const Offsets<BS, D>& off,
+                                                    LDS_PTR(unsigned char) lds, int entry,
+                                                    int st) {
+    using L = TileLayout<float, BS, D>;
+    const int key = st * kKeyStep + (off.lane & 31);
+    const int h = off.lane >> 5;
+    f32x16_t s = {};
+#pragma unroll
+    for (int c = 0; c < D / 8; ++c) {
+      const f32x4_t k = *(LDS_PTR(const f32x4_t))(lds + off.base + entry +
+                                                   L::chunk_offset(key, (D / 8) * h + c));
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        s = __builtin_amdgcn_mfma_f32_32x32x2f32(k[e], q.r[c][e], s, 0, 0, 0);
+    }
+    return s;
+  }
+
+  // Instruction i of a 32-key step contracts the keys held in accumulator
+  // register i: key 8 (i / 4) + 4 h + i % 4 for lane half h.
+  template <int BS, int D>
+  static __device__ __forceinline__ float accumulate(f32x16_t (&o)[D / 32], const f32x16_t& p,
+                                                     const Offsets<BS, D>& off,
+                                                     LDS_PTR(unsigned char) lds, int entry,
+                                                     int st) {
+    using L = TileLayout<float, BS, D>;
+    const int h = off.lane >> 5;
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sum += p[i];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const int feature = dt * 32 + (off.lane & 31);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = st * kKeyStep + 8 * (i / 4) + 4 * h + (i % 4);
+        const float va = *(LDS_PTR(const float))(lds + off.base + entry + L::kTileBytes +
+                                                 L::chunk_offset(row, feature >> 2) +
+                                                 (feature & 3) * 4);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(va, p[i], o[dt], 0, 0, 0);
+      }
+    }
+    return sum;
+  }
+
+  static __device__ __forceinline__ void store_o4(float* dst, float a, float b, float c,
+                                                  float d) {
+    f32x4_t w = {a, b, c, d};
+    *reinterpret_cast<f32x4_t*>(dst) = w;
+  }
+};
+
+// s_waitcnt: vector-memory count <= n and LDS/scalar count == 0.
+template <int n>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  // gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]
+  __builtin_amdgcn_s_waitcnt((n & 0xF) | (0x7 << 4) | (0x0 << 8) | ((n >> 4) << 14));
+}
+
+// Direct-to-LDS copy of 16 bytes per lane: lane i reads sbase + voff (its
+// own offset) and the data lands at LDS byte address m0 + 16 i.  Written as
+// asm so that the compiler does not add waits for these copies in front of
+// LDS reads of other buffers; the kernel waits for them itself (s_waitcnt
+// vmcnt before the barrier that publishes a buffer).  The asm has no register
+// outputs.  It sets M0, which nothing else in these kernels uses.
+__device__ __forceinline__ void lds_dma16(const void* sbase, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(m0)
+               : "memory", "m0");
+}
+
+// Workgroup barrier without a memory fence: the caller has already waited for
+// the memory operations the barrier publishes.  The empty asm statements keep
+// the compiler from moving memory accesses across it.
+__device__ __forceinline__ void raw_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+
+// Direct-to-LDS copy of 4 bytes per lane (same rules as lds_dma16): lane i's
+// dword lands at LDS byte address m0 + 4 i.
+__device__ __forceinline__ void lds_dma4(const void* sbase, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(m0)
+               : "memory", "m0");
+}
+
+}  // namespace
