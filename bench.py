@@ -282,12 +282,45 @@ def practical_ceilings():
             "device_copy": "1 GiB copy, read + write bytes, 5 reps"}
 
 
-def side_line(name, args, device, causal):
+class BackwardCase:
+    """One backward pass (dQ and D, then dK and dV) over a workload, with the
+    forward's output and LSE computed once beforehand."""
+
+    def __init__(self, name, seed, device, causal=False):
+        import torch
+
+        import block_sparse_attention_csr_amd as bsa
+        from synthetic_inputs import make_qkv
+
+        self.fwd = Case(name, seed, device, causal=causal)
+        self.bsa = bsa
+        w = self.fwd.w
+        self.dout = make_qkv(w.B, w.H, w.N, w.d, w.torch_dtype, seed + 7)[0].to(device)
+        rp, ci = bsa.build_pattern(w.N, w.block_size, mask=self.fwd.mask, causal=causal)
+        cp, ri = bsa.transpose_pattern(rp, ci)
+        self.pat = [t.to(device) for t in (rp, ci, cp, ri)]
+        self.grads = [torch.empty_like(self.fwd.q) for _ in range(3)]
+        self.delta = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=device)
+        self.fwd.step()
+        torch.cuda.synchronize()
+        # five products per selected pair (S recomputed, dP, dV, dQ, dK count as
+        # the standard 2.5x of the forward's two)
+        self.flops = 2.5 * self.fwd.flops
+        self.compulsory_bytes = 2.0 * self.fwd.compulsory_bytes
+
+    def step(self):
+        f = self.fwd
+        dq, dk, dv = self.grads
+        self.bsa.backward(f.q, f.k, f.v, f.out, f.lse, self.dout, *self.pat, f.w.block_size,
+                          causal=f.causal, dq=dq, dk=dk, dv=dv, delta=self.delta)
+
+
+def side_line(name, args, device, causal, backward=False):
     """A graph-timed line for another workload (the saturating B = 32 shape,
     or its causal forward) reported beside the headline."""
     import torch
 
-    sat = Case(name, args.seed, device, causal=causal)
+    sat = (BackwardCase if backward else Case)(name, args.seed, device, causal=causal)
     for _ in range(5):
         sat.step()
     sat_steps = max(10, min(100, args.steps // 10))
@@ -295,7 +328,7 @@ def side_line(name, args, device, causal):
     s_launch = time_events_per_launch(sat, sat_steps)
     s_step = s_graph if s_graph is not None else time_eager(sat, sat_steps)
     s_kernel = s_evt if s_evt is not None else s_launch
-    s_traffic = None if causal else load_traffic(name)
+    s_traffic = None if causal or backward else load_traffic(name)
     line = {
         "value": round(sat.flops / s_step / 1e12, 3),
         "unit": "TFLOP/s",
@@ -310,6 +343,9 @@ def side_line(name, args, device, causal):
     }
     if causal:
         line["flop_counting"] = "selected (query, key) pairs: diagonal blocks count bs(bs+1)/2"
+    if backward:
+        line["flop_counting"] = ("2.5x the forward's selected-pair flop (five products per pair: "
+                                 "S, dP, dV, dQ, dK); two kernels per step")
     del sat
     torch.cuda.empty_cache()
     return line
@@ -413,6 +449,8 @@ def main(argv=None):
                                                             causal=False)
         result["causal_worked_example_b32"] = side_line("worked_example_b32", args, device,
                                                         causal=True)
+        result["backward_worked_example_b32"] = side_line("worked_example_b32", args, device,
+                                                          causal=False, backward=True)
 
     if not args.no_ceilings:
         result["practical_ceilings"] = practical_ceilings()

@@ -20,8 +20,8 @@ import os
 import numpy as np
 
 __all__ = [
-    "BsaError", "build_pattern", "forward", "status_string", "abi_version", "library_path",
-    "PatternCache", "BSA_OK", "stack_head_patterns",
+    "BsaError", "build_pattern", "forward", "backward", "transpose_pattern", "status_string",
+    "abi_version", "library_path", "PatternCache", "BSA_OK", "stack_head_patterns",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -91,6 +91,10 @@ def _load():
     lib.bsa_forward_ex.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp,
                                    i64, ctypes.c_float, i32, i32, i32, vp]
     lib.bsa_forward_ex.restype = i32
+    lib.bsa_transpose_pattern.argtypes = [i32, p32, p32, i64, p32, p32]
+    lib.bsa_transpose_pattern.restype = i32
+    lib.bsa_backward.argtypes = [vp] * 10 + [i32] * 6 + [vp] * 4 + [i64, ctypes.c_float, i32, vp]
+    lib.bsa_backward.restype = i32
     lib.bsa_status_string.argtypes = [i32]
     lib.bsa_status_string.restype = ctypes.c_char_p
     lib.bsa_abi_version.argtypes = []
@@ -256,6 +260,64 @@ def forward(q, k, v, row_ptr, col_idx, block_size: int, scale: float | None = No
     if st != BSA_OK:
         raise BsaError(st, "bsa_forward")
     return out, lse
+
+
+def transpose_pattern(row_ptr, col_idx):
+    """CSC of a CSR pattern (bsa_transpose_pattern): (col_ptr int32[M+1],
+    row_idx int32[nnz]) as CPU torch tensors; inputs are CPU int32 tensors."""
+    import torch
+
+    rp = np.ascontiguousarray(np.asarray(row_ptr.cpu() if hasattr(row_ptr, "cpu") else row_ptr,
+                                         dtype=np.int32))
+    ci = np.ascontiguousarray(np.asarray(col_idx.cpu() if hasattr(col_idx, "cpu") else col_idx,
+                                         dtype=np.int32))
+    M = rp.size - 1
+    cp = np.zeros(M + 1, dtype=np.int32)
+    ri = np.zeros(max(ci.size, 1), dtype=np.int32)
+    p32 = ctypes.POINTER(ctypes.c_int32)
+    st = _load().bsa_transpose_pattern(M, rp.ctypes.data_as(p32), ci.ctypes.data_as(p32),
+                                       ci.size, cp.ctypes.data_as(p32), ri.ctypes.data_as(p32))
+    if st != BSA_OK:
+        raise BsaError(st, "bsa_transpose_pattern")
+    return torch.from_numpy(cp), torch.from_numpy(ri[:ci.size].copy())
+
+
+def backward(q, k, v, o, lse, dout, row_ptr, col_idx, col_ptr, row_idx, block_size: int,
+             scale: float | None = None, *, causal: bool = False, dq=None, dk=None, dv=None,
+             delta=None, stream=None):
+    """Gradients (dq, dk, dv) of ``forward`` for the upstream gradient ``dout``.
+
+    q, k, v, o, dout: CUDA [B, H, N, d] tensors of one dtype; lse the
+    forward's LSE; row_ptr/col_idx the forward's device CSR and
+    col_ptr/row_idx its device CSC (``transpose_pattern``).  Enqueued on the
+    current stream (or ``stream``), not synchronised.
+    """
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if not t.is_cuda or not t.is_contiguous() or t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be a contiguous CUDA tensor like q")
+    for t in (row_ptr, col_idx, col_ptr, row_idx):
+        if t.dtype != torch.int32 or not t.is_cuda:
+            raise ValueError("patterns must be int32 CUDA tensors")
+    B, H, N, d = q.shape
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    if delta is None:
+        delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = _load().bsa_backward(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, N, d,
+        int(block_size), _dtype_code(q), row_ptr.data_ptr(), col_idx.data_ptr(),
+        col_ptr.data_ptr(), row_idx.data_ptr(), int(col_idx.numel()),
+        0.0 if scale is None else float(scale), FORWARD_CAUSAL if causal else 0,
+        stream.cuda_stream)
+    if st != BSA_OK:
+        raise BsaError(st, "bsa_backward")
+    return dq, dk, dv
 
 
 class PatternCache:

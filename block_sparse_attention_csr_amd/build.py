@@ -2,8 +2,9 @@
 
     python -m block_sparse_attention_csr_amd.build
 
-The host pattern builder is plain C++ (g++); the kernel and the forward entry
-point are HIP (hipcc --offload-arch=gfx950).  Every build recompiles.
+The host pattern builder is plain C++ (g++); the kernels and their entry
+points (forward.hip, backward.hip) are HIP (hipcc --offload-arch=gfx950).
+Every build recompiles.
 """
 
 from __future__ import annotations
@@ -49,13 +50,14 @@ def _run(cmd, verbose):
 def build(verbose: bool = False, extra_hip_flags=None) -> str:
     os.makedirs(BUILD, exist_ok=True)
     pattern_o = os.path.join(BUILD, "pattern.o")
-    forward_o = os.path.join(BUILD, "forward.o")
+    objs = [os.path.join(BUILD, n) for n in ("forward.o", "backward.o")]
     _run([CXX, *CXX_FLAGS, f"-I{INCLUDE}", "-c", os.path.join(CSRC, "pattern.cpp"),
           "-o", pattern_o], verbose)
-    _run([HIPCC, *HIP_FLAGS, *(extra_hip_flags or []), f"-I{INCLUDE}", "-c",
-          os.path.join(CSRC, "forward.hip"), "-o", forward_o], verbose)
+    for src, obj in zip(("forward.hip", "backward.hip"), objs):
+        _run([HIPCC, *HIP_FLAGS, *(extra_hip_flags or []), f"-I{INCLUDE}", "-c",
+              os.path.join(CSRC, src), "-o", obj], verbose)
     tmp = LIB + ".tmp"
-    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", pattern_o, forward_o, "-o", tmp],
+    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", pattern_o, *objs, "-o", tmp],
          verbose)
     shutil.move(tmp, LIB)
     return LIB

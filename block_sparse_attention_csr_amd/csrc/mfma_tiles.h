@@ -322,10 +322,20 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 // LDS reads of other buffers; the kernel waits for them itself (s_waitcnt
 // vmcnt before the barrier that publishes a buffer).  The asm has no register
 // outputs.  It sets M0, which nothing else in these kernels uses.
+// The base and M0 must be wave-uniform; readfirstlane states that to the
+// compiler, which then keeps them in SGPRs (a no-op when they already are).
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t b = reinterpret_cast<uint64_t>(p);
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+  return reinterpret_cast<const void*>(lo | (hi << 32));
+}
+
 __device__ __forceinline__ void lds_dma16(const void* sbase, uint32_t voff, uint32_t m0) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(voff), "s"(sbase), "s"(m0)
+               : "v"(voff), "s"(uniform_ptr(sbase)),
+                 "s"((uint32_t)__builtin_amdgcn_readfirstlane((int)m0))
                : "memory", "m0");
 }
 
@@ -344,7 +354,8 @@ __device__ __forceinline__ void raw_barrier() {
 __device__ __forceinline__ void lds_dma4(const void* sbase, uint32_t voff, uint32_t m0) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
                :
-               : "v"(voff), "s"(sbase), "s"(m0)
+               : "v"(voff), "s"(uniform_ptr(sbase)),
+                 "s"((uint32_t)__builtin_amdgcn_readfirstlane((int)m0))
                : "memory", "m0");
 }
 

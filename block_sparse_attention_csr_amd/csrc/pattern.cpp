@@ -197,6 +197,30 @@ extern "C" bsa_status bsa_build_pattern(const bsa_pattern_desc* desc, int32_t* r
   return BSA_OK;
 }
 
+extern "C" bsa_status bsa_transpose_pattern(int32_t M, const int32_t* row_ptr,
+                                            const int32_t* col_idx, int64_t nnz,
+                                            int32_t* col_ptr, int32_t* row_idx) {
+  if (row_ptr == nullptr || col_ptr == nullptr || (nnz > 0 && (col_idx == nullptr ||
+                                                                row_idx == nullptr)))
+    return BSA_ERR_NULL_POINTER;
+  if (M <= 0 || row_ptr[0] != 0 || row_ptr[M] != nnz) return BSA_ERR_SHAPE;
+  for (int32_t i = 0; i < M; ++i)
+    if (row_ptr[i + 1] < row_ptr[i]) return BSA_ERR_SHAPE;
+  std::vector<int64_t> count(static_cast<size_t>(M) + 1, 0);
+  for (int64_t t = 0; t < nnz; ++t) {
+    const int32_t j = col_idx[t];
+    if (j < 0 || j >= M) return BSA_ERR_INDEX_RANGE;
+    ++count[static_cast<size_t>(j) + 1];
+  }
+  for (int32_t j = 0; j < M; ++j) count[j + 1] += count[j];
+  for (int32_t j = 0; j <= M; ++j) col_ptr[j] = static_cast<int32_t>(count[j]);
+  // Rows are visited in ascending order, so every column comes out ascending.
+  for (int32_t i = 0; i < M; ++i)
+    for (int32_t t = row_ptr[i]; t < row_ptr[i + 1]; ++t)
+      row_idx[count[static_cast<size_t>(col_idx[t])]++] = i;
+  return BSA_OK;
+}
+
 extern "C" const char* bsa_status_string(int32_t status) {
   switch (status) {
     case BSA_OK: return "BSA_OK";

@@ -197,6 +197,61 @@ bsa_status bsa_forward_ex(const void* q, const void* k, const void* v, void* o, 
                           const int32_t* col_idx, int64_t nnz, float scale, int32_t flags,
                           int32_t group, int32_t key_split, void* stream);
 
+/*
+ * bsa_transpose_pattern -- the CSC (column-major) form of a CSR pattern.
+ *
+ * For every K block j, the query blocks whose rows select it, ascending:
+ *   col_ptr[0] = 0, col_ptr[j + 1] = col_ptr[j] + |{i : j in S(i)}|,
+ *   row_idx[col_ptr[j] .. col_ptr[j + 1]) = those i.
+ * The backward's dK/dV kernel walks these columns.
+ *
+ * M        blocks per sequence (> 0).
+ * row_ptr  host int32[M + 1], col_idx host int32[nnz]: a pattern as
+ *          bsa_build_pattern returns it (entries in [0, M)).
+ * col_ptr  host, caller-owned int32[M + 1]; row_idx host int32[nnz].
+ * Errors: BSA_ERR_NULL_POINTER, BSA_ERR_SHAPE (M <= 0, nnz != row_ptr[M],
+ * row_ptr not non-decreasing from 0), BSA_ERR_INDEX_RANGE (an entry outside
+ * [0, M)).  Host only, synchronous.
+ */
+bsa_status bsa_transpose_pattern(int32_t M, const int32_t* row_ptr, const int32_t* col_idx,
+                                 int64_t nnz, int32_t* col_ptr, int32_t* row_idx);
+
+/*
+ * bsa_backward -- gradients of bsa_forward: dQ, dK, dV.
+ *
+ * With P the softmax of bsa_forward (recomputed from its LSE), O its output
+ * and dO the gradient of a loss with respect to O:
+ *   dV = P^T dO,  dP = dO V^T,  D_r = dO_r . O_r,  dS = P * (dP - D),
+ *   dQ = scale dS K,  dK = scale dS^T Q.
+ * (The log-linear page's section 5.3 backward without its gradient
+ * compensation heuristic.)
+ *
+ * q, k, v, o, dout  device, [batch, heads, seq_len, head_dim] of `dtype`,
+ *          16-byte aligned: the forward's inputs, its output and dO.
+ * lse      device float32 [batch, heads, seq_len]: the forward's LSE.
+ * dq, dk, dv  device, caller-owned, same shape and dtype; written.
+ * delta    device, caller-owned float32 [batch, heads, seq_len]: workspace
+ *          (receives D).
+ * row_ptr, col_idx  device copies of the forward's CSR pattern;
+ * col_ptr, row_idx  device copies of its bsa_transpose_pattern.
+ * nnz      the pattern's entry count (host).
+ * scale    as for bsa_forward (<= 0: 1 / sqrt(head_dim)).
+ * flags    0 or BSA_FORWARD_CAUSAL (the forward's causal masking).
+ * stream   a hipStream_t or NULL; two launches are enqueued (dQ and D,
+ *          then dK and dV), without synchronising.
+ *
+ * Supported: dtype BF16 or F32, block_size 32 or 64, head_dim 64 or 128,
+ * M = seq_len / block_size <= 4096.  Errors as for bsa_forward; unknown
+ * flags (including BSA_FORWARD_PATTERN_PER_HEAD) are BSA_ERR_INVALID_ARGUMENT.
+ */
+bsa_status bsa_backward(const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                        float* delta, int32_t batch, int32_t heads, int32_t seq_len,
+                        int32_t head_dim, int32_t block_size, int32_t dtype,
+                        const int32_t* row_ptr, const int32_t* col_idx, const int32_t* col_ptr,
+                        const int32_t* row_idx, int64_t nnz, float scale, int32_t flags,
+                        void* stream);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* bsa_status_string(int32_t status);
 

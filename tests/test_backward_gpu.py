@@ -1,0 +1,128 @@
+"""GPU parity of the backward (bsa_backward through the C ABI) against the
+float64 oracle: dQ, dK, dV for every dtype, block size and head size, plain
+and causal, on log-linear, random and all-ones patterns."""
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_csr_amd as bsa
+import oracle
+from synthetic_inputs import WORKLOADS, make_qkv, random_block_mask
+
+pytestmark = pytest.mark.gpu
+
+# bf16: P and dS are rounded to bf16 before their products (as in the
+# forward), so the bound is relative to the gradient's magnitude:
+# max|err| <= 2e-2 * max(1, max|ref|).  fp32: max|err| <= 1e-4 * max|ref|.
+BF16_TOL = 2e-2
+F32_TOL = 1e-4
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    bsa._load()
+
+
+def _f64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def _check(name, got, ref, dtype):
+    got = _f64(got)
+    assert np.isfinite(got).all(), f"{name}: non-finite gradient"
+    err = np.abs(got - ref).max()
+    mag = np.abs(ref).max()
+    if dtype == torch.float32:
+        assert err <= F32_TOL * mag, f"{name}: max err {err:.3e} vs max |ref| {mag:.3e}"
+    else:
+        assert err <= BF16_TOL * max(1.0, mag), f"{name}: max err {err:.3e} vs max |ref| {mag:.3e}"
+    return err / max(1.0, mag)
+
+
+def _mask(kind, M, seed):
+    if kind == "loglinear":
+        return oracle.block_mask_from_sets(oracle.loglinear_block_sets(M * 32, 32)), None
+    if kind == "ones":
+        m = np.ones((M, M), np.uint8)
+    else:
+        m = random_block_mask(M, 0.4, seed)
+    return m, m
+
+
+def _run(q, k, v, do, bs, user_mask, causal, scale=None):
+    dev = torch.device("cuda")
+    N = q.shape[2]
+    rp, ci = bsa.build_pattern(N, bs, mask=user_mask, causal=causal)
+    cp, ri = bsa.transpose_pattern(rp, ci)
+    q, k, v, do = (t.to(dev) for t in (q, k, v, do))
+    rp, ci, cp, ri = (t.to(dev) for t in (rp, ci, cp, ri))
+    o, lse = bsa.forward(q, k, v, rp, ci, bs, scale, causal=causal)
+    dq, dk, dv = bsa.backward(q, k, v, o, lse, do, rp, ci, cp, ri, bs, scale, causal=causal)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+CASES = [(dt, bs, d, kind, B, H, M) for dt in ("bf16", "f32") for bs in (32, 64)
+         for d in (64, 128)
+         for kind, B, H, M in (("loglinear", 1, 2, 9), ("random", 2, 1, 7), ("ones", 1, 1, 5))]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dt,bs,d,kind,B,H,M", CASES)
+def test_backward_parity(dt, bs, d, kind, B, H, M, causal):
+    dtype = torch.bfloat16 if dt == "bf16" else torch.float32
+    N = bs * M
+    seed = zlib.crc32(repr((dt, bs, d, kind, B, H, M, causal)).encode()) % 1000
+    q, k, v = make_qkv(B, H, N, d, dtype, seed)
+    do = make_qkv(B, H, N, d, dtype, seed + 1)[0]
+    if kind == "loglinear":
+        sets = oracle.loglinear_block_sets(N, bs)
+        mask, user = oracle.block_mask_from_sets(sets), None
+    else:
+        mask, user = _mask(kind, M, seed)
+    if causal:
+        mask = np.tril(mask)
+    dq, dk, dv = _run(q, k, v, do, bs, user, causal)
+    rq, rk, rv, _ = oracle.block_sparse_attention_backward(_f64(q), _f64(k), _f64(v), _f64(do),
+                                                           mask, bs, causal=causal)
+    what = f"{dt} bs{bs} d{d} {kind} causal={causal}"
+    _check(f"dQ {what}", dq, rq, dtype)
+    _check(f"dK {what}", dk, rk, dtype)
+    _check(f"dV {what}", dv, rv, dtype)
+
+
+def test_backward_scale_override():
+    q, k, v = make_qkv(1, 2, 64 * 6, 64, torch.bfloat16, 5)
+    do = make_qkv(1, 2, 64 * 6, 64, torch.bfloat16, 6)[0]
+    m = random_block_mask(6, 0.5, 5)
+    dq, dk, dv = _run(q, k, v, do, 64, m, False, scale=0.3)
+    rq, rk, rv, _ = oracle.block_sparse_attention_backward(_f64(q), _f64(k), _f64(v), _f64(do),
+                                                           m, 64, scale=0.3)
+    for name, a, b in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        _check(name, a, b, torch.bfloat16)
+
+
+def test_backward_worked_example_sampled_heads():
+    w = WORKLOADS["worked_example"]
+    q, k, v = make_qkv(1, 2, w.N, w.d, w.torch_dtype, 0)
+    do = make_qkv(1, 2, w.N, w.d, w.torch_dtype, 1)[0]
+    dq, dk, dv = _run(q, k, v, do, w.block_size, None, False)
+    mask = oracle.block_mask_from_sets(oracle.loglinear_block_sets(w.N, w.block_size))
+    rq, rk, rv, _ = oracle.block_sparse_attention_backward(_f64(q), _f64(k), _f64(v), _f64(do),
+                                                           mask, w.block_size)
+    for name, a, b in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        print(name, _check(name, a, b, torch.bfloat16))
+
+
+def test_backward_deterministic():
+    q, k, v = make_qkv(2, 2, 1024, 64, torch.bfloat16, 3)
+    do = make_qkv(2, 2, 1024, 64, torch.bfloat16, 4)[0]
+    a = _run(q, k, v, do, 32, None, False)
+    b = _run(q, k, v, do, 32, None, False)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)

@@ -236,3 +236,28 @@ def test_stack_head_patterns_offsets():
     assert rp.numel() == 2 * (M + 1) and ci.numel() == a[1].numel() + b[1].numel()
     assert (rp[:M + 1] == a[0]).all() and (rp[M + 1:] == b[0] + a[1].numel()).all()
     assert (ci[:a[1].numel()] == a[1]).all() and (ci[a[1].numel():] == b[1]).all()
+
+
+@pytest.mark.parametrize("kind", ["loglinear", "mask", "bigbird"])
+def test_transpose_pattern_matches_numpy(kind):
+    N, bs = 4096, 32
+    M = N // bs
+    kw = {"mask": random_block_mask(M, 0.2, 4)} if kind == "mask" else (
+        {"kind": "bigbird", "num_random": 3, "seed": 9} if kind == "bigbird" else {})
+    rp, ci = bsa.build_pattern(N, bs, **kw)
+    cp, ri = bsa.transpose_pattern(rp, ci)
+    dense = oracle.block_mask_from_csr(rp.numpy(), ci.numpy(), M)
+    cp_ref, ri_ref = oracle.csr_from_block_mask(dense.T.copy())
+    assert np.array_equal(cp.numpy(), cp_ref) and np.array_equal(ri.numpy(), ri_ref)
+
+
+def test_transpose_pattern_errors():
+    import torch
+    rp = torch.tensor([0, 1, 2], dtype=torch.int32)
+    with pytest.raises(bsa.BsaError) as e:
+        bsa.transpose_pattern(rp, torch.tensor([0, 2], dtype=torch.int32))
+    assert e.value.status == 5
+    with pytest.raises(bsa.BsaError) as e:
+        bsa.transpose_pattern(torch.tensor([0, 2, 1], dtype=torch.int32),
+                              torch.tensor([0, 1], dtype=torch.int32))
+    assert e.value.status == 3
