@@ -360,19 +360,23 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 8 * BS>::W)) void bsa_bwd
         for (int r = 0; r < 16; ++r)
           if ((lane & 31) > 8 * (r / 4) + 4 * h + (r % 4)) s[r] = -INFINITY;
       }
-      // Register r of the lane half h holds query 32 sq + 8 (r / 4) + 4 h + r % 4.
-      f32x4_t lse4[4], d4[4];
+      // Register r of the lane half h holds query 32 sq + 8 (r / 4) + 4 h + r % 4;
+      // its LSE, then its D, are read from the stage four at a time.
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        lse4[g] = vec[(32 * sq + 8 * g + 4 * h) / 4];
-        d4[g] = vec[(BS + 32 * sq + 8 * g + 4 * h) / 4];
-      }
+        const f32x4_t l4 = vec[(32 * sq + 8 * g + 4 * h) / 4];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = fast_exp2(fmaf(s[r], c2, -lse4[r / 4][r % 4] * kLog2e));
+        for (int e = 0; e < 4; ++e)
+          s[4 * g + e] = fast_exp2(fmaf(s[4 * g + e], c2, -l4[e] * kLog2e));
+      }
       (void)O::template accumulate<BS, D>(dv, s, off, tile, 0, sq);  // dO^T P
       const f32x16_t dp = O::template scores<BS, D>(vop, off, tile, L::kTileBytes, sq);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = s[r] * (dp[r] - d4[r / 4][r % 4]);  // dS
+      for (int g = 0; g < 4; ++g) {
+        const f32x4_t d4 = vec[(BS + 32 * sq + 8 * g + 4 * h) / 4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[4 * g + e] = s[4 * g + e] * (dp[4 * g + e] - d4[e]);  // dS
+      }
       (void)O::template accumulate<BS, D>(dk, s, off, tile, -L::kTileBytes, sq);  // Q^T dS
     }
   };
