@@ -15,6 +15,8 @@ It is deliberately plain and slow:
 * ``oracle.attention`` -- dense softmax attention in float64 with an explicit
   block mask expanded to tokens, one query block at a time.
 * ``oracle.backward`` -- the plain gradients dQ, dK, dV of that forward.
+* ``oracle.decode`` -- one new token against a KV cache: row t of the causal
+  forward, over the cached positions its block's pattern row selects.
 
 Sources (web pages; cited by title and section):
 
@@ -51,6 +53,7 @@ from .pattern import (
 )
 from .attention import block_sparse_attention_head, block_sparse_attention
 from .backward import block_sparse_attention_backward_head, block_sparse_attention_backward
+from .decode import block_sparse_decode_head, block_sparse_decode
 
 __all__ = [
     "ceil_log2",
@@ -68,4 +71,6 @@ __all__ = [
     "block_sparse_attention",
     "block_sparse_attention_backward_head",
     "block_sparse_attention_backward",
+    "block_sparse_decode_head",
+    "block_sparse_decode",
 ]

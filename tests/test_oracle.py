@@ -496,3 +496,92 @@ def test_backward_matches_sdpa_autograd(kind):
     for a, b in ((dq, gq), (dk, gk), (dv, gv)):
         assert np.abs(a - b).max() < 1e-12 * max(1.0, np.abs(b).max())
     assert np.abs(dvec - (g * o).sum(axis=1)).max() < 1e-12
+
+
+# ----------------------------------------------------------------------------- decode
+
+
+def _decode_visible(length, mask, bs):
+    t = length - 1
+    pos = np.arange(length)
+    return mask[t // bs][pos // bs] != 0
+
+
+@pytest.mark.parametrize("length", [1, 31, 32, 33, 100, 255, 256])
+def test_decode_equals_masked_sdpa_on_the_prefix(length):
+    rng = np.random.default_rng(length)
+    n_cap, d, bs = 256, 16, 32
+    q = rng.standard_normal(d)
+    k, v = rng.standard_normal((n_cap, d)), rng.standard_normal((n_cap, d))
+    mask = random_block_mask(n_cap // bs, 0.4, 11)
+    o, lse = oracle.block_sparse_decode_head(q, k, v, length, mask, bs)
+    vis = _decode_visible(length, mask, bs)
+    ref = _sdpa(q[None], k[:length], v[:length], mask=vis[None])[0]
+    np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
+    s = (k[:length] @ q) / math.sqrt(d)
+    assert abs(lse - logsumexp(s[vis])) < 1e-12
+
+
+def test_decode_textbook_loop():
+    rng = np.random.default_rng(3)
+    n_cap, d, bs, length = 64, 4, 16, 40
+    q, k, v = rng.standard_normal(d), rng.standard_normal((n_cap, d)), rng.standard_normal((n_cap, d))
+    mask = np.array([[1, 0, 0, 0], [0, 1, 0, 0], [1, 0, 1, 1], [0, 0, 0, 1]], np.uint8)
+    # token 39 is in block 2, which selects blocks 0, 2 (and 3, all after it)
+    num, den, mx = np.zeros(d), 0.0, -math.inf
+    scores = [(p, float(q @ k[p]) * 0.5) for p in list(range(0, 16)) + list(range(32, 40))]
+    mx = max(s for _, s in scores)
+    for p, s in scores:
+        w = math.exp(s - mx)
+        num += w * v[p]
+        den += w
+    o, lse = oracle.block_sparse_decode_head(q, k, v, length, mask, bs)
+    np.testing.assert_allclose(o, num / den, rtol=0, atol=1e-13)
+    assert abs(lse - (mx + math.log(den))) < 1e-13
+
+
+def test_decode_zero_query_is_uniform_over_visible_keys():
+    rng = np.random.default_rng(4)
+    n_cap, d, bs = 4096, 8, 32
+    k, v = rng.standard_normal((n_cap, d)), rng.standard_normal((n_cap, d))
+    sets = oracle.loglinear_block_sets(n_cap, bs)
+    mask = block_mask_from_sets(sets)
+    # worked-example pattern: the last token (block 127) selects {0, 64, 123, 125, 126, 127}
+    o, lse = oracle.block_sparse_decode_head(np.zeros(d), k, v, n_cap, mask, bs)
+    rows = np.concatenate([np.arange(j * bs, (j + 1) * bs) for j in (0, 64, 123, 125, 126, 127)])
+    np.testing.assert_allclose(o, v[rows].mean(axis=0), rtol=0, atol=1e-12)
+    assert abs(lse - math.log(6 * bs)) < 1e-12
+    # a token in the middle of block 100 sees blocks {0, 64, 96, 98, 99} in full and
+    # 17 keys of its own block
+    length = 100 * bs + 17
+    o, lse = oracle.block_sparse_decode_head(np.zeros(d), k, v, length, mask, bs)
+    assert abs(lse - math.log(5 * bs + 17)) < 1e-12
+
+
+def test_decode_token_without_visible_keys_and_bad_length():
+    n_cap, d, bs = 64, 4, 16
+    k = v = np.ones((n_cap, d))
+    mask = np.eye(4, dtype=np.uint8)
+    mask[2, 2] = 0
+    mask[2, 3] = 1  # block 2 selects only a later block
+    o, lse = oracle.block_sparse_decode_head(np.ones(d), k, v, 40, mask, bs)
+    assert np.all(o == 0) and lse == -math.inf
+    with pytest.raises(ValueError):
+        oracle.block_sparse_decode_head(np.ones(d), k, v, 0, mask, bs)
+    with pytest.raises(ValueError):
+        oracle.block_sparse_decode_head(np.ones(d), k, v, n_cap + 1, mask, bs)
+
+
+def test_decode_batched_wrapper_with_per_head_masks():
+    rng = np.random.default_rng(5)
+    B, H, n_cap, d, bs = 2, 3, 128, 8, 32
+    q = rng.standard_normal((B, H, d))
+    k, v = rng.standard_normal((B, H, n_cap, d)), rng.standard_normal((B, H, n_cap, d))
+    masks = np.stack([random_block_mask(4, 0.5, s) for s in range(H)])
+    lengths = [77, 128]
+    o, lse = oracle.block_sparse_decode(q, k, v, lengths, masks, bs)
+    for b in range(B):
+        for h in range(H):
+            o1, l1 = oracle.block_sparse_decode_head(q[b, h], k[b, h], v[b, h], lengths[b],
+                                                     masks[h], bs)
+            assert np.array_equal(o[b, h], o1) and lse[b, h] == l1
