@@ -95,6 +95,8 @@ def _load():
     lib.bsa_transpose_pattern.restype = i32
     lib.bsa_backward.argtypes = [vp] * 10 + [i32] * 6 + [vp] * 4 + [i64, ctypes.c_float, i32, vp]
     lib.bsa_backward.restype = i32
+    lib.bsa_decode.argtypes = [vp] * 5 + [i32] * 6 + [vp] * 3 + [i64, ctypes.c_float, i32, vp]
+    lib.bsa_decode.restype = i32
     lib.bsa_status_string.argtypes = [i32]
     lib.bsa_status_string.restype = ctypes.c_char_p
     lib.bsa_abi_version.argtypes = []
@@ -318,6 +320,54 @@ def backward(q, k, v, o, lse, dout, row_ptr, col_idx, col_ptr, row_idx, block_si
     if st != BSA_OK:
         raise BsaError(st, "bsa_backward")
     return dq, dk, dv
+
+
+def decode(q, k_cache, v_cache, seqlens, row_ptr, col_idx, block_size: int,
+           scale: float | None = None, *, per_head: bool = False, out=None, lse=None,
+           nnz: int | None = None, stream=None):
+    """One new token per sequence against a block-aligned KV cache (bsa_decode).
+
+    q: CUDA [B, H, d]; k_cache, v_cache: CUDA [B, H, N_cap, d] of q's dtype,
+    contiguous; seqlens: int32 CUDA [B], each sequence's cached length L_b
+    (the new token, already in the cache, is at position L_b - 1).
+    row_ptr/col_idx: the device CSR of a pattern with N_cap / block_size rows
+    (``per_head``: row_ptr [H, M + 1]).  Returns (o [B, H, d], lse [B, H]
+    float32); enqueued on the current stream (or ``stream``), not synchronised.
+    """
+    import torch
+
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous CUDA tensor")
+    if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("q must be [B, H, d] and the caches [B, H, N_cap, d]")
+    B, H, d = q.shape
+    if k_cache.shape[0] != B or k_cache.shape[1] != H or k_cache.shape[3] != d:
+        raise ValueError("q and the caches disagree on B, H or d")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("q and the caches must share a dtype")
+    if seqlens.dtype != torch.int32 or not seqlens.is_cuda or seqlens.numel() != B:
+        raise ValueError("seqlens must be an int32 CUDA tensor of B entries")
+    for t in (row_ptr, col_idx):
+        if t.dtype != torch.int32 or not t.is_cuda:
+            raise ValueError("row_ptr / col_idx must be int32 CUDA tensors")
+    n_cap = k_cache.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    if nnz is None:
+        nnz = col_idx.numel()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = _load().bsa_decode(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(), lse.data_ptr(),
+        B, H, n_cap, d, int(block_size), _dtype_code(q), seqlens.data_ptr(),
+        row_ptr.data_ptr(), col_idx.data_ptr(), int(nnz), 0.0 if scale is None else float(scale),
+        FORWARD_PATTERN_PER_HEAD if per_head else 0, stream.cuda_stream)
+    if st != BSA_OK:
+        raise BsaError(st, "bsa_decode")
+    return out, lse
 
 
 class PatternCache:

@@ -3,7 +3,7 @@
     python -m block_sparse_attention_csr_amd.build
 
 The host pattern builder is plain C++ (g++); the kernels and their entry
-points (forward.hip, backward.hip) are HIP (hipcc --offload-arch=gfx950).
+points (forward.hip, backward.hip, decode.hip) are HIP (hipcc --offload-arch=gfx950).
 Every build recompiles.
 """
 
@@ -50,10 +50,11 @@ def _run(cmd, verbose):
 def build(verbose: bool = False, extra_hip_flags=None) -> str:
     os.makedirs(BUILD, exist_ok=True)
     pattern_o = os.path.join(BUILD, "pattern.o")
-    objs = [os.path.join(BUILD, n) for n in ("forward.o", "backward.o")]
+    sources = ("forward.hip", "backward.hip", "decode.hip")
+    objs = [os.path.join(BUILD, n.replace(".hip", ".o")) for n in sources]
     _run([CXX, *CXX_FLAGS, f"-I{INCLUDE}", "-c", os.path.join(CSRC, "pattern.cpp"),
           "-o", pattern_o], verbose)
-    for src, obj in zip(("forward.hip", "backward.hip"), objs):
+    for src, obj in zip(sources, objs):
         _run([HIPCC, *HIP_FLAGS, *(extra_hip_flags or []), f"-I{INCLUDE}", "-c",
               os.path.join(CSRC, src), "-o", obj], verbose)
     tmp = LIB + ".tmp"

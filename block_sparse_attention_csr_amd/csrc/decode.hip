@@ -1,0 +1,355 @@
+// Block-sparse attention decode for gfx950 (MI355X): one new token per
+// sequence against a block-aligned KV cache.
+//
+// What is computed: the KV cache of sequence b holds L_b tokens and the new
+// token is the last, at position t = L_b - 1 in block i = t / BS.  Its output
+// is row t of the causal forward: softmax(scale q . K_p) V_p over the cached
+// positions p <= t whose block the pattern row S(i) selects ("Block Sparse
+// Attention: Log-Linear complexity sparse attention implementation",
+// czchanglian.com, section 3.3 for the normalisation over the connected
+// blocks; section 1 motivates the KV-cache use).  The log-sum-exp is written
+// as well.
+//
+// Mapping: one workgroup of W waves per (batch, head).  The work is
+// memory-bound (each cached K/V element is used once, by two multiply-adds),
+// so it runs on the VALU, not on MFMA:
+//  * The selected blocks are cut into units of KU keys, four 16-byte loads
+//    per lane for K and four for V; lane l holds 16-byte chunk l % LPK of
+//    the keys l / LPK + KPI n (n = 0..3), so every load instruction reads
+//    one contiguous 1 KB run of the cache.
+//  * Units are dealt round-robin to the waves; each wave loads its next unit
+//    while it computes the current one, with an exact online softmax.
+//  * A score is the chunk's partial dot product summed over the LPK lanes of
+//    its key (ds_swizzle butterflies); the unit max over the key groups.
+//  * At the end each wave sums its O over the key groups and the W waves
+//    merge (O, m, l) through LDS.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <type_traits>
+
+#include "bsa.h"
+#include "mfma_tiles.h"
+
+namespace {
+
+constexpr int kDecodeWaves = 4;
+
+struct DecParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int32_t* seqlens;
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  int32_t heads;
+  int32_t n_cap;       // cache capacity in tokens (multiple of the block size)
+  int32_t M;           // n_cap / block size
+  int32_t row_stride;  // row_ptr entries per head: M + 1 (one pattern per head) or 0
+  float scale_log2;    // scale * log2(e)
+};
+
+template <typename T, int BS, int D>
+struct DecCfg {
+  static constexpr int E = 16 / (int)sizeof(T);  // elements per 16-byte chunk
+  static constexpr int LPK = D / E;              // lanes per key
+  static constexpr int KPI = kWave / LPK;        // keys per load instruction
+  static constexpr int NI = 4;                   // loads per unit (K, and again V)
+  static constexpr int KU = NI * KPI;            // keys per unit
+  static constexpr int SUB = BS / KU;            // units per block
+  static_assert(LPK <= 32 && SUB >= 1 && BS % KU == 0, "decode unit shape");
+};
+
+// Lane value combined with lane ^ mask, for mask < 32 (no LDS memory is used).
+template <int mask>
+__device__ __forceinline__ float xor_lane(float x) {
+  static_assert(mask > 0 && mask < 32, "swizzle mask");
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), (mask << 10) | 0x1F));
+}
+
+// Sum (or max) over the lanes lane ^ m, m = FROM, 2 FROM, ... < TO (powers of
+// two): the lane groups that differ only in those bits.
+template <int FROM, int TO>
+__device__ __forceinline__ float lanes_sum(float x) {
+  if constexpr (FROM >= TO) {
+    return x;
+  } else if constexpr (FROM < 32) {
+    return lanes_sum<FROM * 2, TO>(x + xor_lane<FROM>(x));
+  } else {
+    return halves_sum(x);
+  }
+}
+template <int FROM, int TO>
+__device__ __forceinline__ float lanes_max(float x) {
+  if constexpr (FROM >= TO) {
+    return x;
+  } else if constexpr (FROM < 32) {
+    return lanes_max<FROM * 2, TO>(__builtin_elementwise_maximum(x, xor_lane<FROM>(x)));
+  } else {
+    return halves_max(x);
+  }
+}
+
+// The E elements of a 16-byte chunk as floats.
+template <typename T>
+__device__ __forceinline__ void chunk_to_float(const u32x4_t& c, float* f) {
+  if constexpr (std::is_same<T, __bf16>::value) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      f[2 * w] = __uint_as_float(c[w] << 16);
+      f[2 * w + 1] = __uint_as_float(c[w] & 0xFFFF0000u);
+    }
+  } else {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) f[w] = __uint_as_float(c[w]);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store_elem(T* dst, float x) {
+  if constexpr (std::is_same<T, __bf16>::value) *dst = (__bf16)x;  // round to nearest even
+  else *dst = x;
+}
+
+template <typename T, int BS, int D>
+__global__ __launch_bounds__(kWave * kDecodeWaves) void bsa_decode_kernel(DecParams p) {
+  using C = DecCfg<T, BS, D>;
+  constexpr int W = kDecodeWaves;
+  constexpr int E = C::E;
+  constexpr int LPK = C::LPK;
+  constexpr int KPI = C::KPI;
+  constexpr int SUB = C::SUB;
+
+  __shared__ float part[W][D + 2];  // per wave: O (unnormalised), m, l
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = uniform(threadIdx.x / kWave);
+  const int bh = blockIdx.x;
+  const int b = bh / p.heads;
+  const int h = bh % p.heads;
+  const int chunk = lane % LPK;  // 16-byte chunk of a key this lane holds
+  const int kq = lane / LPK;     // key within a load instruction's group
+
+  const int L = p.seqlens[b];
+  const bool valid_len = L >= 1 && L <= p.n_cap;
+  const int t = valid_len ? L - 1 : 0;
+  const int qb = t / BS;
+  const int32_t* row_ptr = p.row_ptr + (size_t)h * p.row_stride;
+  const int rs = valid_len ? row_ptr[qb] : 0;
+  const int re = valid_len ? row_ptr[qb + 1] : 0;
+  const int nslots = (re - rs) * SUB;
+
+  const size_t head = (size_t)bh * p.n_cap * D;
+  const T* K = static_cast<const T*>(p.k) + head;
+  const T* V = static_cast<const T*>(p.v) + head;
+
+  float qf[E];
+  {
+    const u32x4_t qc =
+        *reinterpret_cast<const u32x4_t*>(static_cast<const T*>(p.q) + (size_t)bh * D + chunk * E);
+    chunk_to_float<T>(qc, qf);
+  }
+
+  // The row's entries, 64 at a time in one VGPR (lane l: entry base + l).
+  int ent_base = -kWave;
+  int ent = -1;
+  auto entry = [&](int e) -> int {  // col_idx[rs + e], wave-uniform
+    const int base = e & ~(kWave - 1);
+    if (base != ent_base) {
+      ent_base = base;
+      const int idx = rs + base + lane;
+      ent = idx < re ? p.col_idx[idx] : -1;
+    }
+    return __builtin_amdgcn_readlane(ent, e - base);
+  };
+  // First key of slot s (entry s / SUB, unit s % SUB), or -1 when the slot
+  // holds no visible key: a block after the token's block, a unit after the
+  // token, or an entry outside [0, M).
+  auto slot_key = [&](int s) -> int {
+    const int j = entry(s / SUB);
+    if (j < 0 || j > qb) return -1;
+    const int key0 = j * BS + (s % SUB) * C::KU;
+    return key0 <= t ? key0 : -1;
+  };
+  auto next_slot = [&](int s, int& key0) -> int {
+    for (; s < nslots; s += W) {
+      key0 = slot_key(s);
+      if (key0 >= 0) return s;
+    }
+    return nslots;
+  };
+  auto load = [&](int key0, u32x4_t (&kr)[C::NI], u32x4_t (&vr)[C::NI]) {
+#pragma unroll
+    for (int n = 0; n < C::NI; ++n) {
+      const size_t off = (size_t)(key0 + n * KPI + kq) * D + chunk * E;
+      kr[n] = *reinterpret_cast<const u32x4_t*>(K + off);
+      vr[n] = *reinterpret_cast<const u32x4_t*>(V + off);
+    }
+  };
+
+  const float c2 = p.scale_log2;
+  float m2 = -INFINITY;  // running max of the scaled scores (log2 domain)
+  float l = 0.f;         // this lane's share of the exponential sum
+  float o[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) o[e] = 0.f;
+
+  int key_cur = -1;
+  int s = next_slot(wave, key_cur);
+  u32x4_t kr[C::NI], vr[C::NI];
+  if (s < nslots) load(key_cur, kr, vr);
+  while (s < nslots) {
+    // the next unit's loads go out before this unit's arithmetic
+    int key_next = -1;
+    const int sn = next_slot(s + W, key_next);
+    u32x4_t kn[C::NI], vn[C::NI];
+    if (sn < nslots) load(key_next, kn, vn);
+
+    // scores of the lane's keys key_cur + KPI n + kq (scaled, log2 domain)
+    float sc[C::NI];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int n = 0; n < C::NI; ++n) {
+      float kf[E];
+      chunk_to_float<T>(kr[n], kf);
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) d = fmaf(qf[e], kf[e], d);
+      d = lanes_sum<1, LPK>(d) * c2;
+      sc[n] = key_cur + n * KPI + kq <= t ? d : -INFINITY;
+      mx = __builtin_elementwise_maximum(mx, sc[n]);
+    }
+    mx = lanes_max<LPK, kWave>(mx);  // finite: the unit's first key is visible
+    const float m_new = fmaxf(m2, mx);
+    const float alpha = fast_exp2(m2 - m_new);  // 0 on the first unit (m2 = -inf)
+    m2 = m_new;
+    l *= alpha;
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] *= alpha;
+#pragma unroll
+    for (int n = 0; n < C::NI; ++n) {
+      // Keys after the token are skipped by selection, not by a zero weight:
+      // the cache beyond L_b may hold anything, NaN included.
+      const bool visible = key_cur + n * KPI + kq <= t;
+      const float pn = fast_exp2(sc[n] - m_new);
+      l += visible ? pn : 0.f;
+      float vf[E];
+      chunk_to_float<T>(vr[n], vf);
+#pragma unroll
+      for (int e = 0; e < E; ++e) o[e] = visible ? fmaf(pn, vf[e], o[e]) : o[e];
+    }
+#pragma unroll
+    for (int n = 0; n < C::NI; ++n) {
+      kr[n] = kn[n];
+      vr[n] = vn[n];
+    }
+    key_cur = key_next;
+    s = sn;
+  }
+
+  // Sum over the key groups: every lane of chunk c then holds the wave's
+  // O[c E .. c E + E) and l (each key's weight counted once per group).
+  l = lanes_sum<LPK, kWave>(l);
+#pragma unroll
+  for (int e = 0; e < E; ++e) o[e] = lanes_sum<LPK, kWave>(o[e]);
+  if (kq == 0) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) part[wave][chunk * E + e] = o[e];
+  }
+  if (lane == 0) {
+    part[wave][D] = m2;
+    part[wave][D + 1] = l;
+  }
+  __syncthreads();
+
+  // Merge the waves: thread x < D finishes output element x.
+  const int x = threadIdx.x;
+  if (x < D) {
+    float m_all = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < W; ++w) m_all = fmaxf(m_all, part[w][D]);
+    float l_all = 0.f, acc = 0.f;
+    if (m_all != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        const float a = fast_exp2(part[w][D] - m_all);  // 0 for a wave with no unit
+        l_all = fmaf(part[w][D + 1], a, l_all);
+        acc = fmaf(part[w][x], a, acc);
+      }
+    }
+    const float inv = l_all > 0.f ? 1.f / l_all : 0.f;
+    store_elem<T>(static_cast<T*>(p.o) + (size_t)bh * D + x, acc * inv);
+    if (x == 0 && p.lse != nullptr)
+      p.lse[bh] = l_all > 0.f ? (m_all + log2f(l_all)) * 0.69314718055994530942f : -INFINITY;
+  }
+}
+
+template <typename T, int BS, int D>
+bsa_status launch_decode(const DecParams& p, int num_wg, hipStream_t stream) {
+  hipLaunchKernelGGL((bsa_decode_kernel<T, BS, D>), dim3(num_wg), dim3(kWave * kDecodeWaves), 0,
+                     stream, p);
+  return hipGetLastError() == hipSuccess ? BSA_OK : BSA_ERR_HIP;
+}
+
+template <typename T>
+bsa_status dispatch_decode(const DecParams& p, int num_wg, int bs, int d, hipStream_t stream) {
+  if (bs == 32 && d == 64) return launch_decode<T, 32, 64>(p, num_wg, stream);
+  if (bs == 32 && d == 128) return launch_decode<T, 32, 128>(p, num_wg, stream);
+  if (bs == 64 && d == 64) return launch_decode<T, 64, 64>(p, num_wg, stream);
+  if (bs == 64 && d == 128) return launch_decode<T, 64, 128>(p, num_wg, stream);
+  return BSA_ERR_INVALID_ARGUMENT;
+}
+
+}  // namespace
+
+extern "C" bsa_status bsa_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
+                                 float* lse, int32_t batch, int32_t heads, int32_t cache_len,
+                                 int32_t head_dim, int32_t block_size, int32_t dtype,
+                                 const int32_t* seqlens, const int32_t* row_ptr,
+                                 const int32_t* col_idx, int64_t nnz, float scale, int32_t flags,
+                                 void* stream) {
+  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || o == nullptr ||
+      seqlens == nullptr || row_ptr == nullptr || col_idx == nullptr)
+    return BSA_ERR_NULL_POINTER;
+  if (dtype != BSA_DTYPE_F32 && dtype != BSA_DTYPE_BF16) return BSA_ERR_INVALID_ARGUMENT;
+  if (block_size != 32 && block_size != 64) return BSA_ERR_INVALID_ARGUMENT;
+  if (head_dim != 64 && head_dim != 128) return BSA_ERR_INVALID_ARGUMENT;
+  if (batch <= 0 || heads <= 0 || cache_len <= 0 || cache_len % block_size != 0)
+    return BSA_ERR_SHAPE;
+  if (!(scale == scale) || std::isinf(scale)) return BSA_ERR_INVALID_ARGUMENT;
+  if ((flags & ~BSA_FORWARD_PATTERN_PER_HEAD) != 0) return BSA_ERR_INVALID_ARGUMENT;
+  const bool per_head = (flags & BSA_FORWARD_PATTERN_PER_HEAD) != 0;
+  const int64_t M = cache_len / block_size;
+  const int64_t patterns = per_head ? heads : 1;
+  if (nnz < patterns * M || nnz > patterns * M * M) return BSA_ERR_SHAPE;
+  if ((int64_t)batch * heads > INT32_MAX) return BSA_ERR_SHAPE;
+  const uintptr_t align = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_cache) |
+                          reinterpret_cast<uintptr_t>(v_cache);
+  if (align % 16 != 0) return BSA_ERR_INVALID_ARGUMENT;
+
+  DecParams p;
+  p.q = q;
+  p.k = k_cache;
+  p.v = v_cache;
+  p.o = o;
+  p.lse = lse;
+  p.seqlens = seqlens;
+  p.row_ptr = row_ptr;
+  p.col_idx = col_idx;
+  p.heads = heads;
+  p.n_cap = cache_len;
+  p.M = static_cast<int32_t>(M);
+  p.row_stride = per_head ? static_cast<int32_t>(M + 1) : 0;
+  const float s = scale > 0.f ? scale : 1.0f / std::sqrt(static_cast<float>(head_dim));
+  p.scale_log2 = s * 1.4426950408889634f;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  const int num_wg = batch * heads;
+  if (dtype == BSA_DTYPE_F32) return dispatch_decode<float>(p, num_wg, block_size, head_dim, st);
+  return dispatch_decode<__bf16>(p, num_wg, block_size, head_dim, st);
+}

@@ -252,6 +252,45 @@ bsa_status bsa_backward(const void* q, const void* k, const void* v, const void*
                         const int32_t* row_idx, int64_t nnz, float scale, int32_t flags,
                         void* stream);
 
+/*
+ * bsa_decode -- one new token per sequence against a block-aligned KV cache.
+ *
+ * The KV cache of sequence b holds L_b = seqlens[b] tokens; the new token is
+ * the last of them, at position t = L_b - 1 in query block i = t / block_size
+ * (its K and V are already in the cache).  Its output is row t of the causal
+ * bsa_forward: softmax(scale q . K_p) V_p over the cached positions p <= t
+ * whose block the pattern row S(i) selects (the log-linear page, section 3.3:
+ * the softmax runs over the connected blocks only; its section 1 puts the
+ * method's gains at inference, in the KV cache and in latency).
+ *
+ * q        device, [batch, heads, head_dim] of `dtype`, 16-byte aligned.
+ * k_cache, v_cache  device, [batch, heads, cache_len, head_dim] of `dtype`,
+ *          16-byte aligned; positions >= L_b are never read into the result
+ *          (they may hold anything).
+ * o        device, caller-owned [batch, heads, head_dim] of `dtype`; written.
+ * lse      device float32 [batch, heads] (natural-log log-sum-exp of the
+ *          scaled visible scores), or NULL.
+ * cache_len  capacity N_cap of the cache, a multiple of block_size; the
+ *          pattern has M = cache_len / block_size rows.
+ * seqlens  device int32[batch].  A length outside [1, cache_len] (which the
+ *          host cannot check without synchronising) gives O = 0 and
+ *          LSE = -inf for that sequence, as does a token that sees no
+ *          position (its block selects neither itself nor an earlier block).
+ * row_ptr, col_idx, nnz  a pattern of M rows as for bsa_forward (entries
+ *          j > i are skipped: decoding is causal).
+ * scale    <= 0 selects 1 / sqrt(head_dim).
+ * flags    0 or BSA_FORWARD_PATTERN_PER_HEAD (row_ptr [heads, M + 1]).
+ * stream   a hipStream_t or NULL; one launch, not synchronised.
+ *
+ * Supported: dtype BF16 or F32, block_size 32 or 64, head_dim 64 or 128.
+ * Errors as for bsa_forward; unknown flags are BSA_ERR_INVALID_ARGUMENT.
+ */
+bsa_status bsa_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
+                      float* lse, int32_t batch, int32_t heads, int32_t cache_len,
+                      int32_t head_dim, int32_t block_size, int32_t dtype,
+                      const int32_t* seqlens, const int32_t* row_ptr, const int32_t* col_idx,
+                      int64_t nnz, float scale, int32_t flags, void* stream);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* bsa_status_string(int32_t status);
 

@@ -117,3 +117,33 @@ def test_forward_ex_per_head_nnz_range():
 def test_forward_ex_bad_shape_flags_combination():
     assert _fwd_ex(1, d=96) == 2
     assert _fwd_ex(1, N=4010) == 3
+
+
+def _dec(**over):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=4, H=8, N=4096, d=64, bs=32,
+                dtype=1, seqlens=FAKE, row_ptr=FAKE, col_idx=FAKE, nnz=1251, scale=0.0,
+                flags=0, stream=None)
+    args.update(over)
+    a = args
+    return bsa._load().bsa_decode(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"],
+                                  a["N"], a["d"], a["bs"], a["dtype"], a["seqlens"],
+                                  a["row_ptr"], a["col_idx"], a["nnz"],
+                                  ctypes.c_float(a["scale"]), a["flags"], a["stream"])
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "o", "seqlens", "row_ptr", "col_idx"])
+def test_decode_null_pointer(field):
+    assert _dec(**{field: None}) == 1
+
+
+@pytest.mark.parametrize("over", [{"d": 96}, {"bs": 16}, {"dtype": 2}, {"k": FAKE + 4},
+                                  {"scale": float("nan")}, {"flags": 1}, {"flags": 4}])
+def test_decode_invalid_argument(over):
+    assert _dec(**over) == 2
+
+
+@pytest.mark.parametrize("over", [{"B": 0}, {"H": 0}, {"N": 4010}, {"nnz": 127},
+                                  {"nnz": 128 * 128 + 1}, {"flags": 2, "nnz": 1000}])
+def test_decode_shape_errors(over):
+    # flags 2 (one pattern per head) needs heads * M <= nnz
+    assert _dec(**over) == 3
