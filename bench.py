@@ -129,6 +129,86 @@ class Case:
                          out=self.out, lse=self.lse, nnz=nnz, causal=self.causal)
 
 
+class DecodeCase:
+    """One decode step: a new token for each of B sequences against a KV cache
+    of capacity N (cached lengths uniform on [1, N]), log-linear pattern."""
+
+    def __init__(self, name, seed, device):
+        import numpy as np
+        import torch
+
+        import block_sparse_attention_csr_amd as bsa
+        from synthetic_inputs import WORKLOADS, decode_lengths, make_decode_inputs
+
+        self.bsa = bsa
+        self.w = w = WORKLOADS[name]
+        q, k, v = make_decode_inputs(w.B, w.H, w.N, w.d, w.torch_dtype, seed)
+        lengths = decode_lengths(w.B, w.N, seed)
+        self.q, self.k, self.v = (t.to(device) for t in (q, k, v))
+        self.lengths = lengths.to(device)
+        self.out = torch.empty_like(self.q)
+        self.lse = torch.empty((w.B, w.H), dtype=torch.float32, device=device)
+        rp, ci = bsa.build_pattern(w.N, w.block_size)
+        self.rp, self.ci, self.nnz = rp.to(device), ci.to(device), int(ci.numel())
+        # Visible cached positions of each sequence's new token: the positions
+        # <= t of the blocks j <= t // bs its pattern row selects.
+        rp_h, ci_h = rp.numpy(), ci.numpy()
+        visible = 0
+        for L in lengths.tolist():
+            t = L - 1
+            i = t // w.block_size
+            for j in ci_h[rp_h[i]:rp_h[i + 1]]:
+                if j <= i:
+                    visible += min(w.block_size, t - int(j) * w.block_size + 1)
+        elt = 2 if w.dtype == "bf16" else 4
+        self.visible_keys = visible
+        # Algorithmic bytes: every visible K and V row read once, q read, O and
+        # LSE written; flop: q.k and p.v per visible key.
+        self.bytes = (2.0 * visible * w.H * w.d * elt + 2.0 * w.B * w.H * w.d * elt
+                      + 4.0 * w.B * w.H)
+        self.flops = 4.0 * visible * w.H * w.d
+
+    def step(self):
+        w = self.w
+        self.bsa.decode(self.q, self.k, self.v, self.lengths, self.rp, self.ci, w.block_size,
+                        out=self.out, lse=self.lse, nnz=self.nnz)
+
+
+def decode_line(name, args, device):
+    """A graph-timed decode step (bsa_decode): HBM-bound, reported in GB/s of
+    algorithmic bytes against the 8 TB/s peak, and in tokens per second."""
+    import torch
+
+    case = DecodeCase(name, args.seed, device)
+    for _ in range(5):
+        case.step()
+    steps = max(20, min(200, args.steps // 5))
+    g_step, g_evt = time_graph(case, steps) if not args.no_graph else (None, None)
+    launch = time_events_per_launch(case, steps)
+    step_s = g_step if g_step is not None else time_eager(case, steps)
+    kernel_s = g_evt if g_evt is not None else launch
+    w = case.w
+    gbps = case.bytes / kernel_s / 1e9
+    line = {
+        "value": round(case.bytes / step_s / 1e9, 1),
+        "unit": "GB/s",
+        "tokens_per_s": round(w.B / step_s, 1),
+        "ms_per_step": step_s * 1e3,
+        "kernel_us": kernel_s * 1e6,
+        "per_launch_event_us": launch * 1e6,
+        "description": w.description,
+        "visible_keys_summed_over_batch_per_head": case.visible_keys,
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "kernel": "bsa_decode_kernel",
+                     "algorithmic_bytes_per_launch": case.bytes,
+                     "algorithmic_flop_per_launch": case.flops},
+    }
+    del case
+    torch.cuda.empty_cache()
+    return line
+
+
 def time_eager(case, steps):
     import torch
 
@@ -451,6 +531,8 @@ def main(argv=None):
                                                         causal=True)
         result["backward_worked_example_b32"] = side_line("worked_example_b32", args, device,
                                                           causal=False, backward=True)
+        result["decode_worked_example"] = decode_line("decode_worked_example", args, device)
+        result["decode_long"] = decode_line("decode_long", args, device)
 
     if not args.no_ceilings:
         result["practical_ceilings"] = practical_ceilings()

@@ -16,6 +16,9 @@ Recipe (stated once, used everywhere):
   the diagonal block is forced on so that no query block is empty.
 * Local+global block mask: blocks within +-radius of the diagonal, the global
   columns in every row, and the global rows dense.
+* Decode: q [B, H, d] and the KV caches [B, H, N, d] drawn like Q, K, V (one
+  generator seeded ``seed``, in that order); cached lengths uniform on
+  [1, N] from a generator seeded ``seed + 2``.
 """
 
 from __future__ import annotations
@@ -66,6 +69,15 @@ WORKLOADS = {
     # raised until the grid (32768 workgroups) fills the GPU many times over.
     "worked_example_b32": Workload("worked_example_b32", 32, 8, 4096, 64, 32, "bf16", "loglinear",
                                    "B=32 H=8 N=4096 d=64 block 32 (M=128), log-linear, bf16"),
+    # Decode: one new token per sequence against a KV cache of capacity N, the
+    # cached lengths drawn uniformly from [1, N] (a serving batch's length mix).
+    "decode_worked_example": Workload("decode_worked_example", 128, 8, 4096, 64, 32, "bf16",
+                                      "loglinear",
+                                      "decode, B=128 sequences, H=8, KV cache N=4096 d=64 block "
+                                      "32 (M=128), log-linear, lengths U[1, 4096], bf16"),
+    "decode_long": Workload("decode_long", 16, 32, 32768, 128, 64, "bf16", "loglinear",
+                            "decode, B=16 sequences, H=32, KV cache N=32768 d=128 block 64 "
+                            "(M=512), log-linear, lengths U[1, 32768], bf16"),
 }
 
 BERNOULLI_KEEP_P = 0.3
@@ -116,6 +128,23 @@ def workload_block_mask(w: Workload, seed: int = 0):
     if w.pattern == "bernoulli":
         return bernoulli_block_mask(w.M, seed=seed)
     raise ValueError(w.pattern)
+
+
+def decode_lengths(B: int, n_cap: int, seed: int = 0) -> torch.Tensor:
+    """Cached lengths of B sequences, uniform on [1, n_cap], int32 (CPU);
+    their own generator, seeded ``seed + 2``."""
+    g = torch.Generator("cpu").manual_seed(seed + 2)
+    return torch.randint(1, n_cap + 1, (B,), generator=g, dtype=torch.int64).to(torch.int32)
+
+
+def make_decode_inputs(B: int, H: int, n_cap: int, d: int, dtype=torch.bfloat16, seed: int = 0):
+    """q [B, H, d] and the caches [B, H, n_cap, d]: drawn in the order q, K, V
+    with one generator seeded ``seed`` (float32 N(0,1), rounded once)."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    q = torch.randn(B, H, d, generator=g, dtype=torch.float32).to(dtype)
+    k = torch.randn(B, H, n_cap, d, generator=g, dtype=torch.float32).to(dtype)
+    v = torch.randn(B, H, n_cap, d, generator=g, dtype=torch.float32).to(dtype)
+    return q, k, v
 
 
 def random_block_mask(M: int, p: float, seed: int, force_diagonal: bool = True) -> np.ndarray:
