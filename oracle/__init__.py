@@ -17,6 +17,8 @@ It is deliberately plain and slow:
 * ``oracle.backward`` -- the plain gradients dQ, dK, dV of that forward.
 * ``oracle.decode`` -- one new token against a KV cache: row t of the causal
   forward, over the cached positions its block's pattern row selects.
+* ``oracle.quantize`` -- int8 K/V with one scale per block (symmetric,
+  float32 decisions), dequantisation, and decode on a dequantised cache.
 
 Sources (web pages; cited by title and section):
 
@@ -54,6 +56,7 @@ from .pattern import (
 from .attention import block_sparse_attention_head, block_sparse_attention
 from .backward import block_sparse_attention_backward_head, block_sparse_attention_backward
 from .decode import block_sparse_decode_head, block_sparse_decode
+from .quantize import quantize_blocks, dequantize_blocks, block_sparse_decode_int8
 
 __all__ = [
     "ceil_log2",
@@ -73,4 +76,7 @@ __all__ = [
     "block_sparse_attention_backward",
     "block_sparse_decode_head",
     "block_sparse_decode",
+    "quantize_blocks",
+    "dequantize_blocks",
+    "block_sparse_decode_int8",
 ]

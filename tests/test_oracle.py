@@ -585,3 +585,61 @@ def test_decode_batched_wrapper_with_per_head_masks():
             o1, l1 = oracle.block_sparse_decode_head(q[b, h], k[b, h], v[b, h], lengths[b],
                                                      masks[h], bs)
             assert np.array_equal(o[b, h], o1) and lse[b, h] == l1
+
+
+# ----------------------------------------------------------------------------- int8 K/V
+
+
+def test_quantize_closed_form_power_of_two_scale():
+    # values k / 64, k = -127..127, with one element at 127 / 64: scale = 1/64
+    # exactly and every code equals k
+    bs, d = 32, 8
+    rng = np.random.default_rng(0)
+    k = rng.integers(-127, 128, size=(2, bs, d))
+    k[0, 5, 3] = 127
+    k[1, 0, 0] = -127
+    x = (k / 64.0).reshape(2 * bs, d).astype(np.float32)
+    codes, scales = oracle.quantize_blocks(x, bs)
+    assert scales.dtype == np.float32 and np.all(scales == np.float32(1 / 64))
+    assert np.array_equal(codes.reshape(2, bs, d), k.astype(np.int8))
+
+
+def test_quantize_bounds_extremes_and_zero_block():
+    bs, d = 16, 32
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((3, 4 * bs, d)).astype(np.float32)
+    x[1, bs:2 * bs] = 0.0  # an all-zero block
+    codes, scales = oracle.quantize_blocks(x, bs)
+    assert codes.dtype == np.int8 and scales.shape == (3, 4)
+    assert np.abs(codes.astype(int)).max() <= 127
+    assert scales[1, 1] == 0 and np.all(codes[1, bs:2 * bs] == 0)
+    deq = oracle.dequantize_blocks(codes, scales, bs)
+    step = np.repeat(scales, bs, axis=-1)[..., None].astype(np.float64)
+    assert np.all(np.abs(deq - x) <= step / 2 * (1 + 1e-6))
+    for b in range(3):
+        for j in range(4):
+            blk = x[b, j * bs:(j + 1) * bs]
+            if scales[b, j] == 0:
+                continue
+            r, c = np.unravel_index(np.abs(blk).argmax(), blk.shape)
+            assert abs(int(codes[b, j * bs + r, c])) == 127
+
+
+def test_decode_int8_on_dequantised_cache_equals_masked_sdpa():
+    rng = np.random.default_rng(2)
+    n_cap, d, bs, length = 256, 16, 32, 201
+    q = rng.standard_normal(d)
+    k = rng.standard_normal((n_cap, d)).astype(np.float32)
+    v = rng.standard_normal((n_cap, d)).astype(np.float32)
+    kc, ks = oracle.quantize_blocks(k, bs)
+    vc, vs = oracle.quantize_blocks(v, bs)
+    mask = random_block_mask(n_cap // bs, 0.5, 4)
+    o, lse = oracle.block_sparse_decode_int8(q[None, None], kc[None, None], ks[None, None],
+                                             vc[None, None], vs[None, None], [length], mask, bs)
+    kd = kc.astype(np.float64) * np.repeat(ks, bs)[:, None]
+    vd = vc.astype(np.float64) * np.repeat(vs, bs)[:, None]
+    vis = _decode_visible(length, mask, bs)
+    ref = _sdpa(q[None], kd[:length], vd[:length], mask=vis[None])[0]
+    np.testing.assert_allclose(o[0, 0], ref, rtol=0, atol=1e-12)
+    s = (kd[:length] @ q) / math.sqrt(d)
+    assert abs(lse[0, 0] - logsumexp(s[vis])) < 1e-12
