@@ -97,6 +97,11 @@ def _load():
     lib.bsa_backward.restype = i32
     lib.bsa_decode.argtypes = [vp] * 5 + [i32] * 6 + [vp] * 3 + [i64, ctypes.c_float, i32, vp]
     lib.bsa_decode.restype = i32
+    lib.bsa_quantize_kv.argtypes = [vp] * 3 + [i32] * 6 + [vp]
+    lib.bsa_quantize_kv.restype = i32
+    lib.bsa_decode_int8kv.argtypes = [vp] * 7 + [i32] * 6 + [vp] * 3 + [i64, ctypes.c_float,
+                                                                          i32, vp]
+    lib.bsa_decode_int8kv.restype = i32
     lib.bsa_status_string.argtypes = [i32]
     lib.bsa_status_string.restype = ctypes.c_char_p
     lib.bsa_abi_version.argtypes = []
@@ -367,6 +372,69 @@ def decode(q, k_cache, v_cache, seqlens, row_ptr, col_idx, block_size: int,
         FORWARD_PATTERN_PER_HEAD if per_head else 0, stream.cuda_stream)
     if st != BSA_OK:
         raise BsaError(st, "bsa_decode")
+    return out, lse
+
+
+def quantize_kv(x, block_size: int, *, codes=None, scales=None, stream=None):
+    """int8 codes and per-block float32 scales of a CUDA [B, H, N, d] tensor
+    (bsa_quantize_kv): returns (codes int8 [B, H, N, d], scales [B, H, N / bs])."""
+    import torch
+
+    if not x.is_cuda or not x.is_contiguous() or x.dim() != 4:
+        raise ValueError("x must be a contiguous CUDA tensor [B, H, N, d]")
+    B, H, N, d = x.shape
+    if codes is None:
+        codes = torch.empty(x.shape, dtype=torch.int8, device=x.device)
+    if scales is None:
+        scales = torch.empty((B, H, N // block_size), dtype=torch.float32, device=x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    st = _load().bsa_quantize_kv(x.data_ptr(), codes.data_ptr(), scales.data_ptr(), B, H, N, d,
+                                 int(block_size), _dtype_code(x), stream.cuda_stream)
+    if st != BSA_OK:
+        raise BsaError(st, "bsa_quantize_kv")
+    return codes, scales
+
+
+def decode_int8kv(q, k_codes, k_scales, v_codes, v_scales, seqlens, row_ptr, col_idx,
+                  block_size: int, scale: float | None = None, *, per_head: bool = False,
+                  out=None, lse=None, nnz: int | None = None, stream=None):
+    """``decode`` on an int8 KV cache with per-block scales (bsa_decode_int8kv):
+    caches int8 [B, H, N_cap, d] and scales float32 [B, H, N_cap / bs] as
+    ``quantize_kv`` writes them; q [B, H, d] bfloat16 or float32."""
+    import torch
+
+    if q.dim() != 3 or not q.is_cuda or not q.is_contiguous():
+        raise ValueError("q must be a contiguous CUDA tensor [B, H, d]")
+    B, H, d = q.shape
+    for name, t in (("k_codes", k_codes), ("v_codes", v_codes)):
+        if t.dtype != torch.int8 or not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError(f"{name} must be a contiguous int8 CUDA tensor [B, H, N_cap, d]")
+        if t.shape[0] != B or t.shape[1] != H or t.shape[3] != d:
+            raise ValueError(f"{name} disagrees with q on B, H or d")
+    n_cap = k_codes.shape[2]
+    for name, t in (("k_scales", k_scales), ("v_scales", v_scales)):
+        if (t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous()
+                or tuple(t.shape) != (B, H, n_cap // block_size)):
+            raise ValueError(f"{name} must be a float32 CUDA tensor [B, H, N_cap / block_size]")
+    if seqlens.dtype != torch.int32 or not seqlens.is_cuda or seqlens.numel() != B:
+        raise ValueError("seqlens must be an int32 CUDA tensor of B entries")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    if nnz is None:
+        nnz = col_idx.numel()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = _load().bsa_decode_int8kv(
+        q.data_ptr(), k_codes.data_ptr(), k_scales.data_ptr(), v_codes.data_ptr(),
+        v_scales.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, n_cap, d, int(block_size),
+        _dtype_code(q), seqlens.data_ptr(), row_ptr.data_ptr(), col_idx.data_ptr(), int(nnz),
+        0.0 if scale is None else float(scale), FORWARD_PATTERN_PER_HEAD if per_head else 0,
+        stream.cuda_stream)
+    if st != BSA_OK:
+        raise BsaError(st, "bsa_decode_int8kv")
     return out, lse
 
 

@@ -23,6 +23,14 @@
 //    its key (ds_swizzle butterflies); the unit max over the key groups.
 //  * At the end each wave sums its O over the key groups and the W waves
 //    merge (O, m, l) through LDS.
+//
+// int8 caches (the log-linear page, section 6.3: KV cache in int8, attention
+// in 16-bit floating point, one scale per block): codes convert exactly to
+// float; a unit lies in one block, so its K scale multiplies the unit's
+// scores and its V scale the unit's weights (the exponential sum uses the
+// unscaled weights).  The same file holds the quantiser that writes such a
+// cache: per (batch, head, block), scale = max|x| / 127 and
+// code = rint(x / scale) clamped to [-127, 127], both in float32.
 
 #include <hip/hip_runtime.h>
 
@@ -39,8 +47,10 @@ constexpr int kDecodeWaves = 4;
 
 struct DecParams {
   const void* q;
-  const void* k;
+  const void* k;        // cache: q's type, or int8 codes
   const void* v;
+  const float* k_scale;  // int8 caches: [batch, heads, M] per-block scales
+  const float* v_scale;
   void* o;
   float* lse;
   const int32_t* seqlens;
@@ -53,12 +63,12 @@ struct DecParams {
   float scale_log2;    // scale * log2(e)
 };
 
-template <typename T, int BS, int D>
+template <typename TC, int BS, int D>
 struct DecCfg {
-  static constexpr int E = 16 / (int)sizeof(T);  // elements per 16-byte chunk
+  static constexpr int E = 16 / (int)sizeof(TC);  // cache elements per 16-byte chunk
   static constexpr int LPK = D / E;              // lanes per key
   static constexpr int KPI = kWave / LPK;        // keys per load instruction
-  static constexpr int NI = 4;                   // loads per unit (K, and again V)
+  static constexpr int NI = BS / KPI < 4 ? BS / KPI : 4;  // loads per unit (K, and again V)
   static constexpr int KU = NI * KPI;            // keys per unit
   static constexpr int SUB = BS / KU;            // units per block
   static_assert(LPK <= 32 && SUB >= 1 && BS % KU == 0, "decode unit shape");
@@ -94,10 +104,15 @@ __device__ __forceinline__ float lanes_max(float x) {
   }
 }
 
-// The E elements of a 16-byte chunk as floats.
+// The elements of a 16-byte chunk as floats (exact for every type).
 template <typename T>
 __device__ __forceinline__ void chunk_to_float(const u32x4_t& c, float* f) {
-  if constexpr (std::is_same<T, __bf16>::value) {
+  if constexpr (std::is_same<T, int8_t>::value) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) f[4 * w + b] = (float)(int8_t)(c[w] >> (8 * b));
+  } else if constexpr (std::is_same<T, __bf16>::value) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       f[2 * w] = __uint_as_float(c[w] << 16);
@@ -115,9 +130,19 @@ __device__ __forceinline__ void store_elem(T* dst, float x) {
   else *dst = x;
 }
 
-template <typename T, int BS, int D>
+// E elements of q (type T) starting at `src`, as floats.
+template <typename T, int E>
+__device__ __forceinline__ void load_floats(const T* src, float* f) {
+  constexpr int per = 16 / (int)sizeof(T);
+#pragma unroll
+  for (int c = 0; c < E / per; ++c)
+    chunk_to_float<T>(*reinterpret_cast<const u32x4_t*>(src + c * per), f + c * per);
+}
+
+template <typename T, typename TC, int BS, int D>
 __global__ __launch_bounds__(kWave * kDecodeWaves) void bsa_decode_kernel(DecParams p) {
-  using C = DecCfg<T, BS, D>;
+  using C = DecCfg<TC, BS, D>;
+  constexpr bool kInt8 = std::is_same<TC, int8_t>::value;
   constexpr int W = kDecodeWaves;
   constexpr int E = C::E;
   constexpr int LPK = C::LPK;
@@ -144,15 +169,11 @@ __global__ __launch_bounds__(kWave * kDecodeWaves) void bsa_decode_kernel(DecPar
   const int nslots = (re - rs) * SUB;
 
   const size_t head = (size_t)bh * p.n_cap * D;
-  const T* K = static_cast<const T*>(p.k) + head;
-  const T* V = static_cast<const T*>(p.v) + head;
+  const TC* K = static_cast<const TC*>(p.k) + head;
+  const TC* V = static_cast<const TC*>(p.v) + head;
 
   float qf[E];
-  {
-    const u32x4_t qc =
-        *reinterpret_cast<const u32x4_t*>(static_cast<const T*>(p.q) + (size_t)bh * D + chunk * E);
-    chunk_to_float<T>(qc, qf);
-  }
+  load_floats<T, E>(static_cast<const T*>(p.q) + (size_t)bh * D + chunk * E, qf);
 
   // The row's entries, 64 at a time in one VGPR (lane l: entry base + l).
   int ent_base = -kWave;
@@ -210,16 +231,23 @@ __global__ __launch_bounds__(kWave * kDecodeWaves) void bsa_decode_kernel(DecPar
     if (sn < nslots) load(key_next, kn, vn);
 
     // scores of the lane's keys key_cur + KPI n + kq (scaled, log2 domain)
+    // int8: the unit's block scales (the scores' and the weights' factors)
+    float ks = c2, vs = 1.f;
+    if constexpr (kInt8) {
+      const size_t blk = (size_t)bh * p.M + key_cur / BS;
+      ks = p.k_scale[blk] * c2;
+      vs = p.v_scale[blk];
+    }
     float sc[C::NI];
     float mx = -INFINITY;
 #pragma unroll
     for (int n = 0; n < C::NI; ++n) {
       float kf[E];
-      chunk_to_float<T>(kr[n], kf);
+      chunk_to_float<TC>(kr[n], kf);
       float d = 0.f;
 #pragma unroll
       for (int e = 0; e < E; ++e) d = fmaf(qf[e], kf[e], d);
-      d = lanes_sum<1, LPK>(d) * c2;
+      d = lanes_sum<1, LPK>(d) * ks;
       sc[n] = key_cur + n * KPI + kq <= t ? d : -INFINITY;
       mx = __builtin_elementwise_maximum(mx, sc[n]);
     }
@@ -237,10 +265,11 @@ __global__ __launch_bounds__(kWave * kDecodeWaves) void bsa_decode_kernel(DecPar
       const bool visible = key_cur + n * KPI + kq <= t;
       const float pn = fast_exp2(sc[n] - m_new);
       l += visible ? pn : 0.f;
+      const float pv = pn * vs;
       float vf[E];
-      chunk_to_float<T>(vr[n], vf);
+      chunk_to_float<TC>(vr[n], vf);
 #pragma unroll
-      for (int e = 0; e < E; ++e) o[e] = visible ? fmaf(pn, vf[e], o[e]) : o[e];
+      for (int e = 0; e < E; ++e) o[e] = visible ? fmaf(pv, vf[e], o[e]) : o[e];
     }
 #pragma unroll
     for (int n = 0; n < C::NI; ++n) {
@@ -288,33 +317,32 @@ __global__ __launch_bounds__(kWave * kDecodeWaves) void bsa_decode_kernel(DecPar
   }
 }
 
-template <typename T, int BS, int D>
+template <typename T, typename TC, int BS, int D>
 bsa_status launch_decode(const DecParams& p, int num_wg, hipStream_t stream) {
-  hipLaunchKernelGGL((bsa_decode_kernel<T, BS, D>), dim3(num_wg), dim3(kWave * kDecodeWaves), 0,
-                     stream, p);
+  hipLaunchKernelGGL((bsa_decode_kernel<T, TC, BS, D>), dim3(num_wg), dim3(kWave * kDecodeWaves),
+                     0, stream, p);
   return hipGetLastError() == hipSuccess ? BSA_OK : BSA_ERR_HIP;
 }
 
-template <typename T>
+template <typename T, typename TC>
 bsa_status dispatch_decode(const DecParams& p, int num_wg, int bs, int d, hipStream_t stream) {
-  if (bs == 32 && d == 64) return launch_decode<T, 32, 64>(p, num_wg, stream);
-  if (bs == 32 && d == 128) return launch_decode<T, 32, 128>(p, num_wg, stream);
-  if (bs == 64 && d == 64) return launch_decode<T, 64, 64>(p, num_wg, stream);
-  if (bs == 64 && d == 128) return launch_decode<T, 64, 128>(p, num_wg, stream);
+  if (bs == 32 && d == 64) return launch_decode<T, TC, 32, 64>(p, num_wg, stream);
+  if (bs == 32 && d == 128) return launch_decode<T, TC, 32, 128>(p, num_wg, stream);
+  if (bs == 64 && d == 64) return launch_decode<T, TC, 64, 64>(p, num_wg, stream);
+  if (bs == 64 && d == 128) return launch_decode<T, TC, 64, 128>(p, num_wg, stream);
   return BSA_ERR_INVALID_ARGUMENT;
 }
 
-}  // namespace
-
-extern "C" bsa_status bsa_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
-                                 float* lse, int32_t batch, int32_t heads, int32_t cache_len,
-                                 int32_t head_dim, int32_t block_size, int32_t dtype,
-                                 const int32_t* seqlens, const int32_t* row_ptr,
-                                 const int32_t* col_idx, int64_t nnz, float scale, int32_t flags,
-                                 void* stream) {
+bsa_status decode_impl(const void* q, const void* k_cache, const float* k_scale,
+                       const void* v_cache, const float* v_scale, bool int8_cache, void* o,
+                       float* lse, int32_t batch, int32_t heads, int32_t cache_len,
+                       int32_t head_dim, int32_t block_size, int32_t dtype,
+                       const int32_t* seqlens, const int32_t* row_ptr, const int32_t* col_idx,
+                       int64_t nnz, float scale, int32_t flags, void* stream) {
   if (q == nullptr || k_cache == nullptr || v_cache == nullptr || o == nullptr ||
       seqlens == nullptr || row_ptr == nullptr || col_idx == nullptr)
     return BSA_ERR_NULL_POINTER;
+  if (int8_cache && (k_scale == nullptr || v_scale == nullptr)) return BSA_ERR_NULL_POINTER;
   if (dtype != BSA_DTYPE_F32 && dtype != BSA_DTYPE_BF16) return BSA_ERR_INVALID_ARGUMENT;
   if (block_size != 32 && block_size != 64) return BSA_ERR_INVALID_ARGUMENT;
   if (head_dim != 64 && head_dim != 128) return BSA_ERR_INVALID_ARGUMENT;
@@ -335,6 +363,8 @@ extern "C" bsa_status bsa_decode(const void* q, const void* k_cache, const void*
   p.q = q;
   p.k = k_cache;
   p.v = v_cache;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
   p.o = o;
   p.lse = lse;
   p.seqlens = seqlens;
@@ -350,6 +380,128 @@ extern "C" bsa_status bsa_decode(const void* q, const void* k_cache, const void*
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   const int num_wg = batch * heads;
-  if (dtype == BSA_DTYPE_F32) return dispatch_decode<float>(p, num_wg, block_size, head_dim, st);
-  return dispatch_decode<__bf16>(p, num_wg, block_size, head_dim, st);
+  if (dtype == BSA_DTYPE_F32)
+    return int8_cache ? dispatch_decode<float, int8_t>(p, num_wg, block_size, head_dim, st)
+                      : dispatch_decode<float, float>(p, num_wg, block_size, head_dim, st);
+  return int8_cache ? dispatch_decode<__bf16, int8_t>(p, num_wg, block_size, head_dim, st)
+                    : dispatch_decode<__bf16, __bf16>(p, num_wg, block_size, head_dim, st);
+}
+
+// ---------------------------------------------------------------- quantiser
+// One workgroup per (batch, head, block): the block's BS x D values are read
+// once into registers (16-byte chunks), reduced to max|x|, then coded.
+constexpr int kQuantThreads = 256;
+
+template <typename T, int BS, int D>
+__global__ __launch_bounds__(kQuantThreads) void bsa_quantize_kernel(const T* __restrict__ x,
+                                                                    int8_t* __restrict__ codes,
+                                                                    float* __restrict__ scales) {
+  constexpr int per = 16 / (int)sizeof(T);      // elements per 16-byte chunk
+  constexpr int kChunks = BS * D / per;
+  constexpr int kPerThread = kChunks / kQuantThreads;
+  static_assert(kChunks % kQuantThreads == 0 && per % 4 == 0, "quantiser shape");
+  __shared__ float wave_max[kQuantThreads / kWave];
+
+  const size_t base = (size_t)blockIdx.x * BS * D;
+  float f[kPerThread][per];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    const int c = i * kQuantThreads + threadIdx.x;
+    chunk_to_float<T>(*reinterpret_cast<const u32x4_t*>(x + base + (size_t)c * per), f[i]);
+#pragma unroll
+    for (int e = 0; e < per; ++e) amax = fmaxf(amax, fabsf(f[i][e]));
+  }
+  amax = lanes_max<1, kWave>(amax);
+  if ((threadIdx.x & (kWave - 1)) == 0) wave_max[threadIdx.x / kWave] = amax;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kQuantThreads / kWave; ++w) amax = fmaxf(amax, wave_max[w]);
+  const float scale = amax / 127.0f;  // correctly rounded float32 division
+  if (threadIdx.x == 0) scales[blockIdx.x] = scale;
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    const int c = i * kQuantThreads + threadIdx.x;
+    uint32_t w[per / 4];
+#pragma unroll
+    for (int k = 0; k < per / 4; ++k) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        float qv = scale > 0.f ? rintf(f[i][4 * k + b] / scale) : 0.f;
+        qv = fminf(fmaxf(qv, -127.f), 127.f);
+        word |= ((uint32_t)(int32_t)qv & 0xFFu) << (8 * b);
+      }
+      w[k] = word;
+    }
+    int8_t* dst = codes + base + (size_t)c * per;
+    if constexpr (per == 8) {
+      *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{w[0], w[1]};
+    } else {
+      *reinterpret_cast<uint32_t*>(dst) = w[0];
+    }
+  }
+}
+
+template <typename T, int BS, int D>
+bsa_status launch_quantize(const void* x, int8_t* codes, float* scales, int64_t blocks,
+                           hipStream_t stream) {
+  hipLaunchKernelGGL((bsa_quantize_kernel<T, BS, D>), dim3((uint32_t)blocks),
+                     dim3(kQuantThreads), 0, stream, static_cast<const T*>(x), codes, scales);
+  return hipGetLastError() == hipSuccess ? BSA_OK : BSA_ERR_HIP;
+}
+
+template <typename T>
+bsa_status dispatch_quantize(const void* x, int8_t* codes, float* scales, int64_t blocks, int bs,
+                             int d, hipStream_t stream) {
+  if (bs == 32 && d == 64) return launch_quantize<T, 32, 64>(x, codes, scales, blocks, stream);
+  if (bs == 32 && d == 128) return launch_quantize<T, 32, 128>(x, codes, scales, blocks, stream);
+  if (bs == 64 && d == 64) return launch_quantize<T, 64, 64>(x, codes, scales, blocks, stream);
+  if (bs == 64 && d == 128) return launch_quantize<T, 64, 128>(x, codes, scales, blocks, stream);
+  return BSA_ERR_INVALID_ARGUMENT;
+}
+
+}  // namespace
+
+extern "C" bsa_status bsa_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
+                                 float* lse, int32_t batch, int32_t heads, int32_t cache_len,
+                                 int32_t head_dim, int32_t block_size, int32_t dtype,
+                                 const int32_t* seqlens, const int32_t* row_ptr,
+                                 const int32_t* col_idx, int64_t nnz, float scale, int32_t flags,
+                                 void* stream) {
+  return decode_impl(q, k_cache, nullptr, v_cache, nullptr, false, o, lse, batch, heads,
+                     cache_len, head_dim, block_size, dtype, seqlens, row_ptr, col_idx, nnz,
+                     scale, flags, stream);
+}
+
+extern "C" bsa_status bsa_decode_int8kv(const void* q, const int8_t* k_codes,
+                                        const float* k_scales, const int8_t* v_codes,
+                                        const float* v_scales, void* o, float* lse,
+                                        int32_t batch, int32_t heads, int32_t cache_len,
+                                        int32_t head_dim, int32_t block_size, int32_t dtype,
+                                        const int32_t* seqlens, const int32_t* row_ptr,
+                                        const int32_t* col_idx, int64_t nnz, float scale,
+                                        int32_t flags, void* stream) {
+  return decode_impl(q, k_codes, k_scales, v_codes, v_scales, true, o, lse, batch, heads,
+                     cache_len, head_dim, block_size, dtype, seqlens, row_ptr, col_idx, nnz,
+                     scale, flags, stream);
+}
+
+extern "C" bsa_status bsa_quantize_kv(const void* x, int8_t* codes, float* scales, int32_t batch,
+                                      int32_t heads, int32_t seq_len, int32_t head_dim,
+                                      int32_t block_size, int32_t dtype, void* stream) {
+  if (x == nullptr || codes == nullptr || scales == nullptr) return BSA_ERR_NULL_POINTER;
+  if (dtype != BSA_DTYPE_F32 && dtype != BSA_DTYPE_BF16) return BSA_ERR_INVALID_ARGUMENT;
+  if (block_size != 32 && block_size != 64) return BSA_ERR_INVALID_ARGUMENT;
+  if (head_dim != 64 && head_dim != 128) return BSA_ERR_INVALID_ARGUMENT;
+  if (batch <= 0 || heads <= 0 || seq_len <= 0 || seq_len % block_size != 0) return BSA_ERR_SHAPE;
+  const uintptr_t align = reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(codes);
+  if (align % 16 != 0) return BSA_ERR_INVALID_ARGUMENT;
+  const int64_t blocks = (int64_t)batch * heads * (seq_len / block_size);
+  if (blocks > INT32_MAX) return BSA_ERR_SHAPE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (dtype == BSA_DTYPE_F32)
+    return dispatch_quantize<float>(x, codes, scales, blocks, block_size, head_dim, st);
+  return dispatch_quantize<__bf16>(x, codes, scales, blocks, block_size, head_dim, st);
 }

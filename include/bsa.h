@@ -291,6 +291,53 @@ bsa_status bsa_decode(const void* q, const void* k_cache, const void* v_cache, v
                       const int32_t* seqlens, const int32_t* row_ptr, const int32_t* col_idx,
                       int64_t nnz, float scale, int32_t flags, void* stream);
 
+/*
+ * bsa_quantize_kv -- int8 codes and one scale per block of a K or V tensor.
+ *
+ * The log-linear page's section 6.3 keeps the KV cache in int8 with one
+ * scale per block and computes attention in 16-bit floating point.  The
+ * quantiser here is symmetric, per (batch, head, block of block_size
+ * positions) over all head_dim features, every decision in float32:
+ *   scale = max|x| / 127,  code = clamp(rint(x / scale), -127, 127)
+ * (correctly rounded divisions, ties to even; an all-zero block gets scale 0
+ * and codes 0).  Values are code * scale.
+ *
+ * x       device [batch, heads, seq_len, head_dim] of `dtype`, finite,
+ *         16-byte aligned.
+ * codes   device, caller-owned int8 [batch, heads, seq_len, head_dim],
+ *         16-byte aligned; written.
+ * scales  device, caller-owned float32 [batch, heads, seq_len / block_size];
+ *         written.
+ * Supported: dtype BF16 or F32, block_size 32 or 64, head_dim 64 or 128.
+ * One launch on `stream`, not synchronised.  Errors as for bsa_forward.
+ */
+bsa_status bsa_quantize_kv(const void* x, int8_t* codes, float* scales, int32_t batch,
+                           int32_t heads, int32_t seq_len, int32_t head_dim, int32_t block_size,
+                           int32_t dtype, void* stream);
+
+/*
+ * bsa_decode_int8kv -- bsa_decode on an int8 KV cache with per-block scales.
+ *
+ * Same computation as bsa_decode with K_p = k_codes[p] * k_scales[p / bs]
+ * and V_p = v_codes[p] * v_scales[p / bs] (per batch and head), as written by
+ * bsa_quantize_kv.  The codes convert exactly; the K scale multiplies the
+ * scores and the V scale the softmax weights (section 6.3 of the log-linear
+ * page: int8 storage, floating-point attention).
+ *
+ * q, o, lse, seqlens, row_ptr, col_idx, nnz, scale, flags, stream: as for
+ *          bsa_decode (`dtype` is q's and o's type).
+ * k_codes, v_codes    device int8 [batch, heads, cache_len, head_dim],
+ *          16-byte aligned.
+ * k_scales, v_scales  device float32 [batch, heads, cache_len / block_size].
+ * Errors as for bsa_decode (NULL scales: BSA_ERR_NULL_POINTER).
+ */
+bsa_status bsa_decode_int8kv(const void* q, const int8_t* k_codes, const float* k_scales,
+                             const int8_t* v_codes, const float* v_scales, void* o, float* lse,
+                             int32_t batch, int32_t heads, int32_t cache_len, int32_t head_dim,
+                             int32_t block_size, int32_t dtype, const int32_t* seqlens,
+                             const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz,
+                             float scale, int32_t flags, void* stream);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* bsa_status_string(int32_t status);
 

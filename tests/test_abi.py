@@ -147,3 +147,20 @@ def test_decode_invalid_argument(over):
 def test_decode_shape_errors(over):
     # flags 2 (one pattern per head) needs heads * M <= nnz
     assert _dec(**over) == 3
+
+
+def test_quantize_and_int8_decode_host_errors():
+    lib = bsa._load()
+    f = ctypes.c_float
+    q = lambda **o: lib.bsa_quantize_kv(o.get("x", FAKE), o.get("codes", FAKE),
+                                        o.get("scales", FAKE), o.get("B", 2), o.get("H", 4),
+                                        o.get("N", 1024), o.get("d", 64), o.get("bs", 32),
+                                        o.get("dtype", 1), None)
+    assert q(x=None) == 1 and q(codes=None) == 1 and q(scales=None) == 1
+    assert q(d=96) == 2 and q(bs=16) == 2 and q(dtype=3) == 2 and q(codes=FAKE + 8) == 2
+    assert q(N=1000) == 3 and q(B=0) == 3
+    d8 = lambda **o: lib.bsa_decode_int8kv(
+        FAKE, FAKE, o.get("ks", FAKE), FAKE, o.get("vs", FAKE), FAKE, FAKE, 4, 8, 4096, 64, 32,
+        1, FAKE, FAKE, FAKE, o.get("nnz", 1251), f(0.0), o.get("flags", 0), None)
+    assert d8(ks=None) == 1 and d8(vs=None) == 1
+    assert d8(flags=1) == 2 and d8(nnz=5) == 3
