@@ -133,7 +133,7 @@ class DecodeCase:
     """One decode step: a new token for each of B sequences against a KV cache
     of capacity N (cached lengths uniform on [1, N]), log-linear pattern."""
 
-    def __init__(self, name, seed, device):
+    def __init__(self, name, seed, device, int8=False):
         import numpy as np
         import torch
 
@@ -141,10 +141,15 @@ class DecodeCase:
         from synthetic_inputs import WORKLOADS, decode_lengths, make_decode_inputs
 
         self.bsa = bsa
+        self.int8 = int8
         self.w = w = WORKLOADS[name]
         q, k, v = make_decode_inputs(w.B, w.H, w.N, w.d, w.torch_dtype, seed)
         lengths = decode_lengths(w.B, w.N, seed)
         self.q, self.k, self.v = (t.to(device) for t in (q, k, v))
+        if int8:  # the cache as int8 codes + per-block scales (quantised once, untimed)
+            self.kc, self.ks = bsa.quantize_kv(self.k, w.block_size)
+            self.vc, self.vs = bsa.quantize_kv(self.v, w.block_size)
+            del self.k, self.v
         self.lengths = lengths.to(device)
         self.out = torch.empty_like(self.q)
         self.lse = torch.empty((w.B, w.H), dtype=torch.float32, device=device)
@@ -161,25 +166,39 @@ class DecodeCase:
                 if j <= i:
                     visible += min(w.block_size, t - int(j) * w.block_size + 1)
         elt = 2 if w.dtype == "bf16" else 4
+        kv_elt = 1 if int8 else elt
         self.visible_keys = visible
-        # Algorithmic bytes: every visible K and V row read once, q read, O and
-        # LSE written; flop: q.k and p.v per visible key.
-        self.bytes = (2.0 * visible * w.H * w.d * elt + 2.0 * w.B * w.H * w.d * elt
+        # Algorithmic bytes: every visible K and V row read once (int8: plus the
+        # two scales of each visible block), q read, O and LSE written; flop:
+        # q.k and p.v per visible key.
+        self.bytes = (2.0 * visible * w.H * w.d * kv_elt + 2.0 * w.B * w.H * w.d * elt
                       + 4.0 * w.B * w.H)
+        if int8:
+            blocks = 0
+            for L in lengths.tolist():
+                i = (L - 1) // w.block_size
+                blocks += sum(1 for j in ci_h[rp_h[i]:rp_h[i + 1]] if j <= i)
+            self.bytes += 8.0 * blocks * w.H
         self.flops = 4.0 * visible * w.H * w.d
 
     def step(self):
         w = self.w
-        self.bsa.decode(self.q, self.k, self.v, self.lengths, self.rp, self.ci, w.block_size,
-                        out=self.out, lse=self.lse, nnz=self.nnz)
+        if self.int8:
+            self.bsa.decode_int8kv(self.q, self.kc, self.ks, self.vc, self.vs, self.lengths,
+                                   self.rp, self.ci, w.block_size, out=self.out, lse=self.lse,
+                                   nnz=self.nnz)
+        else:
+            self.bsa.decode(self.q, self.k, self.v, self.lengths, self.rp, self.ci, w.block_size,
+                            out=self.out, lse=self.lse, nnz=self.nnz)
 
 
-def decode_line(name, args, device):
-    """A graph-timed decode step (bsa_decode): HBM-bound, reported in GB/s of
-    algorithmic bytes against the 8 TB/s peak, and in tokens per second."""
+def decode_line(name, args, device, int8=False):
+    """A graph-timed decode step (bsa_decode, or bsa_decode_int8kv on an int8
+    cache): HBM-bound, reported in GB/s of algorithmic bytes against the
+    8 TB/s peak, and in tokens per second."""
     import torch
 
-    case = DecodeCase(name, args.seed, device)
+    case = DecodeCase(name, args.seed, device, int8=int8)
     for _ in range(5):
         case.step()
     steps = max(20, min(200, args.steps // 5))
@@ -201,6 +220,7 @@ def decode_line(name, args, device):
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None,
                      "kernel": "bsa_decode_kernel",
+                     "kv_cache": "int8 + per-block float32 scales" if int8 else w.dtype,
                      "algorithmic_bytes_per_launch": case.bytes,
                      "algorithmic_flop_per_launch": case.flops},
     }
@@ -533,6 +553,9 @@ def main(argv=None):
                                                           causal=False, backward=True)
         result["decode_worked_example"] = decode_line("decode_worked_example", args, device)
         result["decode_long"] = decode_line("decode_long", args, device)
+        result["decode_worked_example_int8kv"] = decode_line("decode_worked_example", args,
+                                                             device, int8=True)
+        result["decode_long_int8kv"] = decode_line("decode_long", args, device, int8=True)
 
     if not args.no_ceilings:
         result["practical_ceilings"] = practical_ceilings()

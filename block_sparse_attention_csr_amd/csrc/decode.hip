@@ -26,9 +26,11 @@
 //
 // int8 caches (the log-linear page, section 6.3: KV cache in int8, attention
 // in 16-bit floating point, one scale per block): codes convert exactly to
-// float; a unit lies in one block, so its K scale multiplies the unit's
-// scores and its V scale the unit's weights (the exponential sum uses the
-// unscaled weights).  The same file holds the quantiser that writes such a
+// float, each as (code + 128) from one unsigned-byte conversion, the 128
+// taken off once per sum (q's chunk sum for the scores, the weight sum for
+// O); a unit lies in one block, so its K scale multiplies the unit's scores
+// and its V scale the unit's weights (the exponential sum uses the unscaled
+// weights).  The same file holds the quantiser that writes such a
 // cache: per (batch, head, block), scale = max|x| / 127 and
 // code = rint(x / scale) clamped to [-127, 127], both in float32.
 
@@ -124,6 +126,17 @@ __device__ __forceinline__ void chunk_to_float(const u32x4_t& c, float* f) {
   }
 }
 
+// int8 codes as floats plus 128 (one unsigned-byte conversion each; the
+// caller takes the 128 off once per sum instead of once per element).
+__device__ __forceinline__ void codes_to_float_biased(const u32x4_t& c, float* f) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t u = c[w] ^ 0x80808080u;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) f[4 * w + b] = (float)((u >> (8 * b)) & 0xFFu);
+  }
+}
+
 template <typename T>
 __device__ __forceinline__ void store_elem(T* dst, float x) {
   if constexpr (std::is_same<T, __bf16>::value) *dst = (__bf16)x;  // round to nearest even
@@ -174,6 +187,11 @@ __global__ __launch_bounds__(kWave * kDecodeWaves) void bsa_decode_kernel(DecPar
 
   float qf[E];
   load_floats<T, E>(static_cast<const T*>(p.q) + (size_t)bh * D + chunk * E, qf);
+  float qsum = 0.f;  // int8: sum of the lane's q elements (for the code offset)
+  if constexpr (kInt8) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) qsum += qf[e];
+  }
 
   // The row's entries, 64 at a time in one VGPR (lane l: entry base + l).
   int ent_base = -kWave;
@@ -203,12 +221,18 @@ __global__ __launch_bounds__(kWave * kDecodeWaves) void bsa_decode_kernel(DecPar
     }
     return nslots;
   };
-  auto load = [&](int key0, u32x4_t (&kr)[C::NI], u32x4_t (&vr)[C::NI]) {
+  // A unit's loads: its K and V chunks and, for int8, its block's two scales
+  // (so that no load is left for the compute to wait on).
+  auto load = [&](int key0, u32x4_t (&kr)[C::NI], u32x4_t (&vr)[C::NI], f32x2_t& sc2) {
 #pragma unroll
     for (int n = 0; n < C::NI; ++n) {
       const size_t off = (size_t)(key0 + n * KPI + kq) * D + chunk * E;
       kr[n] = *reinterpret_cast<const u32x4_t*>(K + off);
       vr[n] = *reinterpret_cast<const u32x4_t*>(V + off);
+    }
+    if constexpr (kInt8) {
+      const size_t blk = (size_t)bh * p.M + key0 / BS;
+      sc2 = f32x2_t{p.k_scale[blk], p.v_scale[blk]};
     }
   };
 
@@ -218,33 +242,37 @@ __global__ __launch_bounds__(kWave * kDecodeWaves) void bsa_decode_kernel(DecPar
   float o[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) o[e] = 0.f;
+  float pvsum = 0.f;  // int8: sum of the lane's V weights (for the code offset)
 
   int key_cur = -1;
   int s = next_slot(wave, key_cur);
   u32x4_t kr[C::NI], vr[C::NI];
-  if (s < nslots) load(key_cur, kr, vr);
+  f32x2_t sc_cur = {1.f, 1.f};
+  if (s < nslots) load(key_cur, kr, vr, sc_cur);
   while (s < nslots) {
     // the next unit's loads go out before this unit's arithmetic
     int key_next = -1;
     const int sn = next_slot(s + W, key_next);
     u32x4_t kn[C::NI], vn[C::NI];
-    if (sn < nslots) load(key_next, kn, vn);
+    f32x2_t sc_next = {1.f, 1.f};
+    if (sn < nslots) load(key_next, kn, vn, sc_next);
 
     // scores of the lane's keys key_cur + KPI n + kq (scaled, log2 domain)
     // int8: the unit's block scales (the scores' and the weights' factors)
-    float ks = c2, vs = 1.f;
-    if constexpr (kInt8) {
-      const size_t blk = (size_t)bh * p.M + key_cur / BS;
-      ks = p.k_scale[blk] * c2;
-      vs = p.v_scale[blk];
-    }
+    const float ks = sc_cur[0] * c2;
+    const float vs = sc_cur[1];
     float sc[C::NI];
     float mx = -INFINITY;
 #pragma unroll
     for (int n = 0; n < C::NI; ++n) {
       float kf[E];
-      chunk_to_float<TC>(kr[n], kf);
       float d = 0.f;
+      if constexpr (kInt8) {
+        codes_to_float_biased(kr[n], kf);  // code + 128
+        d = -128.f * qsum;
+      } else {
+        chunk_to_float<TC>(kr[n], kf);
+      }
 #pragma unroll
       for (int e = 0; e < E; ++e) d = fmaf(qf[e], kf[e], d);
       d = lanes_sum<1, LPK>(d) * ks;
@@ -256,6 +284,7 @@ __global__ __launch_bounds__(kWave * kDecodeWaves) void bsa_decode_kernel(DecPar
     const float alpha = fast_exp2(m2 - m_new);  // 0 on the first unit (m2 = -inf)
     m2 = m_new;
     l *= alpha;
+    pvsum *= alpha;
 #pragma unroll
     for (int e = 0; e < E; ++e) o[e] *= alpha;
 #pragma unroll
@@ -267,7 +296,12 @@ __global__ __launch_bounds__(kWave * kDecodeWaves) void bsa_decode_kernel(DecPar
       l += visible ? pn : 0.f;
       const float pv = pn * vs;
       float vf[E];
-      chunk_to_float<TC>(vr[n], vf);
+      if constexpr (kInt8) {
+        codes_to_float_biased(vr[n], vf);  // code + 128
+        pvsum += visible ? pv : 0.f;
+      } else {
+        chunk_to_float<TC>(vr[n], vf);
+      }
 #pragma unroll
       for (int e = 0; e < E; ++e) o[e] = visible ? fmaf(pv, vf[e], o[e]) : o[e];
     }
@@ -276,10 +310,15 @@ __global__ __launch_bounds__(kWave * kDecodeWaves) void bsa_decode_kernel(DecPar
       kr[n] = kn[n];
       vr[n] = vn[n];
     }
+    sc_cur = sc_next;
     key_cur = key_next;
     s = sn;
   }
 
+  if constexpr (kInt8) {  // take off the 128 the biased V codes carried
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] = fmaf(-128.f, pvsum, o[e]);
+  }
   // Sum over the key groups: every lane of chunk c then holds the wave's
   // O[c E .. c E + E) and l (each key's weight counted once per group).
   l = lanes_sum<LPK, kWave>(l);
