@@ -34,11 +34,13 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix
 PEAK_HBM_GBPS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "block_sparse_attention_csr_amd", "csrc", "forward.hip")
+DECODE_SRC = os.path.join(ROOT, "block_sparse_attention_csr_amd", "csrc", "decode.hip")
 PROFILES = os.path.join(ROOT, "profiles")
+DECODE_METRIC = "decode GB/s (algorithmic bytes: visible K/V rows) + % of 8 TB/s HBM peak"
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
+def kernel_source_hash(path: str = KERNEL_SRC) -> str:
+    with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
@@ -60,6 +62,8 @@ def parse_args(argv=None):
     p.add_argument("--causal", action="store_true",
                    help="time the causal forward (keys after each query hidden; the pattern "
                         "built causal) instead of the plain one")
+    p.add_argument("--int8-kv", action="store_true",
+                   help="with a decode workload: decode on the int8 cache (bsa_decode_int8kv)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run 5 device-to-device copies of 1 GiB (reference kernel for "
                         "scaling HBM byte counters) and exit")
@@ -208,6 +212,7 @@ def decode_line(name, args, device, int8=False):
     kernel_s = g_evt if g_evt is not None else launch
     w = case.w
     gbps = case.bytes / kernel_s / 1e9
+    traffic = load_traffic(name + ("_int8kv" if int8 else ""), "bsa_decode", DECODE_SRC)
     line = {
         "value": round(case.bytes / step_s / 1e9, 1),
         "unit": "GB/s",
@@ -218,7 +223,9 @@ def decode_line(name, args, device, int8=False):
         "description": w.description,
         "visible_keys_summed_over_batch_per_head": case.visible_keys,
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,
-                     "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": traffic,
+                     "traffic_over_algorithmic": None if traffic is None
+                     else round(traffic / case.bytes, 3),
                      "kernel": "bsa_decode_kernel",
                      "kv_cache": "int8 + per-block float32 scales" if int8 else w.dtype,
                      "algorithmic_bytes_per_launch": case.bytes,
@@ -290,15 +297,15 @@ def time_events_per_launch(case, steps):
     return sum(a.elapsed_time(b) for a, b in evs) * 1e-3 / steps
 
 
-def load_traffic(workload: str):
+def load_traffic(workload: str, prefix: str = "bsa_fwd", src: str = KERNEL_SRC):
     """HBM bytes per launch from committed rocprofv3 counter summaries, valid
     only while the kernel source is unchanged since the counters were taken."""
-    path = os.path.join(PROFILES, f"bsa_fwd_traffic_{workload}.json")
+    path = os.path.join(PROFILES, f"{prefix}_traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash(src):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -468,6 +475,22 @@ def main(argv=None):
         return 1
     device = torch.device("cuda:0")
     torch.cuda.set_device(device)
+
+    if args.workload.startswith("decode"):
+        # A decode workload on its own (profiling and side measurements).
+        line = decode_line(args.workload, args, device, int8=args.int8_kv)
+        from synthetic_inputs import WORKLOADS
+
+        w = WORKLOADS[args.workload]
+        print(json.dumps({
+            "metric": DECODE_METRIC, "value": line.pop("value"), "unit": line.pop("unit"),
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": line.pop("ms_per_step"), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded)",
+            "config": {"workload": w.name, "description": line.pop("description"),
+                       "kv_cache": "int8" if args.int8_kv else w.dtype},
+            **line}), flush=True)
+        return 0
 
     case = Case(args.workload, args.seed, device, causal=args.causal)
     w = case.w
