@@ -93,8 +93,10 @@ struct Cfg {
   static_assert(L::kCopies % SW == 0, "entry parts must split evenly over a slice's waves");
   static constexpr int kParts = L::kCopies / SW;  // 1 KB copies per wave per entry
   // Three tile buffers (prefetch distance 2) while they leave room for three
-  // workgroups per CU, else two (prefetch distance 1).
-  static constexpr int NB = 3 * kSliceBytes <= 48 * 1024 ? 3 : 2;
+  // workgroups per CU, else two (prefetch distance 1).  Key-split shapes keep
+  // two: their slices already run KS entries ahead together, and the smaller
+  // footprint keeps a whole small grid resident at once.
+  static constexpr int NB = KS == 1 && 3 * kSliceBytes <= 48 * 1024 ? 3 : 2;
   // Shapes whose buffers do not fit a workgroup's LDS are not instantiated.
   static constexpr bool kValid = NB * kSliceBytes + 1024 <= 160 * 1024 &&
                                  (KS - 1) * SW * partial_bytes<D>() <= kSliceBytes;
@@ -486,8 +488,10 @@ size_t lds_for(int dtype, int bs, int d, int group, int ks, int M) {
 
 // Workgroup shape.  Large grids: G query blocks per workgroup share their K/V
 // tiles (4 blocks of 32 rows, or 2 of 64).  Smaller grids: one query block
-// per workgroup, which has the shortest critical path; only grids with fewer
-// query blocks than CUs also split each CSR row over KS key-slice wave sets.
+// per workgroup, which has the shortest critical path, with each CSR row split
+// over KS key-slice wave sets while the grid stays within two waves per SIMD
+// (the worked example, 1024 query blocks of one wave, runs 9.2 us with KS = 2
+// against 9.8 us with KS = 1).
 void choose_shape(int64_t bhm, int bs, int d, int dtype, int M, int* group, int* key_split) {
   constexpr int64_t kCus = 256;
   constexpr int64_t kLargeGrid = 8 * 4 * kCus;  // 8 query waves per SIMD
@@ -501,7 +505,9 @@ void choose_shape(int64_t bhm, int bs, int d, int dtype, int M, int* group, int*
     g = bs == 32 ? 4 : 2;
     if (!fits(g, 1)) g = 1;
   } else {
-    while (ks < 4 && qw * ks * 2 <= kMaxWaves && bhm * ks < kCus && fits(1, ks * 2)) ks *= 2;
+    while (ks < 4 && qw * ks * 2 <= kMaxWaves && bhm * qw * ks * 2 <= 2 * 4 * kCus &&
+           fits(1, ks * 2))
+      ks *= 2;
   }
   *group = g;
   *key_split = ks;
