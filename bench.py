@@ -406,6 +406,8 @@ class BackwardCase:
         rp, ci = bsa.build_pattern(w.N, w.block_size, mask=self.fwd.mask, causal=causal)
         cp, ri = bsa.transpose_pattern(rp, ci)
         self.pat = [t.to(device) for t in (rp, ci, cp, ri)]
+        # longest-first block orders of the CSR and the CSC (host, once)
+        self.orders = [bsa.pattern_order(t).to(device) for t in (rp, cp)]
         self.grads = [torch.empty_like(self.fwd.q) for _ in range(3)]
         self.delta = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=device)
         self.fwd.step()
@@ -419,7 +421,8 @@ class BackwardCase:
         f = self.fwd
         dq, dk, dv = self.grads
         self.bsa.backward(f.q, f.k, f.v, f.out, f.lse, self.dout, *self.pat, f.w.block_size,
-                          causal=f.causal, dq=dq, dk=dk, dv=dv, delta=self.delta)
+                          causal=f.causal, dq=dq, dk=dk, dv=dv, delta=self.delta,
+                          row_order=self.orders[0], col_order=self.orders[1])
 
 
 def side_line(name, args, device, causal, backward=False):

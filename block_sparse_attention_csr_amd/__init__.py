@@ -22,6 +22,7 @@ import numpy as np
 __all__ = [
     "BsaError", "build_pattern", "forward", "backward", "transpose_pattern", "status_string",
     "abi_version", "library_path", "PatternCache", "BSA_OK", "stack_head_patterns",
+    "pattern_order", "decode", "quantize_kv", "decode_int8kv",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -93,7 +94,9 @@ def _load():
     lib.bsa_forward_ex.restype = i32
     lib.bsa_transpose_pattern.argtypes = [i32, p32, p32, i64, p32, p32]
     lib.bsa_transpose_pattern.restype = i32
-    lib.bsa_backward.argtypes = [vp] * 10 + [i32] * 6 + [vp] * 4 + [i64, ctypes.c_float, i32, vp]
+    lib.bsa_backward.argtypes = [vp] * 10 + [i32] * 6 + [vp] * 6 + [i64, ctypes.c_float, i32, vp]
+    lib.bsa_pattern_order.argtypes = [i32, p32, p32]
+    lib.bsa_pattern_order.restype = i32
     lib.bsa_backward.restype = i32
     lib.bsa_decode.argtypes = [vp] * 5 + [i32] * 6 + [vp] * 3 + [i64, ctypes.c_float, i32, vp]
     lib.bsa_decode.restype = i32
@@ -289,15 +292,33 @@ def transpose_pattern(row_ptr, col_idx):
     return torch.from_numpy(cp), torch.from_numpy(ri[:ci.size].copy())
 
 
+def pattern_order(ptr):
+    """bsa_pattern_order: the blocks of a CSR row_ptr (or CSC col_ptr), most
+    entries first, as a CPU int32 tensor of M entries."""
+    import torch
+
+    pt = np.ascontiguousarray(np.asarray(ptr.cpu() if hasattr(ptr, "cpu") else ptr,
+                                         dtype=np.int32))
+    M = pt.size - 1
+    order = np.zeros(max(M, 1), dtype=np.int32)
+    p32 = ctypes.POINTER(ctypes.c_int32)
+    st = _load().bsa_pattern_order(M, pt.ctypes.data_as(p32), order.ctypes.data_as(p32))
+    if st != BSA_OK:
+        raise BsaError(st, "bsa_pattern_order")
+    return torch.from_numpy(order[:M].copy())
+
+
 def backward(q, k, v, o, lse, dout, row_ptr, col_idx, col_ptr, row_idx, block_size: int,
              scale: float | None = None, *, causal: bool = False, dq=None, dk=None, dv=None,
-             delta=None, stream=None):
+             delta=None, stream=None, row_order=None, col_order=None):
     """Gradients (dq, dk, dv) of ``forward`` for the upstream gradient ``dout``.
 
     q, k, v, o, dout: CUDA [B, H, N, d] tensors of one dtype; lse the
     forward's LSE; row_ptr/col_idx the forward's device CSR and
-    col_ptr/row_idx its device CSC (``transpose_pattern``).  Enqueued on the
-    current stream (or ``stream``), not synchronised.
+    col_ptr/row_idx its device CSC (``transpose_pattern``); row_order /
+    col_order optional device copies of ``pattern_order`` of the two (the
+    blocks are then taken longest first).  Enqueued on the current stream
+    (or ``stream``), not synchronised.
     """
     import torch
 
@@ -307,6 +328,10 @@ def backward(q, k, v, o, lse, dout, row_ptr, col_idx, col_ptr, row_idx, block_si
     for t in (row_ptr, col_idx, col_ptr, row_idx):
         if t.dtype != torch.int32 or not t.is_cuda:
             raise ValueError("patterns must be int32 CUDA tensors")
+    for t in (row_order, col_order):
+        if t is not None and (t.dtype != torch.int32 or not t.is_cuda
+                              or t.numel() != row_ptr.numel() - 1):
+            raise ValueError("row_order / col_order must be int32 CUDA tensors of M entries")
     B, H, N, d = q.shape
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
@@ -319,7 +344,9 @@ def backward(q, k, v, o, lse, dout, row_ptr, col_idx, col_ptr, row_idx, block_si
         q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, N, d,
         int(block_size), _dtype_code(q), row_ptr.data_ptr(), col_idx.data_ptr(),
-        col_ptr.data_ptr(), row_idx.data_ptr(), int(col_idx.numel()),
+        col_ptr.data_ptr(), row_idx.data_ptr(),
+        None if row_order is None else row_order.data_ptr(),
+        None if col_order is None else col_order.data_ptr(), int(col_idx.numel()),
         0.0 if scale is None else float(scale), FORWARD_CAUSAL if causal else 0,
         stream.cuda_stream)
     if st != BSA_OK:

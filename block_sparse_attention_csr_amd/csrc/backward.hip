@@ -19,6 +19,11 @@
 //    dP = dO V^T keep one key per lane; dV^T += dO^T P and dK^T += Q^T dS read
 //    dO and Q transposed from LDS.
 // Each output element is written once; no atomics.
+//
+// Work per block is uneven (the log-linear anchors' columns, and dense rows
+// of banded masks, hold every block), so with an order array the blocks of
+// each XCD's heads are taken longest first (largest processing time first):
+// a long block then never starts near the end of the grid.
 
 #include <hip/hip_runtime.h>
 
@@ -48,12 +53,33 @@ struct BwdParams {
   const int32_t* col_idx;
   const int32_t* col_ptr;
   const int32_t* row_idx;
+  const int32_t* row_order;  // query blocks, most entries first (or NULL: ascending)
+  const int32_t* col_order;  // key blocks, most entries first (or NULL: ascending)
   int32_t M;
   int32_t N;
   int32_t num_wg;  // batch * heads * M
   float scale;
   float scale_log2;
 };
+
+// (batch*head, block) of a workgroup.  Workgroup ids run XCD by XCD (each XCD
+// one contiguous range, so one head's blocks share an L2); within the range
+// of HX heads, rank k of `order` for every head, then rank k + 1.
+__device__ __forceinline__ void block_of(int wg, int M, int num_wg, const int32_t* order,
+                                         int& bh, int& blk) {
+  if (order == nullptr) {
+    blk = wg % M;
+    bh = wg / M;
+    return;
+  }
+  const int bhs = num_wg / M;
+  const int hx = (bhs + kNumXcd - 1) / kNumXcd;
+  const int gidx = wg / (hx * M);
+  const int r = wg % (hx * M);
+  const int nh = bhs - gidx * hx < hx ? bhs - gidx * hx : hx;
+  bh = gidx * hx + r % nh;
+  blk = order[r / nh];
+}
 
 // Ring depth and copy split of a backward kernel whose stage holds two tiles
 // of BS rows (plus `extra` bytes).
@@ -132,9 +158,8 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 0>::W)) void bsa_bwd_dq(B
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = uniform(threadIdx.x / kWave);  // 32-row query group
   const int M = p.M;
-  const int wg = xcd_remap(blockIdx.x, p.num_wg);
-  const int qb = wg % M;
-  const int bh = wg / M;
+  int bh, qb;
+  block_of(xcd_remap(blockIdx.x, p.num_wg), M, p.num_wg, p.row_order, bh, qb);
   const size_t head = (size_t)bh * p.N * D;
   const T* K = static_cast<const T*>(p.k) + head;
   const T* V = static_cast<const T*>(p.v) + head;
@@ -277,9 +302,8 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 8 * BS>::W)) void bsa_bwd
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = uniform(threadIdx.x / kWave);  // 32-key group
   const int M = p.M;
-  const int wg = xcd_remap(blockIdx.x, p.num_wg);
-  const int kb = wg % M;
-  const int bh = wg / M;
+  int bh, kb;
+  block_of(xcd_remap(blockIdx.x, p.num_wg), M, p.num_wg, p.col_order, bh, kb);
   const size_t head = (size_t)bh * p.N * D;
   const T* Qh = static_cast<const T*>(p.q) + head;
   const T* dOh = static_cast<const T*>(p.dout) + head;
@@ -468,8 +492,9 @@ extern "C" bsa_status bsa_backward(const void* q, const void* k, const void* v, 
                                    void* dv, float* delta, int32_t batch, int32_t heads,
                                    int32_t seq_len, int32_t head_dim, int32_t block_size,
                                    int32_t dtype, const int32_t* row_ptr, const int32_t* col_idx,
-                                   const int32_t* col_ptr, const int32_t* row_idx, int64_t nnz,
-                                   float scale, int32_t flags, void* stream) {
+                                   const int32_t* col_ptr, const int32_t* row_idx,
+                                   const int32_t* row_order, const int32_t* col_order,
+                                   int64_t nnz, float scale, int32_t flags, void* stream) {
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr ||
       dout == nullptr || dq == nullptr || dk == nullptr || dv == nullptr || delta == nullptr ||
       row_ptr == nullptr || col_idx == nullptr || col_ptr == nullptr || row_idx == nullptr)
@@ -507,6 +532,8 @@ extern "C" bsa_status bsa_backward(const void* q, const void* k, const void* v, 
   p.col_idx = col_idx;
   p.col_ptr = col_ptr;
   p.row_idx = row_idx;
+  p.row_order = row_order;
+  p.col_order = col_order;
   p.M = static_cast<int32_t>(M);
   p.N = seq_len;
   p.num_wg = static_cast<int32_t>(num_wg);

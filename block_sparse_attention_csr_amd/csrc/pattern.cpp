@@ -221,6 +221,21 @@ extern "C" bsa_status bsa_transpose_pattern(int32_t M, const int32_t* row_ptr,
   return BSA_OK;
 }
 
+extern "C" bsa_status bsa_pattern_order(int32_t M, const int32_t* ptr, int32_t* order) {
+  if (ptr == nullptr || order == nullptr) return BSA_ERR_NULL_POINTER;
+  if (M <= 0 || ptr[0] != 0) return BSA_ERR_SHAPE;
+  for (int32_t i = 0; i < M; ++i)
+    if (ptr[i + 1] < ptr[i]) return BSA_ERR_SHAPE;
+  std::vector<int32_t> idx(static_cast<size_t>(M));
+  for (int32_t i = 0; i < M; ++i) idx[i] = i;
+  // Longest first; equal lengths keep ascending block order.
+  std::stable_sort(idx.begin(), idx.end(), [ptr](int32_t a, int32_t b) {
+    return ptr[a + 1] - ptr[a] > ptr[b + 1] - ptr[b];
+  });
+  for (int32_t k = 0; k < M; ++k) order[k] = idx[k];
+  return BSA_OK;
+}
+
 extern "C" const char* bsa_status_string(int32_t status) {
   switch (status) {
     case BSA_OK: return "BSA_OK";

@@ -234,6 +234,12 @@ bsa_status bsa_transpose_pattern(int32_t M, const int32_t* row_ptr, const int32_
  *          (receives D).
  * row_ptr, col_idx  device copies of the forward's CSR pattern;
  * col_ptr, row_idx  device copies of its bsa_transpose_pattern.
+ * row_order, col_order  device int32[M] or NULL: bsa_pattern_order of the
+ *          CSR (row_ptr) and of the CSC (col_ptr).  With them each kernel
+ *          takes its blocks longest first (the anchors' columns and dense
+ *          rows hold every block; started last they would run alone at the
+ *          end); NULL takes blocks in ascending order.  The result is the
+ *          same either way.
  * nnz      the pattern's entry count (host).
  * scale    as for bsa_forward (<= 0: 1 / sqrt(head_dim)).
  * flags    0 or BSA_FORWARD_CAUSAL (the forward's causal masking).
@@ -249,8 +255,24 @@ bsa_status bsa_backward(const void* q, const void* k, const void* v, const void*
                         float* delta, int32_t batch, int32_t heads, int32_t seq_len,
                         int32_t head_dim, int32_t block_size, int32_t dtype,
                         const int32_t* row_ptr, const int32_t* col_idx, const int32_t* col_ptr,
-                        const int32_t* row_idx, int64_t nnz, float scale, int32_t flags,
+                        const int32_t* row_idx, const int32_t* row_order,
+                        const int32_t* col_order, int64_t nnz, float scale, int32_t flags,
                         void* stream);
+
+/*
+ * bsa_pattern_order -- the blocks of a CSR (or CSC) pattern, most entries
+ * first: order[0 .. M) is a permutation of 0 .. M-1 sorted by descending
+ * ptr[i + 1] - ptr[i], equal counts in ascending i.  The work-ordering input
+ * of bsa_backward (longest processing time first).
+ *
+ * M      blocks (> 0).
+ * ptr    host int32[M + 1]: row_ptr of bsa_build_pattern or col_ptr of
+ *        bsa_transpose_pattern (non-decreasing from 0).
+ * order  host, caller-owned int32[M]; written.
+ * Errors: BSA_ERR_NULL_POINTER, BSA_ERR_SHAPE (M <= 0, ptr[0] != 0, ptr
+ * decreasing).  Host only, synchronous.
+ */
+bsa_status bsa_pattern_order(int32_t M, const int32_t* ptr, int32_t* order);
 
 /*
  * bsa_decode -- one new token per sequence against a block-aligned KV cache.
@@ -342,7 +364,7 @@ bsa_status bsa_decode_int8kv(const void* q, const int8_t* k_codes, const float* 
 const char* bsa_status_string(int32_t status);
 
 /* ABI version of this header: bump on any incompatible change. */
-#define BSA_ABI_VERSION 2
+#define BSA_ABI_VERSION 3
 int32_t bsa_abi_version(void);
 
 #ifdef __cplusplus

@@ -55,15 +55,22 @@ def _mask(kind, M, seed):
 
 
 def _run(q, k, v, do, bs, user_mask, causal, scale=None):
+    """Backward with the longest-first block orders, checked to give exactly
+    the result of the ascending order (the order only schedules the work)."""
     dev = torch.device("cuda")
     N = q.shape[2]
     rp, ci = bsa.build_pattern(N, bs, mask=user_mask, causal=causal)
     cp, ri = bsa.transpose_pattern(rp, ci)
+    ro, co = bsa.pattern_order(rp), bsa.pattern_order(cp)
     q, k, v, do = (t.to(dev) for t in (q, k, v, do))
-    rp, ci, cp, ri = (t.to(dev) for t in (rp, ci, cp, ri))
+    rp, ci, cp, ri, ro, co = (t.to(dev) for t in (rp, ci, cp, ri, ro, co))
     o, lse = bsa.forward(q, k, v, rp, ci, bs, scale, causal=causal)
-    dq, dk, dv = bsa.backward(q, k, v, o, lse, do, rp, ci, cp, ri, bs, scale, causal=causal)
+    dq, dk, dv = bsa.backward(q, k, v, o, lse, do, rp, ci, cp, ri, bs, scale, causal=causal,
+                              row_order=ro, col_order=co)
+    plain = bsa.backward(q, k, v, o, lse, do, rp, ci, cp, ri, bs, scale, causal=causal)
     torch.cuda.synchronize()
+    for a, b in zip((dq, dk, dv), plain):
+        assert torch.equal(a, b)
     return dq, dk, dv
 
 

@@ -3,6 +3,8 @@
 CSR output must be bit-exact: same row_ptr, same col_idx, int32.
 """
 
+import ctypes
+
 import numpy as np
 import pytest
 
@@ -261,3 +263,33 @@ def test_transpose_pattern_errors():
         bsa.transpose_pattern(torch.tensor([0, 2, 1], dtype=torch.int32),
                               torch.tensor([0, 1], dtype=torch.int32))
     assert e.value.status == 3
+
+
+def test_pattern_order_longest_first_and_stable():
+    # worked example: the anchors' columns (0, 64, 127) hold all 128 query blocks
+    rp, ci = bsa.build_pattern(4096, 32)
+    cp, ri = bsa.transpose_pattern(rp, ci)
+    co = bsa.pattern_order(cp).numpy()
+    assert sorted(co.tolist()) == list(range(128))
+    assert co[:3].tolist() == [0, 64, 127]
+    lens = np.diff(cp.numpy())[co]
+    assert np.all(lens[:-1] >= lens[1:])
+    # equal lengths keep ascending order
+    for a, b in zip(co[:-1], co[1:]):
+        if np.diff(cp.numpy())[a] == np.diff(cp.numpy())[b]:
+            assert a < b
+    ro = bsa.pattern_order(rp).numpy()
+    rl = np.diff(rp.numpy())[ro]
+    assert np.all(rl[:-1] >= rl[1:]) and sorted(ro.tolist()) == list(range(128))
+
+
+def test_pattern_order_errors():
+    lib = bsa._load()
+    p32 = ctypes.POINTER(ctypes.c_int32)
+    ptr = np.array([0, 2, 1, 3], np.int32)
+    out = np.zeros(3, np.int32)
+    assert lib.bsa_pattern_order(3, ptr.ctypes.data_as(p32), out.ctypes.data_as(p32)) == 3
+    ptr = np.array([1, 2, 3], np.int32)
+    assert lib.bsa_pattern_order(2, ptr.ctypes.data_as(p32), out.ctypes.data_as(p32)) == 3
+    assert lib.bsa_pattern_order(0, ptr.ctypes.data_as(p32), out.ctypes.data_as(p32)) == 3
+    assert lib.bsa_pattern_order(2, None, out.ctypes.data_as(p32)) == 1
