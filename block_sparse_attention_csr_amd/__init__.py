@@ -293,8 +293,9 @@ def transpose_pattern(row_ptr, col_idx):
 
 
 def pattern_order(ptr):
-    """bsa_pattern_order: the blocks of a CSR row_ptr (or CSC col_ptr), most
-    entries first, as a CPU int32 tensor of M entries."""
+    """bsa_pattern_order: a work order for the blocks of a CSR row_ptr (or
+    CSC col_ptr) -- blocks with more than twice the mean entry count first,
+    longest first, then the rest ascending -- as a CPU int32 tensor of M."""
     import torch
 
     pt = np.ascontiguousarray(np.asarray(ptr.cpu() if hasattr(ptr, "cpu") else ptr,

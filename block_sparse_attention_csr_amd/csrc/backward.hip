@@ -21,9 +21,9 @@
 // Each output element is written once; no atomics.
 //
 // Work per block is uneven (the log-linear anchors' columns, and dense rows
-// of banded masks, hold every block), so with an order array the blocks of
-// each XCD's heads are taken longest first (largest processing time first):
-// a long block then never starts near the end of the grid.
+// of banded masks, hold every block), so with an order array the long blocks
+// of each XCD's heads are taken first (largest processing time first): a
+// long block then never starts near the end of the grid.
 
 #include <hip/hip_runtime.h>
 
@@ -63,22 +63,44 @@ struct BwdParams {
 };
 
 // (batch*head, block) of a workgroup.  Workgroup ids run XCD by XCD (each XCD
-// one contiguous range, so one head's blocks share an L2); within the range
-// of HX heads, rank k of `order` for every head, then rank k + 1.
+// one contiguous range of HX heads, so one head's blocks share an L2).  With
+// an order array (bsa_pattern_order: the long blocks -- more than twice the
+// mean entry count -- first, then the rest ascending), a range starts with
+// the long blocks of all its heads, then takes the rest head by head.
 __device__ __forceinline__ void block_of(int wg, int M, int num_wg, const int32_t* order,
-                                         int& bh, int& blk) {
+                                         const int32_t* ptr, int& bh, int& blk) {
   if (order == nullptr) {
     blk = wg % M;
     bh = wg / M;
     return;
   }
+  // Number of long blocks: the leading entries of `order` whose count exceeds
+  // twice the mean (the same test the host applies), by bisection.
+  const int64_t total = ptr[M];
+  auto is_long = [&](int k) {
+    const int b = order[k];
+    return (int64_t)(ptr[b + 1] - ptr[b]) * M > 2 * total;
+  };
+  int lo = 0, hi = M;  // is_long holds on [0, lo) and fails on [hi, M)
+  while (lo < hi) {
+    const int mid = (lo + hi) / 2;
+    if (is_long(mid)) lo = mid + 1;
+    else hi = mid;
+  }
+  const int nlong = lo;
   const int bhs = num_wg / M;
   const int hx = (bhs + kNumXcd - 1) / kNumXcd;
   const int gidx = wg / (hx * M);
   const int r = wg % (hx * M);
   const int nh = bhs - gidx * hx < hx ? bhs - gidx * hx : hx;
-  bh = gidx * hx + r % nh;
-  blk = order[r / nh];
+  if (r < nlong * nh) {  // long blocks, rank by rank over the range's heads
+    bh = gidx * hx + r % nh;
+    blk = order[r / nh];
+  } else {               // the rest, head by head
+    const int rr = r - nlong * nh;
+    bh = gidx * hx + rr / (M - nlong);
+    blk = order[nlong + rr % (M - nlong)];
+  }
 }
 
 // Ring depth and copy split of a backward kernel whose stage holds two tiles
@@ -159,7 +181,7 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 0>::W)) void bsa_bwd_dq(B
   const int wave = uniform(threadIdx.x / kWave);  // 32-row query group
   const int M = p.M;
   int bh, qb;
-  block_of(xcd_remap(blockIdx.x, p.num_wg), M, p.num_wg, p.row_order, bh, qb);
+  block_of(xcd_remap(blockIdx.x, p.num_wg), M, p.num_wg, p.row_order, p.row_ptr, bh, qb);
   const size_t head = (size_t)bh * p.N * D;
   const T* K = static_cast<const T*>(p.k) + head;
   const T* V = static_cast<const T*>(p.v) + head;
@@ -303,7 +325,7 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 8 * BS>::W)) void bsa_bwd
   const int wave = uniform(threadIdx.x / kWave);  // 32-key group
   const int M = p.M;
   int bh, kb;
-  block_of(xcd_remap(blockIdx.x, p.num_wg), M, p.num_wg, p.col_order, bh, kb);
+  block_of(xcd_remap(blockIdx.x, p.num_wg), M, p.num_wg, p.col_order, p.col_ptr, bh, kb);
   const size_t head = (size_t)bh * p.N * D;
   const T* Qh = static_cast<const T*>(p.q) + head;
   const T* dOh = static_cast<const T*>(p.dout) + head;

@@ -226,13 +226,21 @@ extern "C" bsa_status bsa_pattern_order(int32_t M, const int32_t* ptr, int32_t* 
   if (M <= 0 || ptr[0] != 0) return BSA_ERR_SHAPE;
   for (int32_t i = 0; i < M; ++i)
     if (ptr[i + 1] < ptr[i]) return BSA_ERR_SHAPE;
-  std::vector<int32_t> idx(static_cast<size_t>(M));
-  for (int32_t i = 0; i < M; ++i) idx[i] = i;
-  // Longest first; equal lengths keep ascending block order.
-  std::stable_sort(idx.begin(), idx.end(), [ptr](int32_t a, int32_t b) {
+  // Blocks with more than twice the mean count go first, longest first; the
+  // rest keep ascending order, so that neighbouring blocks (which share data)
+  // still run close together.
+  const int64_t total = ptr[M];
+  std::vector<int32_t> longer, rest;
+  for (int32_t i = 0; i < M; ++i) {
+    const int64_t n = ptr[i + 1] - ptr[i];
+    (n * M > 2 * total ? longer : rest).push_back(i);
+  }
+  std::stable_sort(longer.begin(), longer.end(), [ptr](int32_t a, int32_t b) {
     return ptr[a + 1] - ptr[a] > ptr[b + 1] - ptr[b];
   });
-  for (int32_t k = 0; k < M; ++k) order[k] = idx[k];
+  int32_t k = 0;
+  for (const int32_t i : longer) order[k++] = i;
+  for (const int32_t i : rest) order[k++] = i;
   return BSA_OK;
 }
 

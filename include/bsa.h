@@ -236,10 +236,11 @@ bsa_status bsa_transpose_pattern(int32_t M, const int32_t* row_ptr, const int32_
  * col_ptr, row_idx  device copies of its bsa_transpose_pattern.
  * row_order, col_order  device int32[M] or NULL: bsa_pattern_order of the
  *          CSR (row_ptr) and of the CSC (col_ptr).  With them each kernel
- *          takes its blocks longest first (the anchors' columns and dense
- *          rows hold every block; started last they would run alone at the
- *          end); NULL takes blocks in ascending order.  The result is the
- *          same either way.
+ *          starts its long blocks first (the anchors' columns and dense rows
+ *          hold every block; started last they would run alone at the end);
+ *          NULL takes blocks in ascending order.  The result is the same
+ *          either way.  An order must be a permutation of 0 .. M-1 (the
+ *          kernels read it as given).
  * nnz      the pattern's entry count (host).
  * scale    as for bsa_forward (<= 0: 1 / sqrt(head_dim)).
  * flags    0 or BSA_FORWARD_CAUSAL (the forward's causal masking).
@@ -260,10 +261,13 @@ bsa_status bsa_backward(const void* q, const void* k, const void* v, const void*
                         void* stream);
 
 /*
- * bsa_pattern_order -- the blocks of a CSR (or CSC) pattern, most entries
- * first: order[0 .. M) is a permutation of 0 .. M-1 sorted by descending
- * ptr[i + 1] - ptr[i], equal counts in ascending i.  The work-ordering input
- * of bsa_backward (longest processing time first).
+ * bsa_pattern_order -- a work order for the blocks of a CSR (or CSC)
+ * pattern: order[0 .. M) is a permutation of 0 .. M-1 that lists first the
+ * blocks whose entry count ptr[i + 1] - ptr[i] exceeds twice the mean
+ * (ptr[M] / M), by descending count (equal counts in ascending i), then all
+ * other blocks in ascending i.  The work-ordering input of bsa_backward: the
+ * few long blocks (anchors' columns, dense rows) start first, while the rest
+ * keep the order in which neighbours share their data.
  *
  * M      blocks (> 0).
  * ptr    host int32[M + 1]: row_ptr of bsa_build_pattern or col_ptr of

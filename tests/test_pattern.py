@@ -265,22 +265,25 @@ def test_transpose_pattern_errors():
     assert e.value.status == 3
 
 
-def test_pattern_order_longest_first_and_stable():
-    # worked example: the anchors' columns (0, 64, 127) hold all 128 query blocks
+def test_pattern_order_long_blocks_first():
+    # worked example: the anchors' columns (0, 64, 127) hold all 128 query
+    # blocks (13x the mean); every other column keeps ascending order
     rp, ci = bsa.build_pattern(4096, 32)
     cp, ri = bsa.transpose_pattern(rp, ci)
-    co = bsa.pattern_order(cp).numpy()
-    assert sorted(co.tolist()) == list(range(128))
-    assert co[:3].tolist() == [0, 64, 127]
-    lens = np.diff(cp.numpy())[co]
-    assert np.all(lens[:-1] >= lens[1:])
-    # equal lengths keep ascending order
-    for a, b in zip(co[:-1], co[1:]):
-        if np.diff(cp.numpy())[a] == np.diff(cp.numpy())[b]:
-            assert a < b
-    ro = bsa.pattern_order(rp).numpy()
-    rl = np.diff(rp.numpy())[ro]
-    assert np.all(rl[:-1] >= rl[1:]) and sorted(ro.tolist()) == list(range(128))
+    co = bsa.pattern_order(cp).numpy().tolist()
+    assert co == [0, 64, 127] + [j for j in range(128) if j not in (0, 64, 127)]
+    # log-linear rows are all within twice the mean: ascending order
+    assert bsa.pattern_order(rp).numpy().tolist() == list(range(128))
+    # counts 1, 9, 2, 30, 1, 12: mean 55/6, so only the 30 exceeds twice it
+    ptr = np.cumsum([0, 1, 9, 2, 30, 1, 12]).astype(np.int32)
+    assert bsa.pattern_order(ptr).numpy().tolist() == [3, 0, 1, 2, 4, 5]
+    # counts 1, 40, 1, 1, 40, 50, 1, 1 (twice the mean 33.75): longest first,
+    # equal counts ascending, then the rest ascending
+    ptr = np.cumsum([0, 1, 40, 1, 1, 40, 50, 1, 1]).astype(np.int32)
+    assert bsa.pattern_order(ptr).numpy().tolist() == [5, 1, 4, 0, 2, 3, 6, 7]
+    # a uniform pattern keeps ascending order
+    ptr = np.arange(0, 5 * 7, 5).astype(np.int32)
+    assert bsa.pattern_order(ptr).numpy().tolist() == list(range(6))
 
 
 def test_pattern_order_errors():
