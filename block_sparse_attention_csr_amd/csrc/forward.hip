@@ -130,11 +130,13 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
   const int M = p.M;
   const int ngroups = (M + G - 1) / G;
   const int wg = xcd_remap(blockIdx.x, p.num_wg);
-  // Groups of a head are taken from both ends inwards (0, n-1, 1, n-2, ...):
-  // the first and last query blocks are the ones a banded pattern's global
-  // rows make dense, and started last they would run alone at the end.
+  // A head's last group runs first, then groups 0, 1, 2, ...: the first and
+  // last query blocks are the ones a banded pattern's global rows make dense,
+  // and started last the last one would run alone at the end.  The rest keep
+  // their order, so neighbouring groups (which share K/V blocks) stay close
+  // in time.
   const int rank = wg % ngroups;
-  const int grp = (rank & 1) ? ngroups - 1 - rank / 2 : rank / 2;
+  const int grp = rank == 0 ? ngroups - 1 : rank - 1;
   const int bh = wg / ngroups;
   const int qb = grp * G + g;
   const bool has_rows = qb < M;
