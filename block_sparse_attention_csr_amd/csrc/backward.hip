@@ -477,9 +477,11 @@ bsa_status launch_bwd(const BwdParams& p, hipStream_t stream) {
   const dim3 grid(p.num_wg);
   const dim3 block(kWave * (BS / kQRows));
   if (list_bytes > 16 * 1024) return BSA_ERR_SHAPE;  // M > 4096 blocks: list does not fit
-  // Shapes with more than 64 KB of LDS need the per-kernel limit raised once.
-  static bool raised = false;
-  if (!raised) {
+  // Shapes with more than 64 KB of LDS need the per-kernel limit raised, once
+  // per device.
+  static std::atomic<uint64_t> raised{0};
+  uint64_t bit;
+  if (due_on_device(raised, &bit)) {
     const void* kernels[2] = {reinterpret_cast<const void*>(&bsa_bwd_dq<T, BS, D, CAUSAL>),
                               reinterpret_cast<const void*>(&bsa_bwd_dkv<T, BS, D, CAUSAL>)};
     for (const void* f : kernels) {
@@ -490,7 +492,7 @@ bsa_status launch_bwd(const BwdParams& p, hipStream_t stream) {
                               static_cast<int>(160 * 1024 - attr.sharedSizeBytes)) != hipSuccess)
         return BSA_ERR_HIP;
     }
-    raised = true;
+    mark_done(raised, bit);
   }
   hipLaunchKernelGGL((bsa_bwd_dq<T, BS, D, CAUSAL>), grid, block, list_bytes, stream, p);
   if (hipGetLastError() != hipSuccess) return BSA_ERR_HIP;

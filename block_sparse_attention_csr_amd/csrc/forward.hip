@@ -426,14 +426,15 @@ bsa_status launch_kernel(const FwdParams& p, hipStream_t stream) {
   const size_t dyn = dynamic_lds_bytes(G, p.M);
   if (dyn + static_lds_bytes<T, BS, D, G, KS>() > kMaxLds) return BSA_ERR_INVALID_ARGUMENT;
   if (dyn + static_lds_bytes<T, BS, D, G, KS>() > 64 * 1024) {
-    static bool raised = false;  // one attribute call per instantiation
-    if (!raised) {
+    static std::atomic<uint64_t> raised{0};  // per instantiation, one bit per device
+    uint64_t bit;
+    if (due_on_device(raised, &bit)) {
       if (hipFuncSetAttribute(reinterpret_cast<const void*>(&bsa_fwd_kernel<T, BS, D, G, KS, CAUSAL>),
                               hipFuncAttributeMaxDynamicSharedMemorySize,
                               static_cast<int>(kMaxLds - static_lds_bytes<T, BS, D, G, KS>())) !=
           hipSuccess)
         return BSA_ERR_HIP;
-      raised = true;
+      mark_done(raised, bit);
     }
   }
   const dim3 block(kWave * C::W);

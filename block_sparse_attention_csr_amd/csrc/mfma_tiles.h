@@ -15,6 +15,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <type_traits>
@@ -357,6 +358,20 @@ __device__ __forceinline__ void lds_dma4(const void* sbase, uint32_t voff, uint3
                : "v"(voff), "s"(uniform_ptr(sbase)),
                  "s"((uint32_t)__builtin_amdgcn_readfirstlane((int)m0))
                : "memory", "m0");
+}
+
+// Host: whether a once-per-device action (raising a kernel's dynamic LDS
+// limit, which is a per-device attribute) is still due on the current
+// device.  `done` holds one bit per device (devices past 63: always due);
+// mark_done sets it after the action succeeded.
+inline bool due_on_device(const std::atomic<uint64_t>& done, uint64_t* bit) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 64;
+  *bit = dev >= 0 && dev < 64 ? (1ull << dev) : 0;
+  return *bit == 0 || (done.load(std::memory_order_acquire) & *bit) == 0;
+}
+inline void mark_done(std::atomic<uint64_t>& done, uint64_t bit) {
+  done.fetch_or(bit, std::memory_order_acq_rel);
 }
 
 }  // namespace
