@@ -22,7 +22,7 @@ import numpy as np
 __all__ = [
     "BsaError", "build_pattern", "forward", "backward", "transpose_pattern", "status_string",
     "abi_version", "library_path", "PatternCache", "BSA_OK", "stack_head_patterns",
-    "pattern_order", "decode", "quantize_kv", "decode_int8kv",
+    "pattern_order", "decode", "quantize_kv", "decode_int8kv", "attention",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -464,6 +464,55 @@ def decode_int8kv(q, k_codes, k_scales, v_codes, v_scales, seqlens, row_ptr, col
     if st != BSA_OK:
         raise BsaError(st, "bsa_decode_int8kv")
     return out, lse
+
+
+def attention(q, k, v, row_ptr, col_idx, col_ptr, row_idx, block_size: int,
+              scale: float | None = None, *, causal: bool = False, row_order=None,
+              col_order=None):
+    """Block-sparse attention as a differentiable torch operation: ``forward``
+    on the way in, ``backward`` (with the saved O and LSE) on the way back.
+    The pattern tensors are device int32 CSR / CSC (and optional work orders,
+    see ``pattern_order``).  Returns O."""
+    return _Attention.apply(q, k, v, row_ptr, col_idx, col_ptr, row_idx, int(block_size),
+                            scale, bool(causal), row_order, col_order)
+
+
+def _make_attention_fn():
+    import torch
+
+    class _AttentionFn(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, row_ptr, col_idx, col_ptr, row_idx, block_size, scale, causal,
+                    row_order, col_order):
+            q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+            o, lse = forward(q, k, v, row_ptr, col_idx, block_size, scale, causal=causal)
+            ctx.save_for_backward(q, k, v, o, lse, row_ptr, col_idx, col_ptr, row_idx)
+            ctx.cfg = (block_size, scale, causal, row_order, col_order)
+            return o
+
+        @staticmethod
+        def backward(ctx, do):
+            q, k, v, o, lse, row_ptr, col_idx, col_ptr, row_idx = ctx.saved_tensors
+            block_size, scale, causal, row_order, col_order = ctx.cfg
+            dq, dk, dv = backward(q, k, v, o, lse, do.contiguous(), row_ptr, col_idx, col_ptr,
+                                  row_idx, block_size, scale, causal=causal,
+                                  row_order=row_order, col_order=col_order)
+            return dq, dk, dv, None, None, None, None, None, None, None, None, None
+
+    return _AttentionFn
+
+
+class _LazyAttention:
+    fn = None
+
+    @classmethod
+    def apply(cls, *args):
+        if cls.fn is None:
+            cls.fn = _make_attention_fn()
+        return cls.fn.apply(*args)
+
+
+_Attention = _LazyAttention
 
 
 class PatternCache:

@@ -133,3 +133,29 @@ def test_backward_deterministic():
     b = _run(q, k, v, do, 32, None, False)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+def test_autograd_wrapper_matches_the_oracle():
+    """bsa.attention as a torch.autograd.Function: O from the forward kernel,
+    gradients from the backward kernels, checked against the oracle."""
+    bs, d, M, B, H = 32, 64, 12, 2, 2
+    N = bs * M
+    q, k, v = make_qkv(B, H, N, d, torch.bfloat16, 41)
+    g = make_qkv(B, H, N, d, torch.bfloat16, 42)[0]
+    dev = torch.device("cuda")
+    rp, ci = bsa.build_pattern(N, bs)
+    cp, ri = bsa.transpose_pattern(rp, ci)
+    ro, co = bsa.pattern_order(rp).to(dev), bsa.pattern_order(cp).to(dev)
+    qd, kd, vd = (t.to(dev).requires_grad_(True) for t in (q, k, v))
+    o = bsa.attention(qd, kd, vd, rp.to(dev), ci.to(dev), cp.to(dev), ri.to(dev), bs,
+                      row_order=ro, col_order=co)
+    (o.float() * g.to(dev).float()).sum().backward()
+    torch.cuda.synchronize()
+    mask = oracle.block_mask_from_sets(oracle.loglinear_block_sets(N, bs))
+    o_ref, _ = oracle.block_sparse_attention(_f64(q), _f64(k), _f64(v), mask, bs)
+    assert np.abs(_f64(o.detach()) - o_ref).max() <= 2e-2
+    rq, rk, rv, _ = oracle.block_sparse_attention_backward(_f64(q), _f64(k), _f64(v), _f64(g),
+                                                           mask, bs)
+    _check("dQ autograd", qd.grad, rq, torch.bfloat16)
+    _check("dK autograd", kd.grad, rk, torch.bfloat16)
+    _check("dV autograd", vd.grad, rv, torch.bfloat16)
