@@ -159,3 +159,31 @@ def test_autograd_wrapper_matches_the_oracle():
     _check("dQ autograd", qd.grad, rq, torch.bfloat16)
     _check("dK autograd", kd.grad, rk, torch.bfloat16)
     _check("dV autograd", vd.grad, rv, torch.bfloat16)
+
+
+def test_backward_largest_block_count_invariants():
+    """M = 4096 blocks (N = 131072 at block 32, the largest the backward
+    takes): properties that hold at any size, since every softmax row sums to
+    one and every row of dS sums to zero:
+      sum over keys of dV = sum over queries of dO,
+      sum over keys of dK = 0,
+    per (batch, head) and feature; plus finite gradients everywhere."""
+    B, H, N, d, bs = 1, 2, 131072, 64, 32
+    q, k, v = make_qkv(B, H, N, d, torch.bfloat16, 8)
+    do = make_qkv(B, H, N, d, torch.bfloat16, 9)[0]
+    dq, dk, dv = _run(q, k, v, do, bs, None, False)
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t.float()).all()
+    sum_dv = dv.double().sum(dim=2)
+    sum_do = do.double().sum(dim=2).to(sum_dv.device)
+    e_dv = (sum_dv - sum_do).abs().max().item()
+    e_dk = dk.double().sum(dim=2).abs().max().item()
+    print(f"M=4096 invariants: max |sum dV - sum dO| {e_dv:.3e}, max |sum dK| {e_dk:.3e}, "
+          f"max |sum dO| {sum_do.abs().max().item():.3e}")
+    # Each gradient element carries a bf16 rounding of relative size up to
+    # 2^-8 on values of magnitude ~1, with random signs: over N terms the sum
+    # drifts by ~2^-8 sqrt(N) (1.4 here; measured 0.2).  One missing 32-row key
+    # block would move the sums by ~32.
+    tol = 2.0 ** -8 * N ** 0.5
+    assert e_dv <= tol
+    assert e_dk <= tol

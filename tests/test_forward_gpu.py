@@ -255,3 +255,25 @@ def test_every_workgroup_shape(dt, bs, d, group, key_split):
     torch.cuda.synchronize()
     o_ref, lse_ref = oracle.block_sparse_attention(_f64(q), _f64(k), _f64(v), mask, bs)
     _compare(_f64(o), _f64(lse), o_ref, lse_ref, dtype, f"{dt} bs{bs} d{d} G{group} KS{key_split}")
+
+
+@pytest.mark.parametrize("B,H", [(1, 1), (2, 2)])
+def test_longest_supported_blocks_sampled(B, H):
+    """N = 131072 at block 32: M = 4096 query blocks, the largest entry list
+    and bitmaps the kernel keeps in LDS.  B = H = 1 runs the one-block
+    workgroups, B = H = 2 the four-block ones; sampled query blocks (start,
+    anchors at M/2 and M-1, end) against the oracle."""
+    N, d, bs = 131072, 64, 32
+    M = N // bs
+    q, k, v = make_qkv(B, H, N, d, torch.bfloat16, 3)
+    o, lse, rp, ci = _run_gpu(q, k, v, bs, None)
+    mask = oracle.block_mask_from_sets(oracle.loglinear_block_sets(N, bs))
+    assert int(rp[-1]) == int(mask.sum())
+    qblocks = [0, 1, 5, M // 2 - 1, M // 2, M // 2 + 3, M - 2, M - 1]
+    for b, h in {(0, 0), (B - 1, H - 1)}:
+        o_ref, lse_ref = oracle.block_sparse_attention_head(
+            _f64(q[b, h]), _f64(k[b, h]), _f64(v[b, h]), mask, bs, query_blocks=qblocks)
+        rows = np.isfinite(lse_ref)
+        _compare(_f64(o[b, h])[rows], _f64(lse[b, h])[rows], o_ref[rows], lse_ref[rows],
+                 torch.bfloat16, f"N={N} b{b} h{h}")
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
