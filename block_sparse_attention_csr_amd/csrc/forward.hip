@@ -151,20 +151,20 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
   const int q0 = (has_rows ? qb : 0) * BS + qg * kQRows;
   O::template load_q<D>(qop, Q + (size_t)q0 * D, lane);
 
-  // ---- entry list: the workgroup's CSR row (G == 1) or the sorted union of
-  // its G rows (G > 1), in LDS; per-row bitmaps say which entries a wave uses.
+  // ---- entry list: the workgroup's CSR row (G == 1, read from col_idx) or
+  // the sorted union of its G rows (G > 1, built in LDS, with per-row bitmaps
+  // that say which entries a wave uses).
   const int MW = (M + 31) / 32;
   int32_t* list = dyn;                                        // [M]
   uint32_t* bitmap = reinterpret_cast<uint32_t*>(dyn + M);    // [(G + 1) * MW] (G > 1)
   const uint32_t* my_row = bitmap + (1 + g) * MW;
   int U;
+  int rs = 0;  // G == 1: the row's first entry in col_idx
   if constexpr (G == 1) {
-    const int rs = row_ptr[grp];
-    const int re = row_ptr[grp + 1];
-    U = re - rs;
-    if (wave == 0)
-      for (int t = lane; t < U; t += kWave) list[t] = p.col_idx[rs + t];
-    __syncthreads();
+    // Every wave reads the row from col_idx itself (64 entries at a time, in
+    // entry_at): no LDS list and no barrier before the first copy.
+    rs = row_ptr[grp];
+    U = row_ptr[grp + 1] - rs;
   } else {
     for (int i = threadIdx.x; i < (G + 1) * MW; i += blockDim.x) bitmap[i] = 0;
     __syncthreads();
@@ -220,7 +220,8 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
     if ((t & ~(kWave - 1)) != chunk_base) {
       chunk_base = t & ~(kWave - 1);
       const int idx = chunk_base + lane;
-      chunk = idx < U ? list[idx] : -1;
+      if constexpr (G == 1) chunk = idx < U ? p.col_idx[rs + idx] : -1;
+      else chunk = idx < U ? list[idx] : -1;
       bool sel = chunk >= 0 && chunk < M && has_rows && (!causal || chunk <= qb);
       if constexpr (G > 1)
         sel = sel && ((my_row[chunk >> 5] >> (chunk & 31)) & 1u) != 0;
@@ -405,9 +406,10 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
   }
 }
 
-// Dynamic LDS: entry list (M ints) and, for G > 1, G + 1 bitmaps.
+// Dynamic LDS (G > 1): the union's entry list (M ints) and G + 1 bitmaps.
 size_t dynamic_lds_bytes(int group, int M) {
-  const size_t words = group > 1 ? (size_t)(group + 1) * ((M + 31) / 32) : 0;
+  if (group == 1) return 0;  // the row is read from col_idx directly
+  const size_t words = (size_t)(group + 1) * ((M + 31) / 32);
   return 4 * ((size_t)M + words);
 }
 
