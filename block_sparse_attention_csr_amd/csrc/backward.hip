@@ -139,20 +139,6 @@ __device__ __forceinline__ float operand_dot(const typename Ops<T>::template QOp
   return s;
 }
 
-// Stores a 32-row x D accumulator X^T (lane = row, registers = features) as
-// rows of `dst` scaled by `mul`.
-template <typename T, int D>
-__device__ __forceinline__ void store_rows(T* dst_row, const f32x16_t (&x)[D / 32], float mul,
-                                           int lane) {
-  const int h = lane >> 5;
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-    for (int gg = 0; gg < 4; ++gg)
-      Ops<T>::store_o4(dst_row + dt * 32 + 8 * gg + 4 * h, x[dt][4 * gg] * mul,
-                       x[dt][4 * gg + 1] * mul, x[dt][4 * gg + 2] * mul, x[dt][4 * gg + 3] * mul);
-}
-
 // Copies a CSR row / CSC column into the LDS entry list (wave 0) and returns
 // its length; the caller synchronises.
 __device__ __forceinline__ int load_list(int32_t* list, const int32_t* idx, int start, int end,
@@ -302,7 +288,10 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 0>::W)) void bsa_bwd_dq(B
       if (i + 2 < U) step(i + 2, std::integral_constant<int, 2>{});
   }
 
-  store_rows<T, D>(static_cast<T*>(p.dq) + head + (size_t)row * D, dq, p.scale, lane);
+  // dQ leaves through this wave's part of the idle ring (whole 16-byte stores).
+  __syncthreads();  // every wave is done with the ring; no copy is in flight
+  store_rows_lds<T, D>(static_cast<T*>(p.dq) + head + (size_t)q0 * D, dq, p.scale, lane,
+                       (LDS_PTR(unsigned char))buf0 + wave * (kQRows * D * (int)sizeof(T)));
 }
 
 // ---------------------------------------------------------------- dK, dV
@@ -464,9 +453,12 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 8 * BS>::W)) void bsa_bwd
       if (i + 2 < U) step(i + 2, std::integral_constant<int, 2>{});
   }
 
-  const int key = k0 + (lane & 31);
-  store_rows<T, D>(static_cast<T*>(p.dk) + head + (size_t)key * D, dk, p.scale, lane);
-  store_rows<T, D>(static_cast<T*>(p.dv) + head + (size_t)key * D, dv, 1.0f, lane);
+  // dK then dV leave through this wave's part of the idle ring.
+  __syncthreads();  // every wave is done with the ring; no copy is in flight
+  LDS_PTR(unsigned char) region =
+      (LDS_PTR(unsigned char))buf0 + wave * (kQRows * D * (int)sizeof(T));
+  store_rows_lds<T, D>(static_cast<T*>(p.dk) + head + (size_t)k0 * D, dk, p.scale, lane, region);
+  store_rows_lds<T, D>(static_cast<T*>(p.dv) + head + (size_t)k0 * D, dv, 1.0f, lane, region);
 }
 
 // ---------------------------------------------------------------- host

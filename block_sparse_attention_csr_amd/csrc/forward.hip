@@ -395,7 +395,6 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
   // LDS region (the ring is idle now), so that the global stores are whole
   // 16-byte chunks of consecutive rows.
   constexpr int kRowB = D * (int)sizeof(T);      // bytes per output row
-  constexpr int kCpr = kRowB / 16;                // 16-byte chunks per row
   constexpr int kStage = kQRows * kRowB;          // a wave's 32 rows
   constexpr int kPerBuf = C::kSliceBytes / kStage;
   constexpr int kStoreWaves = KS > 1 ? SW : C::W;
@@ -409,33 +408,8 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
   if constexpr (kStaged) {
     const int wv = KS > 1 ? ws : wave;  // index among the storing waves
     unsigned char* region = (NB == 3 && wv >= kPerBuf ? buf2 : buf1) + (wv % kPerBuf) * kStage;
-    LDS_PTR(unsigned char) st = (LDS_PTR(unsigned char))region;
-    const int r = lane & 31;
-    auto swz = [](int rr) { return rr & 7; };  // 16-byte chunk XOR key: spreads a column over 8 bank groups
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int gg = 0; gg < 4; ++gg) {
-        const int byte = (32 * dt + 8 * gg + 4 * h) * (int)sizeof(T);
-        const int c = byte / 16;
-        LDS_PTR(unsigned char) dst = st + r * kRowB + ((c ^ swz(r)) << 4) + (byte & 15);
-        const float a0 = o[dt][4 * gg] * inv, a1 = o[dt][4 * gg + 1] * inv;
-        const float a2 = o[dt][4 * gg + 2] * inv, a3 = o[dt][4 * gg + 3] * inv;
-        if constexpr (std::is_same<T, __bf16>::value) {
-          *(LDS_PTR(u32x2_t))dst = u32x2_t{pack_bf16x2(a0, a1), pack_bf16x2(a2, a3)};
-        } else {
-          *(LDS_PTR(f32x4_t))dst = f32x4_t{a0, a1, a2, a3};
-        }
-      }
-    T* Out0 = static_cast<T*>(p.o) + head + (size_t)q0 * D;
-#pragma unroll
-    for (int i = 0; i < kQRows * kCpr / kWave; ++i) {
-      const int k = lane + kWave * i;
-      const int rr = k / kCpr, c = k % kCpr;
-      const u32x4_t v = *(LDS_PTR(const u32x4_t))(st + rr * kRowB + ((c ^ swz(rr)) << 4));
-      *reinterpret_cast<u32x4_t*>(reinterpret_cast<unsigned char*>(Out0) + (size_t)rr * kRowB +
-                                  c * 16) = v;
-    }
+    store_rows_lds<T, D>(static_cast<T*>(p.o) + head + (size_t)q0 * D, o, inv, lane,
+                         (LDS_PTR(unsigned char))region);
   } else {
     T* Out = static_cast<T*>(p.o) + head + (size_t)row * D;
 #pragma unroll

@@ -309,6 +309,43 @@ struct Ops<float> {
   }
 };
 
+// Stores a wave's 32 rows x D of an accumulator in the O^T layout (lane =
+// row, register 4 g + e of tile dt = element 32 dt + 8 g + 4 h + e), scaled
+// by `mul` and rounded to T, through the wave's LDS region `st` (32 D
+// sizeof(T) bytes): written row-major with 16-byte chunks XOR-swizzled by row
+// (8 bank groups), read back as 16-byte chunks of consecutive rows and
+// stored to rows dst0 + r D.  Each lane then issues whole 16-byte stores
+// instead of 8-byte pieces.
+template <typename T, int D>
+__device__ __forceinline__ void store_rows_lds(T* dst0, const f32x16_t (&x)[D / 32], float mul,
+                                               int lane, LDS_PTR(unsigned char) st) {
+  constexpr int kRowB = D * (int)sizeof(T);
+  constexpr int kCpr = kRowB / 16;
+  const int h = lane >> 5;
+  const int r = lane & 31;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int byte = (32 * dt + 8 * g + 4 * h) * (int)sizeof(T);
+      LDS_PTR(unsigned char) dst = st + r * kRowB + (((byte >> 4) ^ (r & 7)) << 4) + (byte & 15);
+      const float a0 = x[dt][4 * g] * mul, a1 = x[dt][4 * g + 1] * mul;
+      const float a2 = x[dt][4 * g + 2] * mul, a3 = x[dt][4 * g + 3] * mul;
+      if constexpr (std::is_same<T, __bf16>::value)
+        *(LDS_PTR(u32x2_t))dst = u32x2_t{pack_bf16x2(a0, a1), pack_bf16x2(a2, a3)};
+      else
+        *(LDS_PTR(f32x4_t))dst = f32x4_t{a0, a1, a2, a3};
+    }
+#pragma unroll
+  for (int i = 0; i < 32 * kCpr / kWave; ++i) {
+    const int k = lane + kWave * i;
+    const int rr = k / kCpr, c = k % kCpr;
+    const u32x4_t v = *(LDS_PTR(const u32x4_t))(st + rr * kRowB + ((c ^ (rr & 7)) << 4));
+    *reinterpret_cast<u32x4_t*>(reinterpret_cast<unsigned char*>(dst0) + (size_t)rr * kRowB +
+                                c * 16) = v;
+  }
+}
+
 // s_waitcnt: vector-memory count <= n and LDS/scalar count == 0.
 template <int n>
 __device__ __forceinline__ void wait_vm_lgkm0() {
