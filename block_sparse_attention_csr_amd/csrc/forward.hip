@@ -153,7 +153,29 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
 
   typename O::template QOperand<D> qop;
   const int q0 = (has_rows ? qb : 0) * BS + qg * kQRows;
-  O::template load_q<D>(qop, Q + (size_t)q0 * D, lane);
+  // bf16, one query block per workgroup: the wave's 32 Q rows come in as
+  // whole 1 KB runs (direct-to-LDS, swizzled like the K/V tiles) into its part
+  // of the ring's last buffer, which no K/V copy touches before the first
+  // step's barrier; the operand is read from there once they land.  (The
+  // operand layout read straight from memory takes 16 bytes from each of 32
+  // rows per load: it cost 5% of the latency-bound small-grid forward.)
+  using QL = TileLayout<T, kQRows, D>;
+  constexpr bool kStageQ = G == 1 && std::is_same<T, __bf16>::value &&
+                           C::W * QL::kTileBytes <= C::kSliceBytes;
+  unsigned char* const q_stage = (NB == 3 ? buf2 : buf1) + (ks * QW + qg) * QL::kTileBytes;
+  if constexpr (kStageQ) {
+    const uint32_t dst = (uint32_t)(uintptr_t)(LDS_PTR(unsigned char))q_stage;
+#pragma unroll
+    for (int part = 0; part < QL::kTileBytes / (kWave * 16); ++part) {
+      const int slot = part * kWave + lane;
+      const int row = slot / QL::kChunksPerRow;
+      const int chunk = (slot % QL::kChunksPerRow) ^ QL::swz(row);
+      lds_dma16(Q + (size_t)q0 * D, (uint32_t)(row * QL::kRowBytes + chunk * 16),
+                dst + part * kWave * 16);
+    }
+  } else {
+    O::template load_q<D>(qop, Q + (size_t)q0 * D, lane);
+  }
 
   // ---- entry list: the workgroup's CSR row (G == 1, read from col_idx) or
   // the sorted union of its G rows (G > 1, built in LDS, with per-row bitmaps
@@ -326,6 +348,12 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
   // copy, tells the compiler they are complete (it does not see the copies
   // and would otherwise wait on the vector-memory counter inside the loop).
   wait_vm_lgkm0<0>();
+  if constexpr (kStageQ) {  // lane (query r, half h) takes chunks 2c + h of row r
+    LDS_PTR(const unsigned char) qs = (LDS_PTR(const unsigned char))q_stage;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+      qop.r[c] = *(LDS_PTR(const u32x4_t))(qs + QL::chunk_offset(lane & 31, 2 * c + (lane >> 5)));
+  }
   issue(jq[0], buf0);
   if (NB == 3) issue(jq[1], buf1);
   auto buffer = [&](auto b_c) -> unsigned char* {
