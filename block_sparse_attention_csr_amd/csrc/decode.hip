@@ -20,7 +20,17 @@
 //  * Units are dealt round-robin to the waves; each wave loads its next unit
 //    while it computes the current one, with an exact online softmax.
 //  * A score is the chunk's partial dot product summed over the LPK lanes of
-//    its key (ds_swizzle butterflies); the unit max over the key groups.
+//    its key; the unit max over the key groups.  The cross-lane steps are
+//    VALU lane moves (DPP within rows of 16 lanes, permlane swaps across
+//    rows), with no LDS round trip in the loop.
+//  * bf16 cache and query: the dot products run two elements per
+//    instruction (v_dot2 on bf16 pairs); P V pairs two keys per element,
+//    with P rounded to bf16 as the MFMA forward rounds it.  float32 data
+//    keeps one fused multiply-add per element.
+//  * Keys after the token only occur in the unit that holds it; there the
+//    V chunks of those keys are zeroed (the cache beyond L_b may hold
+//    anything, NaN included) and their scores set to -inf, so the other
+//    units carry no per-element selection.
 //  * At the end each wave sums its O over the key groups and the W waves
 //    merge (O, m, l) through LDS.
 //
@@ -30,7 +40,12 @@
 // taken off once per sum (q's chunk sum for the scores, the weight sum for
 // O); a unit lies in one block, so its K scale multiplies the unit's scores
 // and its V scale the unit's weights (the exponential sum uses the unscaled
-// weights).  The same file holds the quantiser that writes such a
+// weights).  With a bf16 query and d = 128, the int8 products also run two
+// per instruction: q is scaled by a power of two (exactly) into float16
+// range, and byte permutes turn two biased codes into the f16 values
+// 1024 + code + 128, exact (for the scores two elements of one key, for P V
+// one element of two keys, against the two weights in f16); the 1152 offset
+// is taken off once per chunk, or once at the end for O.  The same file holds the quantiser that writes such a
 // cache: per (batch, head, block), scale = max|x| / 127 and
 // code = rint(x / scale) clamped to [-127, 127], both in float32.
 
@@ -76,34 +91,70 @@ struct DecCfg {
   static_assert(LPK <= 32 && SUB >= 1 && BS % KU == 0, "decode unit shape");
 };
 
-// Lane value combined with lane ^ mask, for mask < 32 (no LDS memory is used).
-template <int mask>
-__device__ __forceinline__ float xor_lane(float x) {
-  static_assert(mask > 0 && mask < 32, "swizzle mask");
-  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), (mask << 10) | 0x1F));
+// A lane's value moved by a DPP pattern within each row of 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;  // lane i of 8 <- lane 7 - i
+constexpr int kDppMirror = 0x140;      // lane i of 16 <- lane 15 - i
+template <int R>
+constexpr int dpp_ror() {  // lane i of 16 <- lane (i + R) mod 16
+  return 0x120 + R;
 }
 
-// Sum (or max) over the lanes lane ^ m, m = FROM, 2 FROM, ... < TO (powers of
-// two): the lane groups that differ only in those bits.
-template <int FROM, int TO>
-__device__ __forceinline__ float lanes_sum(float x) {
-  if constexpr (FROM >= TO) {
-    return x;
-  } else if constexpr (FROM < 32) {
-    return lanes_sum<FROM * 2, TO>(x + xor_lane<FROM>(x));
-  } else {
-    return halves_sum(x);
-  }
+// Sum (or max) of a lane's value with the lane 16 apart within its half of
+// the wave (one v_permlane16_swap).
+__device__ __forceinline__ float sum_rows16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-template <int FROM, int TO>
-__device__ __forceinline__ float lanes_max(float x) {
-  if constexpr (FROM >= TO) {
-    return x;
-  } else if constexpr (FROM < 32) {
-    return lanes_max<FROM * 2, TO>(__builtin_elementwise_maximum(x, xor_lane<FROM>(x)));
-  } else {
-    return halves_max(x);
-  }
+__device__ __forceinline__ float max_rows16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Sum (or max) over each aligned group of N lanes (N a power of two, 1 ..
+// 64); every lane of the group receives it.  Steps below FROM are skipped:
+// the value must then already be equal across each aligned group of FROM
+// lanes.  Steps 4 and 8 pair the two halves of a group by mirroring, which
+// needs exactly that equality (it holds after the steps before them).
+template <int FROM, int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (FROM <= 1 && N >= 2) x += dpp_move<kDppXor1>(x);
+  if constexpr (FROM <= 2 && N >= 4) x += dpp_move<kDppXor2>(x);
+  if constexpr (FROM <= 4 && N >= 8) x += dpp_move<kDppHalfMirror>(x);
+  if constexpr (FROM <= 8 && N >= 16) x += dpp_move<kDppMirror>(x);
+  if constexpr (FROM <= 16 && N >= 32) x = sum_rows16(x);
+  if constexpr (N >= 64) x = halves_sum(x);
+  return x;
+}
+template <int FROM, int N>
+__device__ __forceinline__ float group_max(float x) {
+  if constexpr (FROM <= 1 && N >= 2) x = __builtin_elementwise_maximum(x, dpp_move<kDppXor1>(x));
+  if constexpr (FROM <= 2 && N >= 4) x = __builtin_elementwise_maximum(x, dpp_move<kDppXor2>(x));
+  if constexpr (FROM <= 4 && N >= 8)
+    x = __builtin_elementwise_maximum(x, dpp_move<kDppHalfMirror>(x));
+  if constexpr (FROM <= 8 && N >= 16) x = __builtin_elementwise_maximum(x, dpp_move<kDppMirror>(x));
+  if constexpr (FROM <= 16 && N >= 32) x = max_rows16(x);
+  if constexpr (N >= 64) x = halves_max(x);
+  return x;
+}
+
+// Sum over the lanes with the same lane % S (S a power of two, 1 .. 32): the
+// 64 / S lanes of one residue class, each receiving it.  Any values.
+template <int S>
+__device__ __forceinline__ float stride_sum(float x) {
+  if constexpr (S <= 1) x += dpp_move<kDppXor1>(x);
+  if constexpr (S <= 2) x += dpp_move<dpp_ror<2>()>(x);
+  if constexpr (S <= 4) x += dpp_move<dpp_ror<4>()>(x);
+  if constexpr (S <= 8) x += dpp_move<dpp_ror<8>()>(x);
+  if constexpr (S <= 16) x = sum_rows16(x);
+  return halves_sum(x);
 }
 
 // The elements of a 16-byte chunk as floats (exact for every type).
@@ -137,6 +188,25 @@ __device__ __forceinline__ void codes_to_float_biased(const u32x4_t& c, float* f
   }
 }
 
+// Two biased int8 codes (bytes B0 and B0 + 1 of u, each code + 128) as the
+// f16 pair (1024 + byte, 1024 + byte), exact: each byte under an 0x64
+// exponent byte.
+template <int B0>
+__device__ __forceinline__ uint32_t biased_pair_f16(uint32_t u) {
+  constexpr uint32_t sel = 0x04000400u | ((uint32_t)(B0 + 1) << 16) | (uint32_t)B0;
+  return __builtin_amdgcn_perm(0x64646464u, u, sel);
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c,
+                                false);
+}
+
 template <typename T>
 __device__ __forceinline__ void store_elem(T* dst, float x) {
   if constexpr (std::is_same<T, __bf16>::value) *dst = (__bf16)x;  // round to nearest even
@@ -156,6 +226,11 @@ template <typename T, typename TC, int BS, int D>
 __global__ __launch_bounds__(kWave * kDecodeWaves) void bsa_decode_kernel(DecParams p) {
   using C = DecCfg<TC, BS, D>;
   constexpr bool kInt8 = std::is_same<TC, int8_t>::value;
+  constexpr bool kBf16Q = std::is_same<T, __bf16>::value;
+  constexpr bool kDotBf16 = kBf16Q && std::is_same<TC, __bf16>::value;  // dot2 on bf16 pairs
+  // dot2 on f16 pairs: at d = 128 (at d = 64 a sequence's units are too few
+  // for it to repay the query's conversion, which lies on their critical path)
+  constexpr bool kDotF16 = kBf16Q && kInt8 && D == 128;
   constexpr int W = kDecodeWaves;
   constexpr int E = C::E;
   constexpr int LPK = C::LPK;
@@ -185,10 +260,35 @@ __global__ __launch_bounds__(kWave * kDecodeWaves) void bsa_decode_kernel(DecPar
   const TC* K = static_cast<const TC*>(p.k) + head;
   const TC* V = static_cast<const TC*>(p.v) + head;
 
+  // The lane's q elements: as floats (float32 data), as the raw bf16 pairs
+  // (bf16 cache), or scaled by 2^-qexp into f16 pairs (int8 cache, bf16 q).
   float qf[E];
   load_floats<T, E>(static_cast<const T*>(p.q) + (size_t)bh * D + chunk * E, qf);
-  float qsum = 0.f;  // int8: sum of the lane's q elements (for the code offset)
-  if constexpr (kInt8) {
+  uint32_t qw[E / 2];
+  float qsum = 0.f;    // int8: sum of the lane's q elements (for the code offset)
+  float qmul = 1.f;    // int8 with f16 q: 2^qexp, the scores' factor
+  if constexpr (kDotBf16) {
+#pragma unroll
+    for (int w = 0; w < E / 2; ++w) qw[w] = pack_bf16x2(qf[2 * w], qf[2 * w + 1]);  // exact
+  } else if constexpr (kDotF16) {
+    // max|q| over the whole row (the LPK lanes of a key group hold all of it)
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(qf[e]));
+    amax = group_max<1, LPK>(amax);
+    // scale so that max|q| lands in [2^14, 2^15): every bf16 element then
+    // converts to f16 exactly (bar those below 2^-28 max|q|, which the
+    // float32 sum cannot see either)
+    const int qexp = (amax > 0.f && amax < INFINITY) ? ilogbf(amax) - 14 : 0;
+    qmul = ldexpf(1.f, qexp);
+#pragma unroll
+    for (int w = 0; w < E / 2; ++w) {
+      const auto h2 = __builtin_amdgcn_cvt_pkrtz(ldexpf(qf[2 * w], -qexp),
+                                                    ldexpf(qf[2 * w + 1], -qexp));
+      qw[w] = __builtin_bit_cast(uint32_t, h2);
+      qsum += (float)h2[0] + (float)h2[1];
+    }
+  } else if constexpr (kInt8) {
 #pragma unroll
     for (int e = 0; e < E; ++e) qsum += qf[e];
   }
@@ -244,42 +344,44 @@ __global__ __launch_bounds__(kWave * kDecodeWaves) void bsa_decode_kernel(DecPar
   for (int e = 0; e < E; ++e) o[e] = 0.f;
   float pvsum = 0.f;  // int8: sum of the lane's V weights (for the code offset)
 
-  int key_cur = -1;
-  int s = next_slot(wave, key_cur);
-  u32x4_t kr[C::NI], vr[C::NI];
-  f32x2_t sc_cur = {1.f, 1.f};
-  if (s < nslots) load(key_cur, kr, vr, sc_cur);
-  while (s < nslots) {
-    // the next unit's loads go out before this unit's arithmetic
-    int key_next = -1;
-    const int sn = next_slot(s + W, key_next);
-    u32x4_t kn[C::NI], vn[C::NI];
-    f32x2_t sc_next = {1.f, 1.f};
-    if (sn < nslots) load(key_next, kn, vn, sc_next);
-
-    // scores of the lane's keys key_cur + KPI n + kq (scaled, log2 domain)
+  // One unit: its keys' scores, the online-softmax update, and P V.
+  auto unit = [&](int key0, u32x4_t (&kr)[C::NI], u32x4_t (&vr)[C::NI], const f32x2_t& scv) {
+    // scores of the lane's keys key0 + KPI n + kq (scaled, log2 domain)
     // int8: the unit's block scales (the scores' and the weights' factors)
-    const float ks = sc_cur[0] * c2;
-    const float vs = sc_cur[1];
+    const float ks = scv[0] * c2 * qmul;
+    const float vs = scv[1];
     float sc[C::NI];
     float mx = -INFINITY;
 #pragma unroll
     for (int n = 0; n < C::NI; ++n) {
-      float kf[E];
       float d = 0.f;
-      if constexpr (kInt8) {
-        codes_to_float_biased(kr[n], kf);  // code + 128
-        d = -128.f * qsum;
-      } else {
-        chunk_to_float<TC>(kr[n], kf);
-      }
+      if constexpr (kDotBf16) {
 #pragma unroll
-      for (int e = 0; e < E; ++e) d = fmaf(qf[e], kf[e], d);
-      d = lanes_sum<1, LPK>(d) * ks;
-      sc[n] = key_cur + n * KPI + kq <= t ? d : -INFINITY;
+        for (int w = 0; w < 4; ++w) d = dot2_bf16(kr[n][w], qw[w], d);
+      } else if constexpr (kDotF16) {
+        d = -1152.f * qsum;  // the pairs carry code + 1152
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t u = kr[n][w] ^ 0x80808080u;  // code + 128 per byte
+          d = dot2_f16(biased_pair_f16<0>(u), qw[2 * w], d);
+          d = dot2_f16(biased_pair_f16<2>(u), qw[2 * w + 1], d);
+        }
+      } else {
+        float kf[E];
+        if constexpr (kInt8) {
+          codes_to_float_biased(kr[n], kf);  // code + 128
+          d = -128.f * qsum;
+        } else {
+          chunk_to_float<TC>(kr[n], kf);
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) d = fmaf(qf[e], kf[e], d);
+      }
+      d = group_sum<1, LPK>(d) * ks;
+      sc[n] = key0 + n * KPI + kq <= t ? d : -INFINITY;
       mx = __builtin_elementwise_maximum(mx, sc[n]);
     }
-    mx = lanes_max<LPK, kWave>(mx);  // finite: the unit's first key is visible
+    mx = group_max<LPK, kWave>(mx);  // finite: the unit's first key is visible
     const float m_new = fmaxf(m2, mx);
     const float alpha = fast_exp2(m2 - m_new);  // 0 on the first unit (m2 = -inf)
     m2 = m_new;
@@ -287,43 +389,110 @@ __global__ __launch_bounds__(kWave * kDecodeWaves) void bsa_decode_kernel(DecPar
     pvsum *= alpha;
 #pragma unroll
     for (int e = 0; e < E; ++e) o[e] *= alpha;
+    // The unit that holds the token: the V chunks of the keys after it are
+    // zeroed (their weights are 0 already), so that no value there, NaN
+    // included, reaches O.
+    if (key0 + C::KU - 1 > t) {
+#pragma unroll
+      for (int n = 0; n < C::NI; ++n) {
+        const bool visible = key0 + n * KPI + kq <= t;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) vr[n][w] = visible ? vr[n][w] : 0u;
+      }
+    }
+    float pw[C::NI];  // the keys' weights (0 after the token)
 #pragma unroll
     for (int n = 0; n < C::NI; ++n) {
-      // Keys after the token are skipped by selection, not by a zero weight:
-      // the cache beyond L_b may hold anything, NaN included.
-      const bool visible = key_cur + n * KPI + kq <= t;
-      const float pn = fast_exp2(sc[n] - m_new);
-      l += visible ? pn : 0.f;
-      const float pv = pn * vs;
-      float vf[E];
-      if constexpr (kInt8) {
-        codes_to_float_biased(vr[n], vf);  // code + 128
-        pvsum += visible ? pv : 0.f;
-      } else {
-        chunk_to_float<TC>(vr[n], vf);
+      pw[n] = fast_exp2(sc[n] - m_new);
+      l += pw[n];
+      if constexpr (kInt8 && !kDotF16) pw[n] *= vs;  // (the f16 form scales per unit)
+    }
+    if constexpr (kDotBf16) {
+      static_assert(C::NI % 2 == 0, "keys pair up for v_dot2");
+#pragma unroll
+      for (int n = 0; n < C::NI; n += 2) {
+        const uint32_t pp = pack_bf16x2(pw[n], pw[n + 1]);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          // element 2w (low halves) and 2w + 1 (high halves) of the two keys
+          const uint32_t lo = __builtin_amdgcn_perm(vr[n + 1][w], vr[n][w], 0x05040100u);
+          const uint32_t hi = __builtin_amdgcn_perm(vr[n + 1][w], vr[n][w], 0x07060302u);
+          o[2 * w] = dot2_bf16(lo, pp, o[2 * w]);
+          o[2 * w + 1] = dot2_bf16(hi, pp, o[2 * w + 1]);
+        }
+      }
+    } else if constexpr (kDotF16) {
+      // Two keys' codes per element as the f16 pair (1024 + code + 128) of
+      // each, weighted by the two weights in f16; the unit's V scale then
+      // multiplies the unit's sums once.
+      static_assert(C::NI % 2 == 0, "keys pair up for v_dot2");
+      float oc[E];
+      float psum = 0.f;
+#pragma unroll
+      for (int n = 0; n < C::NI; n += 2) {
+        const auto ph = __builtin_amdgcn_cvt_pkrtz(pw[n], pw[n + 1]);  // weights in [0, 1]
+        const uint32_t pp = __builtin_bit_cast(uint32_t, ph);
+        psum += (float)ph[0] + (float)ph[1];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          // bytes k of both keys side by side: lo holds elements 4w, 4w + 1,
+          // hi elements 4w + 2, 4w + 3
+          const uint32_t lo = __builtin_amdgcn_perm(vr[n + 1][w], vr[n][w], 0x05010400u) ^ 0x80808080u;
+          const uint32_t hi = __builtin_amdgcn_perm(vr[n + 1][w], vr[n][w], 0x07030602u) ^ 0x80808080u;
+          const float c0 = n == 0 ? 0.f : oc[4 * w], c1 = n == 0 ? 0.f : oc[4 * w + 1];
+          const float c2v = n == 0 ? 0.f : oc[4 * w + 2], c3 = n == 0 ? 0.f : oc[4 * w + 3];
+          oc[4 * w] = dot2_f16(biased_pair_f16<0>(lo), pp, c0);
+          oc[4 * w + 1] = dot2_f16(biased_pair_f16<2>(lo), pp, c1);
+          oc[4 * w + 2] = dot2_f16(biased_pair_f16<0>(hi), pp, c2v);
+          oc[4 * w + 3] = dot2_f16(biased_pair_f16<2>(hi), pp, c3);
+        }
       }
 #pragma unroll
-      for (int e = 0; e < E; ++e) o[e] = visible ? fmaf(pv, vf[e], o[e]) : o[e];
-    }
+      for (int e = 0; e < E; ++e) o[e] = fmaf(vs, oc[e], o[e]);
+      pvsum = fmaf(vs, psum, pvsum);
+    } else {
 #pragma unroll
-    for (int n = 0; n < C::NI; ++n) {
-      kr[n] = kn[n];
-      vr[n] = vn[n];
+      for (int n = 0; n < C::NI; ++n) {
+        float vf[E];
+        if constexpr (kInt8) {
+          codes_to_float_biased(vr[n], vf);  // code + 128
+          pvsum += pw[n];
+        } else {
+          chunk_to_float<TC>(vr[n], vf);
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] = fmaf(pw[n], vf[e], o[e]);
+      }
     }
-    sc_cur = sc_next;
-    key_cur = key_next;
-    s = sn;
+  };
+
+  // Two register sets take turns: while one unit is computed, the next
+  // one's loads are in flight into the other set (no copies between them).
+  u32x4_t ka[C::NI], va[C::NI], kb[C::NI], vb[C::NI];
+  f32x2_t sa = {1.f, 1.f}, sb = {1.f, 1.f};
+  int key_a = -1, key_b = -1;
+  int s = next_slot(wave, key_a);
+  if (s < nslots) load(key_a, ka, va, sa);
+  while (s < nslots) {
+    s = next_slot(s + W, key_b);
+    if (s < nslots) load(key_b, kb, vb, sb);
+    unit(key_a, ka, va, sa);
+    if (s >= nslots) break;
+    s = next_slot(s + W, key_a);
+    if (s < nslots) load(key_a, ka, va, sa);
+    unit(key_b, kb, vb, sb);
   }
 
-  if constexpr (kInt8) {  // take off the 128 the biased V codes carried
+  if constexpr (kInt8) {  // take off the offset the biased V codes carried
+    constexpr float kOffset = kDotF16 ? -1152.f : -128.f;
 #pragma unroll
-    for (int e = 0; e < E; ++e) o[e] = fmaf(-128.f, pvsum, o[e]);
+    for (int e = 0; e < E; ++e) o[e] = fmaf(kOffset, pvsum, o[e]);
   }
   // Sum over the key groups: every lane of chunk c then holds the wave's
   // O[c E .. c E + E) and l (each key's weight counted once per group).
-  l = lanes_sum<LPK, kWave>(l);
+  l = stride_sum<LPK>(l);
 #pragma unroll
-  for (int e = 0; e < E; ++e) o[e] = lanes_sum<LPK, kWave>(o[e]);
+  for (int e = 0; e < E; ++e) o[e] = stride_sum<LPK>(o[e]);
   if (kq == 0) {
 #pragma unroll
     for (int e = 0; e < E; ++e) part[wave][chunk * E + e] = o[e];
@@ -451,7 +620,7 @@ __global__ __launch_bounds__(kQuantThreads) void bsa_quantize_kernel(const T* __
 #pragma unroll
     for (int e = 0; e < per; ++e) amax = fmaxf(amax, fabsf(f[i][e]));
   }
-  amax = lanes_max<1, kWave>(amax);
+  amax = group_max<1, kWave>(amax);
   if ((threadIdx.x & (kWave - 1)) == 0) wave_max[threadIdx.x / kWave] = amax;
   __syncthreads();
 #pragma unroll
