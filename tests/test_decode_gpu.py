@@ -121,6 +121,24 @@ def test_decode_dense_rows_longer_than_64_entries():
     _check(o, lse, ro, rl, torch.bfloat16)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("bs,d", [(32, 64), (32, 128), (64, 64), (64, 128)])
+def test_decode_garbage_after_the_token_every_shape(dtype, bs, d):
+    # NaN / inf in the cache after each sequence's length, with the token at
+    # the first, a middle and the last key of a load unit and of a block
+    n_cap = 8 * bs
+    mask = oracle.block_mask_from_sets(oracle.loglinear_block_sets(n_cap, bs))
+    lengths = [1, 2, 17, bs - 1, bs, bs + 1, 3 * bs - 1, 5 * bs + 9, n_cap - 3, n_cap]
+    q, k, v = _make(len(lengths), 2, n_cap, d, dtype, 11 + bs + d)
+    ro, rl = oracle.block_sparse_decode(q.double().numpy(), k.double().numpy(),
+                                        v.double().numpy(), lengths, mask, bs)
+    for b, L in enumerate(lengths):
+        k[b, :, L:] = float("nan") if b % 2 else float("inf")
+        v[b, :, L:] = float("inf") if b % 2 else float("nan")
+    o, lse = _run(q, k, v, lengths, mask, bs, dtype)
+    _check(o, lse, ro, rl, dtype)
+
+
 def test_decode_ignores_cache_beyond_length_and_bad_lengths():
     bs, d, n_cap = 32, 64, 256
     M = n_cap // bs

@@ -95,6 +95,68 @@ def test_decode_int8_loglinear(dtype, bs, d):
     _check(o, lse, ro, rl, dtype)
 
 
+@pytest.mark.parametrize("bs,d", [(32, 64), (32, 128), (64, 64), (64, 128)])
+def test_decode_int8_garbage_after_the_token(bs, d):
+    # after each sequence's length: codes outside [-127, 127] (-128) and
+    # random bytes in the token's own block, NaN scales in the blocks past it
+    n_cap = 8 * bs
+    mask = oracle.block_mask_from_sets(oracle.loglinear_block_sets(n_cap, bs))
+    lengths = [1, 17, bs - 1, bs + 1, 3 * bs - 1, 5 * bs + 9, n_cap]
+    B, H = len(lengths), 2
+    q = _randn((B, H, d), torch.bfloat16, 21 + d)
+    k = _randn((B, H, n_cap, d), torch.float32, 22 + d)
+    v = _randn((B, H, n_cap, d), torch.float32, 23 + d)
+    kc, ks = oracle.quantize_blocks(k.numpy(), bs)
+    vc, vs = oracle.quantize_blocks(v.numpy(), bs)
+    ro, rl = oracle.block_sparse_decode_int8(q.double().numpy(), kc, ks, vc, vs, lengths, mask, bs)
+    rng = np.random.default_rng(bs + d)
+    kc, vc, ks, vs = kc.copy(), vc.copy(), ks.copy(), vs.copy()
+    for b, L in enumerate(lengths):
+        kc[b, :, L:] = rng.integers(-128, 128, kc[b, :, L:].shape, dtype=np.int8)
+        vc[b, :, L:] = -128
+        first_past = -(-L // bs)  # blocks wholly after the token
+        ks[b, :, first_past:] = np.nan
+        vs[b, :, first_past:] = np.inf
+    dev = torch.device("cuda")
+    rp, ci = bsa.build_pattern(n_cap, bs, mask=mask)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    o, lse = bsa.decode_int8kv(q.to(dev), t(kc), t(ks), t(vc), t(vs),
+                               torch.tensor(lengths, dtype=torch.int32, device=dev),
+                               rp.to(dev), ci.to(dev), bs)
+    torch.cuda.synchronize()
+    _check(o.double().cpu().numpy(), lse.double().cpu().numpy(), ro, rl, torch.bfloat16)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("q_scale", [2.0 ** 14, 2.0 ** -20])
+def test_decode_int8_query_magnitudes(d, q_scale):
+    # a bf16 query far outside float16 range (2^14 N(0,1): |q| up to ~2^16)
+    # and one far below its normal range; the scores' float16 form scales q
+    # by a power of two, which must not show in the result
+    bs, n_cap = 32, 512
+    mask = oracle.block_mask_from_sets(oracle.loglinear_block_sets(n_cap, bs))
+    lengths = [n_cap, 300, 45]
+    B, H = len(lengths), 2
+    q = (_randn((B, H, d), torch.float32, 31) * q_scale).to(torch.bfloat16)
+    k = _randn((B, H, n_cap, d), torch.float32, 32)
+    v = _randn((B, H, n_cap, d), torch.float32, 33)
+    kc, ks = oracle.quantize_blocks(k.numpy(), bs)
+    vc, vs = oracle.quantize_blocks(v.numpy(), bs)
+    dev = torch.device("cuda")
+    rp, ci = bsa.build_pattern(n_cap, bs)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    o, lse = bsa.decode_int8kv(q.to(dev), t(kc), t(ks), t(vc), t(vs),
+                               torch.tensor(lengths, dtype=torch.int32, device=dev),
+                               rp.to(dev), ci.to(dev), bs)
+    torch.cuda.synchronize()
+    ro, rl = oracle.block_sparse_decode_int8(q.double().numpy(), kc, ks, vc, vs, lengths, mask, bs)
+    o, lse = o.double().cpu().numpy(), lse.double().cpu().numpy()
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    assert np.abs(o - ro).max() <= 2e-2
+    # the LSE is as large as the scores: float32 relative accuracy
+    assert np.abs(lse - rl).max() <= 2e-2 * max(1.0, 1e-3 * np.abs(rl).max())
+
+
 def test_decode_int8_random_mask_per_head_and_scale():
     bs, d, n_cap, H = 32, 64, 1024, 3
     M = n_cap // bs
