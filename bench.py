@@ -53,6 +53,9 @@ def parse_args(argv=None):
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-graph", action="store_true", help="time eager launches only")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-cold", action="store_true",
+                   help="skip the cold-cache launches (512 MiB write before each)")
+    p.add_argument("--cold-launches", type=int, default=50)
     p.add_argument("--no-saturating", action="store_true",
                    help="skip the B=32 line of the worked-example shape")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -310,6 +313,43 @@ def load_traffic(workload: str, prefix: str = "bsa_fwd", src: str = KERNEL_SRC):
     return rec.get("hbm_bytes_per_launch")
 
 
+def load_mfma(workload: str, src: str = KERNEL_SRC):
+    """Matrix-core flop per launch counted by rocprofv3 (SQ_INSTS_VALU_MFMA_MOPS_*,
+    512 flop each) from committed summaries, valid only while the kernel
+    source is unchanged since the counters were taken."""
+    path = os.path.join(PROFILES, f"bsa_fwd_mfma_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash(src):
+        return None
+    return rec.get("mfma_flop_per_launch")
+
+
+def time_cold(case, launches: int, scratch_mib: int = 512):
+    """Cold-cache launch durations: before each launch a fill kernel writes a
+    scratch buffer larger than the L2s and the MALL together, then HIP events
+    bracket the launch alone.  Returns the median seconds per launch."""
+    import statistics
+
+    import torch
+
+    scratch = torch.empty(scratch_mib << 20, dtype=torch.uint8, device=case.q.device)
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(launches)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(evs):
+        scratch.fill_(i & 0xFF)
+        a.record(stream)
+        case.step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    del scratch
+    return statistics.median(a.elapsed_time(b) for a, b in evs) * 1e-3
+
+
 def cpu_baseline(workload: str, seed: int, min_seconds: float):
     """Time the float64 oracle as it stands on this host's cores over whole
     passes of the workload (or of a bounded head subset for large ones)."""
@@ -439,6 +479,7 @@ def side_line(name, args, device, causal, backward=False):
     s_step = s_graph if s_graph is not None else time_eager(sat, sat_steps)
     s_kernel = s_evt if s_evt is not None else s_launch
     s_traffic = None if causal or backward else load_traffic(name)
+    s_mfma = None if causal or backward else load_mfma(name)
     line = {
         "value": round(sat.flops / s_step / 1e12, 3),
         "unit": "TFLOP/s",
@@ -451,6 +492,10 @@ def side_line(name, args, device, causal, backward=False):
         "traffic_over_algorithmic": None if s_traffic is None
         else round(s_traffic / sat.compulsory_bytes, 3),
     }
+    if not backward and not causal:
+        line["mfma_flop_counted_per_launch"] = s_mfma
+        line["mfma_counted_over_algorithmic"] = (None if s_mfma is None
+                                                 else round(s_mfma / sat.flops, 4))
     if causal:
         line["flop_counting"] = "selected (query, key) pairs: diagonal blocks count bs(bs+1)/2"
     if backward:
@@ -529,6 +574,7 @@ def main(argv=None):
         roof = {"bound": "mfma", "achieved": round(tflops, 3), "peak": peak_flops,
                 "unit": "TFLOP/s", "frac": round(tflops / peak_flops, 4)}
     traffic = None if args.causal else load_traffic(args.workload)
+    mfma_counted = None if args.causal else load_mfma(args.workload)
     roof.update({
         "traffic": traffic,
         "kernel": "bsa_fwd_kernel",
@@ -541,7 +587,21 @@ def main(argv=None):
         "mfma_achieved_tflops": round(tflops, 3),
         "mfma_frac": round(tflops / peak_flops, 4),
         "traffic_over_algorithmic": None if traffic is None else round(traffic / case.compulsory_bytes, 3),
+        "mfma_flop_counted_per_launch": mfma_counted,
+        "mfma_counted_over_algorithmic": None if mfma_counted is None
+        else round(mfma_counted / case.flops, 4),
     })
+    # Cold caches: a 512 MiB write before every launch (no L2 or MALL hits on
+    # the inputs); each launch timed alone.
+    cold = None
+    if not args.no_cold:
+        cold_s = time_cold(case, args.cold_launches)
+        cold = {"kernel_us_median": cold_s * 1e6, "value": round(case.flops / cold_s / 1e12, 3),
+                "unit": "TFLOP/s", "launches": args.cold_launches, "scratch_mib": 512,
+                "compulsory_hbm_gbps": round(case.compulsory_bytes / cold_s / 1e9, 1),
+                "warm_per_launch_event_us": launch_s * 1e6,
+                "timing": "HIP events around each launch alone (compare warm_per_launch_event_us, "
+                          "timed the same way)"}
     result = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -566,6 +626,8 @@ def main(argv=None):
         "first_step_ms_with_pattern_build_and_upload": case.first_step_ms,
         "roofline": roof,
     }
+    if cold is not None:
+        result["cold_cache"] = cold
 
     if not args.no_saturating and args.workload == "worked_example" and not args.causal:
         del case
