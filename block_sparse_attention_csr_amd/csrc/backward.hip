@@ -257,8 +257,9 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 0>::W)) void bsa_bwd_dq(B
 #pragma unroll
   for (int e = 0; e < NB; ++e) jq[e] = entry_at(e, mq[e]);
   wait_vm_lgkm0<0>();  // Q, dO, O, LSE loads and the list are complete
-  issue(jq[0], buf0);
-  if (NB == 3) issue(jq[1], buf1);
+  // The first copies, for the entries there are (none for an empty list).
+  if (U > 0) issue(jq[0], buf0);
+  if (NB == 3 && U > 1) issue(jq[1], buf1);
   auto buffer = [&](auto b_c) -> unsigned char* {
     constexpr int b = decltype(b_c)::value;
     if constexpr (b == 0) return buf0;
@@ -289,7 +290,8 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 0>::W)) void bsa_bwd_dq(B
   }
 
   // dQ leaves through this wave's part of the idle ring (whole 16-byte stores).
-  __syncthreads();  // every wave is done with the ring; no copy is in flight
+  wait_vm_lgkm0<0>();  // no copy is still landing (the compiler does not track them)
+  __syncthreads();     // every wave is done with the ring
   store_rows_lds<T, D>(static_cast<T*>(p.dq) + head + (size_t)q0 * D, dq, p.scale, lane,
                        (LDS_PTR(unsigned char))buf0 + wave * (kQRows * D * (int)sizeof(T)));
 }
@@ -421,8 +423,9 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 8 * BS>::W)) void bsa_bwd
 #pragma unroll
   for (int e = 0; e < NB; ++e) jq[e] = entry_at(e, mq[e]);
   wait_vm_lgkm0<0>();  // K, V loads and the list are complete
-  issue(jq[0], buf0);
-  if (NB == 3) issue(jq[1], buf1);
+  // The first copies, for the entries there are (none for an empty list).
+  if (U > 0) issue(jq[0], buf0);
+  if (NB == 3 && U > 1) issue(jq[1], buf1);
   auto buffer = [&](auto b_c) -> unsigned char* {
     constexpr int b = decltype(b_c)::value;
     if constexpr (b == 0) return buf0;
@@ -454,7 +457,8 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 8 * BS>::W)) void bsa_bwd
   }
 
   // dK then dV leave through this wave's part of the idle ring.
-  __syncthreads();  // every wave is done with the ring; no copy is in flight
+  wait_vm_lgkm0<0>();  // no copy is still landing (the compiler does not track them)
+  __syncthreads();     // every wave is done with the ring
   LDS_PTR(unsigned char) region =
       (LDS_PTR(unsigned char))buf0 + wave * (kQRows * D * (int)sizeof(T));
   store_rows_lds<T, D>(static_cast<T*>(p.dk) + head + (size_t)k0 * D, dk, p.scale, lane, region);

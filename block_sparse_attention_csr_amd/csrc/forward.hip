@@ -354,8 +354,9 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
     for (int c = 0; c < D / 16; ++c)
       qop.r[c] = *(LDS_PTR(const u32x4_t))(qs + QL::chunk_offset(lane & 31, 2 * c + (lane >> 5)));
   }
-  issue(jq[0], buf0);
-  if (NB == 3) issue(jq[1], buf1);
+  // The first copies, for the steps there are (none for a row with no entry).
+  if (niter > 0) issue(jq[0], buf0);
+  if (NB == 3 && niter > 1) issue(jq[1], buf1);
   auto buffer = [&](auto b_c) -> unsigned char* {
     constexpr int b = decltype(b_c)::value;
     if constexpr (b == 0) return buf0;
@@ -385,6 +386,9 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
       if (i + 2 < niter) step(i + 2, std::integral_constant<int, 2>{});
   }
 
+  // No copy may still be landing in the ring once it is reused below (the
+  // copies are not tracked by the compiler's own waits).
+  wait_vm_lgkm0<0>();
   // ---- merge the key slices: slices 1..KS-1 publish (O, m, l); slice 0 merges
   if constexpr (KS > 1) {
     __syncthreads();  // every copy and read of the tile buffers is over

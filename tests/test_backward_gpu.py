@@ -103,6 +103,33 @@ def test_backward_parity(dt, bs, d, kind, B, H, M, causal):
     _check(f"dV {what}", dv, rv, dtype)
 
 
+@pytest.mark.parametrize("dt,bs,d", [(dt, bs, d) for dt in ("bf16", "f32") for bs in (32, 64)
+                                     for d in (64, 128)])
+def test_backward_key_blocks_no_query_selects(dt, bs, d):
+    """Empty CSC columns: every query block selects only blocks 0 and M - 1
+    (and its own for M - 2), so most key blocks are selected by no query:
+    their dK and dV are exactly 0."""
+    dtype = torch.bfloat16 if dt == "bf16" else torch.float32
+    B, H, M = 2, 2, 7
+    N = bs * M
+    m = np.zeros((M, M), np.uint8)
+    m[:, 0] = 1
+    m[:, M - 1] = 1
+    m[M - 2, M - 2] = 1
+    q, k, v = make_qkv(B, H, N, d, dtype, 61)
+    do = make_qkv(B, H, N, d, dtype, 62)[0]
+    dq, dk, dv = _run(q, k, v, do, bs, m, False)
+    rq, rk, rv, _ = oracle.block_sparse_attention_backward(_f64(q), _f64(k), _f64(v), _f64(do),
+                                                           m, bs)
+    for j in range(1, M - 2):  # no query block selects key block j
+        sl = slice(j * bs, (j + 1) * bs)
+        assert torch.all(dk[:, :, sl] == 0) and torch.all(dv[:, :, sl] == 0)
+    what = f"{dt} bs{bs} d{d} empty columns"
+    _check(f"dQ {what}", dq, rq, dtype)
+    _check(f"dK {what}", dk, rk, dtype)
+    _check(f"dV {what}", dv, rv, dtype)
+
+
 def test_backward_scale_override():
     q, k, v = make_qkv(1, 2, 64 * 6, 64, torch.bfloat16, 5)
     do = make_qkv(1, 2, 64 * 6, 64, torch.bfloat16, 6)[0]

@@ -257,6 +257,52 @@ def test_every_workgroup_shape(dt, bs, d, group, key_split):
     _compare(_f64(o), _f64(lse), o_ref, lse_ref, dtype, f"{dt} bs{bs} d{d} G{group} KS{key_split}")
 
 
+@pytest.mark.parametrize("group,key_split", SHAPES)
+@pytest.mark.parametrize("dt,bs,d", [("bf16", 32, 64), ("f32", 64, 128), ("bf16", 64, 128)])
+def test_hand_made_csr_empty_rows_and_out_of_range_entries(dt, bs, d, group, key_split):
+    """A CSR not from bsa_build_pattern: a row with no entry and a row with
+    only entries outside [0, M) get O = 0 and LSE = -inf (no NaN, the failure
+    the log-linear page traces to empty rows); entries outside [0, M) inside a
+    row are skipped; every other row matches the oracle."""
+    if (bs // 32) * group * key_split > 8:
+        pytest.skip("more than 8 waves per workgroup")
+    dtype = torch.bfloat16 if dt == "bf16" else torch.float32
+    B, H, M = 2, 2, 11
+    N = bs * M
+    mask = random_block_mask(M, 0.35, 23)
+    rows = [sorted(np.nonzero(mask[i])[0].tolist()) for i in range(M)]
+    rows[1] = []                       # empty
+    rows[4] = [-3, M + 2]              # only entries outside [0, M)
+    rows[6] = [-1, 0, 6, M]            # effective {0, 6}
+    rp = torch.tensor(np.cumsum([0] + [len(r) for r in rows]), dtype=torch.int32)
+    ci = torch.tensor([j for r in rows for j in r], dtype=torch.int32)
+    q, k, v = make_qkv(B, H, N, d, dtype, 29)
+    dev = torch.device("cuda")
+    try:
+        o, lse = bsa.forward(q.to(dev), k.to(dev), v.to(dev), rp.to(dev), ci.to(dev), bs,
+                             group=group, key_split=key_split)
+    except bsa.BsaError as e:
+        assert e.status == 2
+        pytest.skip(f"shape needs more LDS than a workgroup has: {e}")
+    torch.cuda.synchronize()
+    o, lse = _f64(o), _f64(lse)
+    eff = np.zeros((M, M), np.uint8)
+    for i, r in enumerate(rows):
+        for j in r:
+            if 0 <= j < M:
+                eff[i, j] = 1
+    dead = [i for i in range(M) if not eff[i].any()]
+    assert dead == [1, 4]
+    for i in dead:
+        sl = slice(i * bs, (i + 1) * bs)
+        assert np.all(o[:, :, sl] == 0) and np.all(lse[:, :, sl] == -np.inf)
+        eff[i, i] = 1  # any non-empty row for the oracle; these rows are not compared
+    o_ref, lse_ref = oracle.block_sparse_attention(_f64(q), _f64(k), _f64(v), eff, bs)
+    live = np.concatenate([np.arange(i * bs, (i + 1) * bs) for i in range(M) if i not in dead])
+    _compare(o[:, :, live], lse[:, :, live], o_ref[:, :, live], lse_ref[:, :, live], dtype,
+             f"{dt} bs{bs} d{d} G{group} KS{key_split}")
+
+
 @pytest.mark.parametrize("B,H", [(1, 1), (2, 2)])
 def test_longest_supported_blocks_sampled(B, H):
     """N = 131072 at block 32: M = 4096 query blocks, the largest entry list
