@@ -84,6 +84,12 @@ template <int D>
 constexpr int partial_bytes() {
   return (D / 32) * 16 * kWave * 4 + 2 * kWave * 4;
 }
+// Two key slices split the finish by columns: each publishes the half of its
+// (O, m, l) the other finishes.
+template <int D>
+constexpr int half_partial_bytes() {
+  return (D / 64) * 16 * kWave * 4 + 2 * kWave * 4;
+}
 
 // Compile-time shape of one kernel instantiation.
 template <typename T, int BS, int D, int G, int KS>
@@ -103,7 +109,8 @@ struct Cfg {
   static constexpr int NB = KS == 1 && 3 * kSliceBytes <= 48 * 1024 ? 3 : 2;
   // Shapes whose buffers do not fit a workgroup's LDS are not instantiated.
   static constexpr bool kValid = NB * kSliceBytes + 1024 <= 160 * 1024 &&
-                                 (KS - 1) * SW * partial_bytes<D>() <= kSliceBytes;
+                                 (KS - 1) * SW * partial_bytes<D>() <= kSliceBytes &&
+                                 (KS != 2 || 2 * SW * half_partial_bytes<D>() <= kSliceBytes);
 };
 
 template <typename T, int BS, int D, int G, int KS, bool CAUSAL>
@@ -389,6 +396,62 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
   // No copy may still be landing in the ring once it is reused below (the
   // copies are not tracked by the compiler's own waits).
   wait_vm_lgkm0<0>();
+  // ---- two key slices: each finishes half of the columns.  Slice s keeps
+  // the d-tiles [s H, (s + 1) H), H = D / 64, publishes its other tiles with
+  // its (m, l), merges the other slice's copy of its own tiles and stores them.
+  if constexpr (KS == 2) {
+    constexpr int H = D / 64;
+    constexpr int kPF = half_partial_bytes<D>() / 4;
+    __syncthreads();  // every read of the tile buffers is over
+    float* part = reinterpret_cast<float*>(buf0);
+    auto publish = [&](auto s_c) {
+      constexpr int S = decltype(s_c)::value;
+      float* mine = part + (size_t)(S * SW + ws) * kPF;
+#pragma unroll
+      for (int t = 0; t < H; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mine[(t * 16 + r) * kWave + lane] = o[(1 - S) * H + t][r];
+      mine[H * 16 * kWave + lane] = m2;
+      mine[H * 16 * kWave + kWave + lane] = lsum;
+    };
+    if (ks == 0) publish(std::integral_constant<int, 0>{});
+    else publish(std::integral_constant<int, 1>{});
+    __syncthreads();
+    auto finish = [&](auto s_c) {
+      constexpr int S = decltype(s_c)::value;
+      const float* other = part + (size_t)((1 - S) * SW + ws) * kPF;
+      const float mo = other[H * 16 * kWave + lane];
+      const float lo = other[H * 16 * kWave + kWave + lane];
+      const float m_new = fmaxf(m2, mo);
+      if (m_new != -INFINITY) {  // else neither slice has seen a key
+        const float a_self = fast_exp2(m2 - m_new);
+        const float a_other = fast_exp2(mo - m_new);
+        lsum = lsum * a_self + lo * a_other;
+#pragma unroll
+        for (int t = 0; t < H; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            o[S * H + t][r] = o[S * H + t][r] * a_self + other[(t * 16 + r) * kWave + lane] * a_other;
+        m2 = m_new;
+      }
+      if (!has_rows) return;
+      const float l_all = halves_sum(lsum);
+      const float inv = l_all > 0.f ? 1.f / l_all : 0.f;
+      // staged through buf1 (idle now): 32 rows of 32 H columns per wave
+      constexpr int kStageB = kQRows * H * 32 * (int)sizeof(T);
+      static_assert(2 * SW * kStageB <= C::kSliceBytes, "column stages fit one ring buffer");
+      LDS_PTR(unsigned char) region = (LDS_PTR(unsigned char))buf1 + (S * SW + ws) * kStageB;
+      store_cols_lds<T, D, S * H, H>(static_cast<T*>(p.o) + head + (size_t)q0 * D, o, inv, lane,
+                                     region);
+      if (S == 0 && p.lse != nullptr && (lane >> 5) == 0) {
+        const float lse2 = l_all > 0.f ? m2 + log2f(l_all) : -INFINITY;
+        p.lse[(size_t)bh * p.N + q0 + (lane & 31)] = lse2 * 0.69314718055994530942f;
+      }
+    };
+    if (ks == 0) finish(std::integral_constant<int, 0>{});
+    else finish(std::integral_constant<int, 1>{});
+    return;
+  }
   // ---- merge the key slices: slices 1..KS-1 publish (O, m, l); slice 0 merges
   if constexpr (KS > 1) {
     __syncthreads();  // every copy and read of the tile buffers is over

@@ -346,6 +346,42 @@ __device__ __forceinline__ void store_rows_lds(T* dst0, const f32x16_t (&x)[D / 
   }
 }
 
+// As store_rows_lds, for the NT tiles T0 .. T0 + NT - 1 of the accumulator
+// only (columns 32 T0 .. 32 (T0 + NT) - 1 of each row): the rows are staged
+// NT * 32 sizeof(T) bytes wide, and the stores go to dst0 + r D + 32 T0.
+template <typename T, int D, int T0, int NT>
+__device__ __forceinline__ void store_cols_lds(T* dst0, const f32x16_t (&x)[D / 32], float mul,
+                                               int lane, LDS_PTR(unsigned char) st) {
+  constexpr int kRowB = D * (int)sizeof(T);        // global row stride
+  constexpr int kPartB = NT * 32 * (int)sizeof(T);  // staged row
+  constexpr int kCpr = kPartB / 16;
+  constexpr int kSwz = kCpr < 8 ? kCpr - 1 : 7;
+  static_assert(T0 + NT <= D / 32 && (32 * kCpr) % kWave == 0, "column tiles");
+  const int h = lane >> 5;
+  const int r = lane & 31;
+#pragma unroll
+  for (int dt = 0; dt < NT; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int byte = (32 * dt + 8 * g + 4 * h) * (int)sizeof(T);
+      LDS_PTR(unsigned char) dst = st + r * kPartB + (((byte >> 4) ^ (r & kSwz)) << 4) + (byte & 15);
+      const float a0 = x[T0 + dt][4 * g] * mul, a1 = x[T0 + dt][4 * g + 1] * mul;
+      const float a2 = x[T0 + dt][4 * g + 2] * mul, a3 = x[T0 + dt][4 * g + 3] * mul;
+      if constexpr (std::is_same<T, __bf16>::value)
+        *(LDS_PTR(u32x2_t))dst = u32x2_t{pack_bf16x2(a0, a1), pack_bf16x2(a2, a3)};
+      else
+        *(LDS_PTR(f32x4_t))dst = f32x4_t{a0, a1, a2, a3};
+    }
+  unsigned char* const base = reinterpret_cast<unsigned char*>(dst0) + T0 * 32 * (int)sizeof(T);
+#pragma unroll
+  for (int i = 0; i < 32 * kCpr / kWave; ++i) {
+    const int k = lane + kWave * i;
+    const int rr = k / kCpr, c = k % kCpr;
+    const u32x4_t v = *(LDS_PTR(const u32x4_t))(st + rr * kPartB + ((c ^ (rr & kSwz)) << 4));
+    *reinterpret_cast<u32x4_t*>(base + (size_t)rr * kRowB + c * 16) = v;
+  }
+}
+
 // s_waitcnt: vector-memory count <= n and LDS/scalar count == 0.
 template <int n>
 __device__ __forceinline__ void wait_vm_lgkm0() {
