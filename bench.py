@@ -509,7 +509,7 @@ def side_line(name, args, device, causal, backward=False):
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: this benchmark runs on one GPU only (asked for --gpus {args.gpus}); "
               "the forward shards over (batch, head) with no communication, so the N-GPU "
               "rate is N times the one-GPU rate of the per-GPU share.", file=sys.stderr)
         return 2
