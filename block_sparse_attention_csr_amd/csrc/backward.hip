@@ -1,10 +1,12 @@
 // Block-sparse attention backward for gfx950 (MI355X): dQ, dK, dV.
 //
-// The gradient of the forward in forward.hip (softmax(scale Q K^T) V over the
-// selected blocks, [P3] "the O(N^2) bottleneck of long sequences" and [P1]
-// section 3.3's normalisation over the connected blocks; the backward is the
-// step [P1] section 5.3 takes next, here without its gradient-compensation
-// heuristic).  With P recomputed from the saved log-sum-exp,
+// The gradient of the forward in forward.hip: softmax(scale Q K^T) V over the
+// selected blocks (Ascend CANN SparseFlashAttention article,
+// hwcomputing.csdn.net, "the O(N^2) bottleneck of long sequences"), with the
+// normalisation over the connected blocks only ("Block Sparse Attention:
+// Log-Linear complexity sparse attention implementation", czchanglian.com,
+// section 3.3).  That page's section 5.3 takes the backward as its next
+// step; its gradient-compensation heuristic is not applied here.  With P recomputed from the saved log-sum-exp,
 //   dV = P^T dO,  dP = dO V^T,  D_r = dO_r . O_r,  dS = P * (dP - D),
 //   dQ = scale dS K,  dK = scale dS^T Q.
 //
