@@ -315,7 +315,8 @@ struct Ops<float> {
 // sizeof(T) bytes): written row-major with 16-byte chunks XOR-swizzled by row
 // (8 bank groups), read back as 16-byte chunks of consecutive rows and
 // stored to rows dst0 + r D.  Each lane then issues whole 16-byte stores
-// instead of 8-byte pieces.
+// instead of 8-byte pieces, non-temporal (they fill whole lines and are not
+// read back, so they do not push the K/V tiles out of L2).
 template <typename T, int D>
 __device__ __forceinline__ void store_rows_lds(T* dst0, const f32x16_t (&x)[D / 32], float mul,
                                                int lane, LDS_PTR(unsigned char) st) {
@@ -341,8 +342,11 @@ __device__ __forceinline__ void store_rows_lds(T* dst0, const f32x16_t (&x)[D / 
     const int k = lane + kWave * i;
     const int rr = k / kCpr, c = k % kCpr;
     const u32x4_t v = *(LDS_PTR(const u32x4_t))(st + rr * kRowB + ((c ^ (rr & 7)) << 4));
-    *reinterpret_cast<u32x4_t*>(reinterpret_cast<unsigned char*>(dst0) + (size_t)rr * kRowB +
-                                c * 16) = v;
+    // non-temporal: the output is not read again here, and whole 16-byte
+    // chunks of consecutive rows fill whole lines, so it need not occupy L2
+    __builtin_nontemporal_store(
+        v, reinterpret_cast<u32x4_t*>(reinterpret_cast<unsigned char*>(dst0) +
+                                      (size_t)rr * kRowB + c * 16));
   }
 }
 
@@ -378,7 +382,7 @@ __device__ __forceinline__ void store_cols_lds(T* dst0, const f32x16_t (&x)[D / 
     const int k = lane + kWave * i;
     const int rr = k / kCpr, c = k % kCpr;
     const u32x4_t v = *(LDS_PTR(const u32x4_t))(st + rr * kPartB + ((c ^ (rr & kSwz)) << 4));
-    *reinterpret_cast<u32x4_t*>(base + (size_t)rr * kRowB + c * 16) = v;
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(base + (size_t)rr * kRowB + c * 16));
   }
 }
 
