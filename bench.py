@@ -39,9 +39,18 @@ PROFILES = os.path.join(ROOT, "profiles")
 DECODE_METRIC = "decode GB/s (algorithmic bytes: visible K/V rows) + % of 8 TB/s HBM peak"
 
 
+SHARED_SRC = os.path.join(ROOT, "block_sparse_attention_csr_amd", "csrc", "mfma_tiles.h")
+
+
 def kernel_source_hash(path: str = KERNEL_SRC) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """First 16 hex digits of the SHA-256 over a kernel's source file followed
+    by the device header every kernel file includes (mfma_tiles.h), so that a
+    profile record goes stale when either changes."""
+    h = hashlib.sha256()
+    for p in (path, SHARED_SRC):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def parse_args(argv=None):

@@ -382,7 +382,11 @@ __device__ __forceinline__ void store_cols_lds(T* dst0, const f32x16_t (&x)[D / 
     const int k = lane + kWave * i;
     const int rr = k / kCpr, c = k % kCpr;
     const u32x4_t v = *(LDS_PTR(const u32x4_t))(st + rr * kPartB + ((c ^ (rr & kSwz)) << 4));
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(base + (size_t)rr * kRowB + c * 16));
+    u32x4_t* const out = reinterpret_cast<u32x4_t*>(base + (size_t)rr * kRowB + c * 16);
+    // rows narrower than a 128-byte line leave the other part of the line to
+    // another wave: those stores go through L2, which merges the two halves
+    if constexpr (kPartB >= 128) __builtin_nontemporal_store(v, out);
+    else *out = v;
   }
 }
 
