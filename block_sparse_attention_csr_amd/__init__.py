@@ -219,6 +219,38 @@ def _dtype_code(t):
     raise TypeError(f"unsupported dtype {t.dtype}; bfloat16 or float32 expected")
 
 
+def _check_buffer(t, name, shape, dtype, device):
+    """A caller-supplied device buffer: the library writes or reads it through
+    a raw pointer, so its size, type and place are checked here."""
+    if (not t.is_cuda or t.device != device or not t.is_contiguous()
+            or tuple(t.shape) != tuple(shape) or t.dtype != dtype):
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} "
+                         f"on {device}")
+
+
+def _check_csr(row_ptr, col_idx, device, rows, nnz, names=("row_ptr", "col_idx")):
+    """Device CSR arrays: int32 on the device, `rows` + 1 offsets (the kernels
+    read row_ptr[0 .. rows]) and at least nnz entries."""
+    import torch
+
+    for name, t in zip(names, (row_ptr, col_idx)):
+        if t.dtype != torch.int32 or not t.is_cuda or t.device != device or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 tensor on {device}")
+    if rows is not None and row_ptr.numel() != rows + 1:
+        raise ValueError(f"{names[0]} must hold {rows + 1} offsets, not {row_ptr.numel()}")
+    if col_idx.numel() < nnz:
+        raise ValueError(f"{names[1]} holds {col_idx.numel()} entries, fewer than nnz = {nnz}")
+
+
+def _pattern_rows(N: int, block_size: int, heads: int, per_head: bool):
+    """Offsets minus one that row_ptr must hold, or None when the shape is
+    invalid anyway (the library then reports it)."""
+    if block_size <= 0 or N % block_size != 0:
+        return None
+    M = N // block_size
+    return heads * (M + 1) - 1 if per_head else M
+
+
 def forward(q, k, v, row_ptr, col_idx, block_size: int, scale: float | None = None, *,
             out=None, lse=None, nnz: int | None = None, stream=None, group: int = 0,
             key_split: int = 0, causal: bool = False, per_head: bool = False):
@@ -249,13 +281,21 @@ def forward(q, k, v, row_ptr, col_idx, block_size: int, scale: float | None = No
         raise TypeError("row_ptr / col_idx must be int32")
     if not (row_ptr.is_cuda and col_idx.is_cuda):
         raise ValueError("row_ptr / col_idx must be on the GPU")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k, v must be on one device")
     B, H, N, d = q.shape
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     if nnz is None:
         nnz = col_idx.numel()
+    _check_csr(row_ptr, col_idx, q.device, _pattern_rows(N, int(block_size), H, per_head),
+               int(nnz))
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_buffer(out, "out", q.shape, q.dtype, q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    else:
+        _check_buffer(lse, "lse", (B, H, N), torch.float32, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     lib = _load()
@@ -323,22 +363,29 @@ def backward(q, k, v, o, lse, dout, row_ptr, col_idx, col_ptr, row_idx, block_si
     """
     import torch
 
+    if not q.is_cuda or q.dim() != 4:
+        raise ValueError("q must be a CUDA tensor [B, H, N, d]")
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
-        if not t.is_cuda or not t.is_contiguous() or t.shape != q.shape or t.dtype != q.dtype:
-            raise ValueError(f"{name} must be a contiguous CUDA tensor like q")
-    for t in (row_ptr, col_idx, col_ptr, row_idx):
-        if t.dtype != torch.int32 or not t.is_cuda:
-            raise ValueError("patterns must be int32 CUDA tensors")
+        _check_buffer(t, name, q.shape, q.dtype, q.device)
+    B, H, N, d = q.shape
+    _check_buffer(lse, "lse", (B, H, N), torch.float32, q.device)
+    rows = _pattern_rows(N, int(block_size), H, False)
+    _check_csr(row_ptr, col_idx, q.device, rows, col_idx.numel())
+    _check_csr(col_ptr, row_idx, q.device, rows, col_idx.numel(), ("col_ptr", "row_idx"))
     for t in (row_order, col_order):
         if t is not None and (t.dtype != torch.int32 or not t.is_cuda
                               or t.numel() != row_ptr.numel() - 1):
             raise ValueError("row_order / col_order must be int32 CUDA tensors of M entries")
-    B, H, N, d = q.shape
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t is not None:
+            _check_buffer(t, name, q.shape, q.dtype, q.device)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
     if delta is None:
         delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    else:
+        _check_buffer(delta, "delta", (B, H, N), torch.float32, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     st = _load().bsa_backward(
@@ -353,6 +400,26 @@ def backward(q, k, v, o, lse, dout, row_ptr, col_idx, col_ptr, row_idx, block_si
     if st != BSA_OK:
         raise BsaError(st, "bsa_backward")
     return dq, dk, dv
+
+
+def _decode_common(q, seqlens, row_ptr, col_idx, n_cap, block_size, per_head, nnz, out, lse):
+    """Checks shared by the decode entry points; returns (out, lse)."""
+    import torch
+
+    B, H, d = q.shape
+    if (seqlens.dtype != torch.int32 or not seqlens.is_cuda or seqlens.device != q.device
+            or not seqlens.is_contiguous() or seqlens.numel() != B):
+        raise ValueError(f"seqlens must be a contiguous int32 tensor of {B} entries on {q.device}")
+    _check_csr(row_ptr, col_idx, q.device, _pattern_rows(n_cap, block_size, H, per_head), nnz)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_buffer(out, "out", q.shape, q.dtype, q.device)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    else:
+        _check_buffer(lse, "lse", (B, H), torch.float32, q.device)
+    return out, lse
 
 
 def decode(q, k_cache, v_cache, seqlens, row_ptr, col_idx, block_size: int,
@@ -379,18 +446,13 @@ def decode(q, k_cache, v_cache, seqlens, row_ptr, col_idx, block_size: int,
         raise ValueError("q and the caches disagree on B, H or d")
     if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
         raise ValueError("q and the caches must share a dtype")
-    if seqlens.dtype != torch.int32 or not seqlens.is_cuda or seqlens.numel() != B:
-        raise ValueError("seqlens must be an int32 CUDA tensor of B entries")
-    for t in (row_ptr, col_idx):
-        if t.dtype != torch.int32 or not t.is_cuda:
-            raise ValueError("row_ptr / col_idx must be int32 CUDA tensors")
+    if k_cache.device != q.device or v_cache.device != q.device:
+        raise ValueError("q and the caches must be on one device")
     n_cap = k_cache.shape[2]
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
     if nnz is None:
         nnz = col_idx.numel()
+    out, lse = _decode_common(q, seqlens, row_ptr, col_idx, n_cap, int(block_size), per_head,
+                              int(nnz), out, lse)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     st = _load().bsa_decode(
@@ -413,8 +475,12 @@ def quantize_kv(x, block_size: int, *, codes=None, scales=None, stream=None):
     B, H, N, d = x.shape
     if codes is None:
         codes = torch.empty(x.shape, dtype=torch.int8, device=x.device)
+    else:
+        _check_buffer(codes, "codes", x.shape, torch.int8, x.device)
     if scales is None:
         scales = torch.empty((B, H, N // block_size), dtype=torch.float32, device=x.device)
+    else:
+        _check_buffer(scales, "scales", (B, H, N // block_size), torch.float32, x.device)
     if stream is None:
         stream = torch.cuda.current_stream(x.device)
     st = _load().bsa_quantize_kv(x.data_ptr(), codes.data_ptr(), scales.data_ptr(), B, H, N, d,
@@ -441,18 +507,15 @@ def decode_int8kv(q, k_codes, k_scales, v_codes, v_scales, seqlens, row_ptr, col
         if t.shape[0] != B or t.shape[1] != H or t.shape[3] != d:
             raise ValueError(f"{name} disagrees with q on B, H or d")
     n_cap = k_codes.shape[2]
+    for name, t in (("k_codes", k_codes), ("v_codes", v_codes)):
+        if t.device != q.device or t.shape != k_codes.shape:
+            raise ValueError("q and the code caches must be on one device, the caches alike")
     for name, t in (("k_scales", k_scales), ("v_scales", v_scales)):
-        if (t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous()
-                or tuple(t.shape) != (B, H, n_cap // block_size)):
-            raise ValueError(f"{name} must be a float32 CUDA tensor [B, H, N_cap / block_size]")
-    if seqlens.dtype != torch.int32 or not seqlens.is_cuda or seqlens.numel() != B:
-        raise ValueError("seqlens must be an int32 CUDA tensor of B entries")
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+        _check_buffer(t, name, (B, H, n_cap // block_size), torch.float32, q.device)
     if nnz is None:
         nnz = col_idx.numel()
+    out, lse = _decode_common(q, seqlens, row_ptr, col_idx, n_cap, int(block_size), per_head,
+                              int(nnz), out, lse)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     st = _load().bsa_decode_int8kv(
