@@ -65,6 +65,8 @@ def parse_args(argv=None):
     p.add_argument("--no-cold", action="store_true",
                    help="skip the cold-cache launches (512 MiB write before each)")
     p.add_argument("--cold-launches", type=int, default=50)
+    p.add_argument("--no-row-split", action="store_true",
+                   help="walk every row in one workgroup (no bsa_forward_split)")
     p.add_argument("--no-saturating", action="store_true",
                    help="skip the B=32 line of the worked-example shape")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -101,7 +103,7 @@ def copy_calibration():
 class Case:
     """Inputs, cached pattern and preallocated outputs of one workload."""
 
-    def __init__(self, name, seed, device, causal=False):
+    def __init__(self, name, seed, device, causal=False, row_split=True):
         import numpy as np
         import torch
 
@@ -110,6 +112,9 @@ class Case:
 
         self.bsa = bsa
         self.causal = causal
+        self.row_split = row_split
+        self.split = None
+        self.workspace = None
         self.w = w = WORKLOADS[name]
         self.mask = workload_block_mask(w, seed)
         q, k, v = make_qkv(w.B, w.H, w.N, w.d, w.torch_dtype, seed)
@@ -117,6 +122,14 @@ class Case:
         self.out = torch.empty_like(self.q)
         self.lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=device)
         self.cache = bsa.PatternCache(device)
+        if row_split:
+            # long rows (a banded pattern's global rows) spread over workgroups;
+            # plan and workspace made once, outside the timed steps
+            self.split = self.cache.split_plan(w.N, w.block_size, mask=self.mask, causal=causal)
+            if self.split is not None:
+                need = bsa._load().bsa_row_split_workspace_bytes(w.B, w.H, w.block_size, w.d,
+                                                                 self.split.n_items)
+                self.workspace = torch.empty(need, dtype=torch.uint8, device=device)
         torch.cuda.synchronize()
         # First step: host pattern build + upload (cache miss) + forward.
         t0 = time.perf_counter()
@@ -142,7 +155,8 @@ class Case:
         row_ptr, col_idx, nnz = self.cache.get(w.N, w.block_size, mask=self.mask,
                                                causal=self.causal)
         self.bsa.forward(self.q, self.k, self.v, row_ptr, col_idx, w.block_size,
-                         out=self.out, lse=self.lse, nnz=nnz, causal=self.causal)
+                         out=self.out, lse=self.lse, nnz=nnz, causal=self.causal,
+                         split=self.split, workspace=self.workspace)
 
 
 class DecodeCase:
@@ -549,7 +563,8 @@ def main(argv=None):
             **line}), flush=True)
         return 0
 
-    case = Case(args.workload, args.seed, device, causal=args.causal)
+    case = Case(args.workload, args.seed, device, causal=args.causal,
+                row_split=not args.no_row_split)
     w = case.w
     for _ in range(args.warmup):
         case.step()
@@ -629,6 +644,9 @@ def main(argv=None):
             "d": w.d, "block_size": w.block_size, "nnz_per_head": case.nnz,
             "pattern": w.pattern, "causal": bool(args.causal), "parallelism": "single GPU",
             "timing": "HIP graph of K launches" if graph_s is not None else "eager",
+            "row_split": None if case.split is None else {
+                "heavy_rows_per_head": case.split.n_rows, "items_per_head": case.split.n_items,
+                "launches_per_step": 3},
         },
         "pct_bf16_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "eager_ms_per_step": eager_s * 1e3,

@@ -22,7 +22,8 @@ import numpy as np
 __all__ = [
     "BsaError", "build_pattern", "forward", "backward", "transpose_pattern", "status_string",
     "abi_version", "library_path", "PatternCache", "BSA_OK", "stack_head_patterns",
-    "pattern_order", "decode", "quantize_kv", "decode_int8kv", "attention",
+    "pattern_order", "decode", "quantize_kv", "decode_int8kv", "attention", "plan_row_split",
+    "RowSplitPlan",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -92,6 +93,15 @@ def _load():
     lib.bsa_forward_ex.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp,
                                    i64, ctypes.c_float, i32, i32, i32, vp]
     lib.bsa_forward_ex.restype = i32
+    p8 = ctypes.POINTER(ctypes.c_uint8)
+    lib.bsa_plan_row_split.argtypes = [i32, p32, i32, p8, p32, i32, p32, p32, p32]
+    lib.bsa_plan_row_split.restype = i32
+    lib.bsa_row_split_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.bsa_row_split_workspace_bytes.restype = i64
+    lib.bsa_forward_split.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp,
+                                      i64, ctypes.c_float, i32, vp, vp, i32, vp, i32, vp, i64,
+                                      vp]
+    lib.bsa_forward_split.restype = i32
     lib.bsa_transpose_pattern.argtypes = [i32, p32, p32, i64, p32, p32]
     lib.bsa_transpose_pattern.restype = i32
     lib.bsa_backward.argtypes = [vp] * 10 + [i32] * 6 + [vp] * 6 + [i64, ctypes.c_float, i32, vp]
@@ -219,6 +229,47 @@ def _dtype_code(t):
     raise TypeError(f"unsupported dtype {t.dtype}; bfloat16 or float32 expected")
 
 
+class RowSplitPlan:
+    """A bsa_plan_row_split plan: ``heavy`` uint8 [M], ``items`` int32
+    [n_items, 3] (row, first entry, end entry) and ``rows`` int32 [n_rows, 3]
+    (row, first item, item count), on the CPU or (``to``) on a device."""
+
+    def __init__(self, heavy, items, rows):
+        self.heavy, self.items, self.rows = heavy, items, rows
+        self.n_items = int(items.shape[0])
+        self.n_rows = int(rows.shape[0])
+
+    def to(self, device):
+        return RowSplitPlan(self.heavy.to(device), self.items.to(device), self.rows.to(device))
+
+
+def plan_row_split(row_ptr, chunk: int = 0):
+    """bsa_plan_row_split of a host CSR's offsets: a RowSplitPlan (CPU
+    tensors), or None when no row is long enough to split."""
+    import torch
+
+    pt = np.ascontiguousarray(np.asarray(row_ptr.cpu() if hasattr(row_ptr, "cpu") else row_ptr,
+                                         dtype=np.int32))
+    M = pt.size - 1
+    cap = max(int(pt[-1]), 1)
+    heavy = np.zeros(max(M, 1), np.uint8)
+    items = np.zeros(3 * cap, np.int32)
+    rows = np.zeros(3 * max(M, 1), np.int32)
+    n_items, n_rows = ctypes.c_int32(0), ctypes.c_int32(0)
+    p32 = ctypes.POINTER(ctypes.c_int32)
+    st = _load().bsa_plan_row_split(M, pt.ctypes.data_as(p32), int(chunk),
+                                    heavy.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)),
+                                    items.ctypes.data_as(p32), cap, ctypes.byref(n_items),
+                                    rows.ctypes.data_as(p32), ctypes.byref(n_rows))
+    if st != BSA_OK:
+        raise BsaError(st, "bsa_plan_row_split")
+    if n_items.value == 0:
+        return None
+    return RowSplitPlan(torch.from_numpy(heavy[:M].copy()),
+                        torch.from_numpy(items[:3 * n_items.value].reshape(-1, 3).copy()),
+                        torch.from_numpy(rows[:3 * n_rows.value].reshape(-1, 3).copy()))
+
+
 def _check_buffer(t, name, shape, dtype, device):
     """A caller-supplied device buffer: the library writes or reads it through
     a raw pointer, so its size, type and place are checked here."""
@@ -253,7 +304,8 @@ def _pattern_rows(N: int, block_size: int, heads: int, per_head: bool):
 
 def forward(q, k, v, row_ptr, col_idx, block_size: int, scale: float | None = None, *,
             out=None, lse=None, nnz: int | None = None, stream=None, group: int = 0,
-            key_split: int = 0, causal: bool = False, per_head: bool = False):
+            key_split: int = 0, causal: bool = False, per_head: bool = False, split=None,
+            workspace=None):
     """Block-sparse attention forward on the GPU.
 
     q, k, v: CUDA tensors [B, H, N, d] (bfloat16 or float32), contiguous.
@@ -264,7 +316,10 @@ def forward(q, k, v, row_ptr, col_idx, block_size: int, scale: float | None = No
     col_idx.numel().  ``group`` / ``key_split`` force a workgroup shape
     (bsa_forward_ex); 0 / 0 lets the library choose.  ``causal`` hides keys
     after each query position; ``per_head`` takes row_ptr as [H, M + 1]
-    offsets into one col_idx (see ``stack_head_patterns``).
+    offsets into one col_idx (see ``stack_head_patterns``).  ``split``: a
+    RowSplitPlan of the same pattern on the device (``plan_row_split``): its
+    heavy rows are spread over workgroups (bsa_forward_split); ``workspace``
+    optionally supplies the device bytes it needs, else they are allocated.
     """
     import torch
 
@@ -303,6 +358,27 @@ def forward(q, k, v, row_ptr, col_idx, block_size: int, scale: float | None = No
             d, int(block_size), _dtype_code(q), row_ptr.data_ptr(), col_idx.data_ptr(),
             int(nnz), 0.0 if scale is None else float(scale))
     flags = (FORWARD_CAUSAL if causal else 0) | (FORWARD_PATTERN_PER_HEAD if per_head else 0)
+    if split is not None:
+        if group or key_split or per_head:
+            raise ValueError("a row-split plan takes the automatic shape and one shared pattern")
+        M = N // int(block_size) if int(block_size) > 0 else 0
+        _check_buffer(split.heavy, "split.heavy", (M,), torch.uint8, q.device)
+        _check_buffer(split.items, "split.items", (split.n_items, 3), torch.int32, q.device)
+        _check_buffer(split.rows, "split.rows", (split.n_rows, 3), torch.int32, q.device)
+        need = int(lib.bsa_row_split_workspace_bytes(B, H, int(block_size), d, split.n_items))
+        if need < 0:
+            raise ValueError("unsupported shape for a row-split plan")
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        elif (not workspace.is_cuda or workspace.device != q.device
+              or not workspace.is_contiguous() or workspace.numel() * workspace.element_size() < need):
+            raise ValueError(f"workspace must be a contiguous tensor of >= {need} bytes on {q.device}")
+        st = lib.bsa_forward_split(*args, flags, split.heavy.data_ptr(), split.items.data_ptr(),
+                                   split.n_items, split.rows.data_ptr(), split.n_rows,
+                                   workspace.data_ptr(), need, stream.cuda_stream)
+        if st != BSA_OK:
+            raise BsaError(st, "bsa_forward_split")
+        return out, lse
     if group or key_split or flags:
         st = lib.bsa_forward_ex(*args, flags, int(group), int(key_split), stream.cuda_stream)
     else:
@@ -603,3 +679,17 @@ class PatternCache:
                    col_idx.to(self.device, non_blocking=False), int(col_idx.numel()))
             self._cache[key] = hit
         return hit
+
+    def split_plan(self, seq_len: int, block_size: int, *, mask=None, **options):
+        """The device RowSplitPlan of the same pattern, or None when no row is
+        long enough to split (cached with the pattern)."""
+        row_ptr, _, _ = self.get(seq_len, block_size, mask=mask, **options)
+        key = ("split", seq_len, block_size,
+               None if mask is None else
+               np.ascontiguousarray(np.asarray(mask) != 0, dtype=np.uint8).tobytes(),
+               tuple(sorted((k, tuple(v) if isinstance(v, (list, tuple)) else v)
+                            for k, v in options.items())))
+        if key not in self._cache:
+            plan = plan_row_split(row_ptr.cpu())
+            self._cache[key] = None if plan is None else plan.to(self.device)
+        return self._cache[key]

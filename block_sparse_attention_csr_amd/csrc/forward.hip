@@ -76,6 +76,14 @@ struct FwdParams {
   int32_t causal;     // hide keys after each query position
   int32_t row_stride; // row_ptr entries per head: M + 1 (one pattern per head) or 0
   float scale_log2;   // scale * log2(e)
+  // Rows split across workgroups (bsa_plan_row_split).  Main pass: heavy[r]
+  // != 0 marks a row this pass leaves out.  Split pass (G = KS = 1 only):
+  // split holds (row, first entry, end entry) per item, and each workgroup
+  // writes its item's partial (O, m, l) to partial.
+  const uint8_t* heavy;
+  const int32_t* split;
+  int32_t n_items;
+  float* partial;
 };
 
 // Partial state of a key-slice wave, stored for the merge: O^T in accumulator
@@ -146,11 +154,19 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
   // and started last the last one would run alone at the end.  The rest keep
   // their order, so neighbouring groups (which share K/V blocks) stay close
   // in time.
-  const int rank = wg % ngroups;
-  const int grp = rank == 0 ? ngroups - 1 : rank - 1;
-  const int bh = wg / ngroups;
+  int grp, bh, item = -1;
+  if (G == 1 && KS == 1 && p.split != nullptr) {  // split pass: one item of a heavy row
+    item = wg % p.n_items;
+    bh = wg / p.n_items;
+    grp = p.split[3 * item];
+  } else {
+    const int rank = wg % ngroups;
+    grp = rank == 0 ? ngroups - 1 : rank - 1;
+    bh = wg / ngroups;
+  }
   const int qb = grp * G + g;
-  const bool has_rows = qb < M;
+  // (a row the split pass takes is left out of this pass: no entry, no store)
+  const bool has_rows = qb < M && (item >= 0 || p.heavy == nullptr || p.heavy[qb] == 0);
   constexpr bool causal = CAUSAL;
   const int32_t* const row_ptr = p.row_ptr + (size_t)(bh % p.heads) * p.row_stride;
   const size_t head = (size_t)bh * p.N * D;
@@ -196,8 +212,13 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
   if constexpr (G == 1) {
     // Every wave reads the row from col_idx itself (64 entries at a time, in
     // entry_at): no LDS list and no barrier before the first copy.
-    rs = row_ptr[grp];
-    U = row_ptr[grp + 1] - rs;
+    if (item >= 0) {  // the item's entries of its row
+      rs = p.split[3 * item + 1];
+      U = p.split[3 * item + 2] - rs;
+    } else {
+      rs = row_ptr[grp];
+      U = has_rows ? row_ptr[grp + 1] - rs : 0;
+    }
   } else {
     for (int i = threadIdx.x; i < (G + 1) * MW; i += blockDim.x) bitmap[i] = 0;
     __syncthreads();
@@ -396,6 +417,21 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
   // No copy may still be landing in the ring once it is reused below (the
   // copies are not tracked by the compiler's own waits).
   wait_vm_lgkm0<0>();
+  // ---- split pass: the item's partial state, unnormalised, in accumulator
+  // order [register][lane], then m and l per lane (the merge reads the same)
+  if constexpr (G == 1 && KS == 1) {
+    if (item >= 0) {
+      float* dst = p.partial + ((size_t)bh * p.n_items + item) * QW * (partial_bytes<D>() / 4) +
+                   (size_t)qg * (partial_bytes<D>() / 4);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dst[(dt * 16 + r) * kWave + lane] = o[dt][r];
+      dst[(D / 32) * 16 * kWave + lane] = m2;
+      dst[(D / 32) * 16 * kWave + kWave + lane] = lsum;
+      return;
+    }
+  }
   // ---- two key slices: each finishes half of the columns.  Slice s keeps
   // the d-tiles [s H, (s + 1) H), H = D / 64, publishes its other tiles with
   // its (m, l), merges the other slice's copy of its own tiles and stores them.
@@ -520,6 +556,53 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
   }
 }
 
+// Finishes the rows split across workgroups: one workgroup per (batch*head,
+// heavy row), one wave per 32 query rows.  rows holds (row, first item, item
+// count) per heavy row; each lane merges the items' partial (O, m, l) as the
+// key slices merge theirs, normalises, and stores O and LSE.
+template <typename T, int BS, int D>
+__global__ __launch_bounds__(kWave * (BS / kQRows)) void bsa_fwd_merge_kernel(
+    FwdParams p, const int32_t* rows, int32_t n_rows) {
+  constexpr int QW = BS / kQRows;
+  constexpr int kPF = partial_bytes<D>() / 4;
+  __shared__ __attribute__((aligned(16))) unsigned char stage[QW][kQRows * D * sizeof(T)];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int qg = uniform(threadIdx.x / kWave);
+  const int bh = blockIdx.x / n_rows;
+  const int hr = blockIdx.x % n_rows;
+  const int row = rows[3 * hr], first = rows[3 * hr + 1], count = rows[3 * hr + 2];
+  f32x16_t o[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16_t{};
+  float m2 = -INFINITY, lsum = 0.f;
+  for (int c = 0; c < count; ++c) {
+    const float* src = p.partial + ((size_t)bh * p.n_items + first + c) * QW * kPF +
+                       (size_t)qg * kPF;
+    const float mo = src[(D / 32) * 16 * kWave + lane];
+    const float lo = src[(D / 32) * 16 * kWave + kWave + lane];
+    const float m_new = fmaxf(m2, mo);
+    if (m_new == -INFINITY) continue;  // neither side has seen a key yet
+    const float a_self = fast_exp2(m2 - m_new);
+    const float a_other = fast_exp2(mo - m_new);
+    lsum = lsum * a_self + lo * a_other;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        o[dt][r] = o[dt][r] * a_self + src[(dt * 16 + r) * kWave + lane] * a_other;
+    m2 = m_new;
+  }
+  const float l_all = halves_sum(lsum);
+  const float inv = l_all > 0.f ? 1.f / l_all : 0.f;
+  const int q0 = row * BS + qg * kQRows;
+  store_rows_lds<T, D>(static_cast<T*>(p.o) + (size_t)bh * p.N * D + (size_t)q0 * D, o, inv,
+                       lane, (LDS_PTR(unsigned char))stage[qg]);
+  if (p.lse != nullptr && (lane >> 5) == 0) {
+    const float lse2 = l_all > 0.f ? m2 + log2f(l_all) : -INFINITY;
+    p.lse[(size_t)bh * p.N + q0 + (lane & 31)] = lse2 * 0.69314718055994530942f;
+  }
+}
+
 // Dynamic LDS (G > 1): the union's entry list (M ints) and G + 1 bitmaps.
 size_t dynamic_lds_bytes(int group, int M) {
   if (group == 1) return 0;  // the row is read from col_idx directly
@@ -596,6 +679,31 @@ bsa_status dispatch(const FwdParams& p, int bs, int d, hipStream_t stream) {
   return BSA_ERR_INVALID_ARGUMENT;
 }
 
+template <typename T, int BS, int D>
+bsa_status launch_merge(const FwdParams& p, const int32_t* rows, int32_t n_rows, int64_t grid,
+                        hipStream_t stream) {
+  hipLaunchKernelGGL((bsa_fwd_merge_kernel<T, BS, D>), dim3((uint32_t)grid),
+                     dim3(kWave * (BS / kQRows)), 0, stream, p, rows, n_rows);
+  return hipGetLastError() == hipSuccess ? BSA_OK : BSA_ERR_HIP;
+}
+
+template <typename T>
+bsa_status dispatch_merge(const FwdParams& p, int bs, int d, const int32_t* rows, int32_t n_rows,
+                          int64_t grid, hipStream_t stream) {
+  if (bs == 32 && d == 64) return launch_merge<T, 32, 64>(p, rows, n_rows, grid, stream);
+  if (bs == 32 && d == 128) return launch_merge<T, 32, 128>(p, rows, n_rows, grid, stream);
+  if (bs == 64 && d == 64) return launch_merge<T, 64, 64>(p, rows, n_rows, grid, stream);
+  if (bs == 64 && d == 128) return launch_merge<T, 64, 128>(p, rows, n_rows, grid, stream);
+  return BSA_ERR_INVALID_ARGUMENT;
+}
+
+// Bytes of split-pass partials: per (batch*head, item), one partial state
+// per 32-row wave of the query block.
+int64_t split_workspace_bytes(int64_t bh, int bs, int d, int64_t n_items) {
+  const int64_t per_wave = d == 64 ? partial_bytes<64>() : partial_bytes<128>();
+  return bh * n_items * (bs / kQRows) * per_wave;
+}
+
 // Total LDS of a shape for (dtype, bs, d), or 0 when it is not instantiated.
 size_t lds_for(int dtype, int bs, int d, int group, int ks, int M) {
   size_t st = 0;
@@ -640,11 +748,23 @@ void choose_shape(int64_t bhm, int bs, int d, int dtype, int M, int* group, int*
 
 namespace {
 
+// Rows split across workgroups (bsa_forward_split).
+struct SplitPlan {
+  const uint8_t* heavy;
+  const int32_t* items;
+  int32_t n_items;
+  const int32_t* rows;
+  int32_t n_rows;
+  void* workspace;
+  int64_t workspace_bytes;
+};
+
 bsa_status forward_impl(const void* q, const void* k, const void* v, void* o, float* lse,
                         int32_t batch, int32_t heads, int32_t seq_len, int32_t head_dim,
                         int32_t block_size, int32_t dtype, const int32_t* row_ptr,
                         const int32_t* col_idx, int64_t nnz, float scale, int32_t flags,
-                        int32_t group, int32_t key_split, void* stream) {
+                        int32_t group, int32_t key_split, void* stream,
+                        const SplitPlan* plan = nullptr) {
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || row_ptr == nullptr ||
       col_idx == nullptr)
     return BSA_ERR_NULL_POINTER;
@@ -677,6 +797,29 @@ bsa_status forward_impl(const void* q, const void* k, const void* v, void* o, fl
   p.heads = heads;
   p.causal = (flags & BSA_FORWARD_CAUSAL) != 0 ? 1 : 0;
   p.row_stride = per_head ? static_cast<int32_t>(M + 1) : 0;
+  p.heavy = nullptr;
+  p.split = nullptr;
+  p.n_items = 0;
+  p.partial = nullptr;
+  const bool split = plan != nullptr && plan->n_items > 0;
+  if (plan != nullptr) {
+    if (per_head) return BSA_ERR_INVALID_ARGUMENT;  // the plan is of one shared pattern
+    if (plan->n_items < 0 || plan->n_rows < 0 || (plan->n_items > 0) != (plan->n_rows > 0) ||
+        plan->n_rows > M || plan->n_items > nnz)
+      return BSA_ERR_SHAPE;
+    if (split && (plan->heavy == nullptr || plan->items == nullptr || plan->rows == nullptr ||
+                  plan->workspace == nullptr))
+      return BSA_ERR_NULL_POINTER;
+    if (split) {
+      if ((int64_t)batch * heads * plan->n_items > INT32_MAX) return BSA_ERR_SHAPE;
+      if (reinterpret_cast<uintptr_t>(plan->workspace) % 16 != 0) return BSA_ERR_INVALID_ARGUMENT;
+      if (plan->workspace_bytes <
+          split_workspace_bytes((int64_t)batch * heads, block_size, head_dim, plan->n_items))
+        return BSA_ERR_BUFFER_TOO_SMALL;
+      if (lds_for(dtype, block_size, head_dim, 1, 1, (int)M) == 0) return BSA_ERR_INVALID_ARGUMENT;
+      p.heavy = plan->heavy;
+    }
+  }
   if (group == 0 && key_split == 0) {
     choose_shape((int64_t)batch * heads * M, block_size, head_dim, dtype, (int)M, &p.group,
                  &p.key_split);
@@ -697,8 +840,27 @@ bsa_status forward_impl(const void* q, const void* k, const void* v, void* o, fl
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // clear a stale, non-sticky error from earlier calls
-  if (dtype == BSA_DTYPE_F32) return dispatch<float>(p, block_size, head_dim, st);
-  return dispatch<__bf16>(p, block_size, head_dim, st);
+  bsa_status r = dtype == BSA_DTYPE_F32 ? dispatch<float>(p, block_size, head_dim, st)
+                                        : dispatch<__bf16>(p, block_size, head_dim, st);
+  if (r != BSA_OK || !split) return r;
+  // The heavy rows: their items, one one-block workgroup each, then the merge.
+  // (Forking the items onto a second stream to overlap the main pass was
+  // measured: within a few percent either way, so the calls stay in order.)
+  FwdParams ps = p;
+  ps.heavy = nullptr;
+  ps.group = 1;
+  ps.key_split = 1;
+  ps.split = plan->items;
+  ps.n_items = plan->n_items;
+  ps.partial = static_cast<float*>(plan->workspace);
+  ps.num_wg = batch * heads * plan->n_items;
+  r = dtype == BSA_DTYPE_F32 ? dispatch<float>(ps, block_size, head_dim, st)
+                             : dispatch<__bf16>(ps, block_size, head_dim, st);
+  if (r != BSA_OK) return r;
+  const int64_t grid = (int64_t)batch * heads * plan->n_rows;
+  return dtype == BSA_DTYPE_F32
+             ? dispatch_merge<float>(ps, block_size, head_dim, plan->rows, plan->n_rows, grid, st)
+             : dispatch_merge<__bf16>(ps, block_size, head_dim, plan->rows, plan->n_rows, grid, st);
 }
 
 }  // namespace
@@ -720,4 +882,26 @@ extern "C" bsa_status bsa_forward_ex(const void* q, const void* k, const void* v
                                      int32_t key_split, void* stream) {
   return forward_impl(q, k, v, o, lse, batch, heads, seq_len, head_dim, block_size, dtype,
                       row_ptr, col_idx, nnz, scale, flags, group, key_split, stream);
+}
+
+extern "C" int64_t bsa_row_split_workspace_bytes(int32_t batch, int32_t heads, int32_t block_size,
+                                                 int32_t head_dim, int32_t n_items) {
+  if (batch <= 0 || heads <= 0 || n_items < 0 || (block_size != 32 && block_size != 64) ||
+      (head_dim != 64 && head_dim != 128))
+    return -1;
+  return split_workspace_bytes((int64_t)batch * heads, block_size, head_dim, n_items);
+}
+
+extern "C" bsa_status bsa_forward_split(const void* q, const void* k, const void* v, void* o,
+                                        float* lse, int32_t batch, int32_t heads,
+                                        int32_t seq_len, int32_t head_dim, int32_t block_size,
+                                        int32_t dtype, const int32_t* row_ptr,
+                                        const int32_t* col_idx, int64_t nnz, float scale,
+                                        int32_t flags, const uint8_t* heavy,
+                                        const int32_t* items, int32_t n_items,
+                                        const int32_t* rows, int32_t n_rows, void* workspace,
+                                        int64_t workspace_bytes, void* stream) {
+  const SplitPlan plan{heavy, items, n_items, rows, n_rows, workspace, workspace_bytes};
+  return forward_impl(q, k, v, o, lse, batch, heads, seq_len, head_dim, block_size, dtype,
+                      row_ptr, col_idx, nnz, scale, flags, 0, 0, stream, &plan);
 }

@@ -244,6 +244,44 @@ extern "C" bsa_status bsa_pattern_order(int32_t M, const int32_t* ptr, int32_t* 
   return BSA_OK;
 }
 
+extern "C" bsa_status bsa_plan_row_split(int32_t M, const int32_t* row_ptr, int32_t chunk,
+                                         uint8_t* heavy, int32_t* items, int32_t item_cap,
+                                         int32_t* n_items, int32_t* rows, int32_t* n_rows) {
+  if (row_ptr == nullptr || heavy == nullptr || n_items == nullptr || rows == nullptr ||
+      n_rows == nullptr || (items == nullptr && item_cap > 0))
+    return BSA_ERR_NULL_POINTER;
+  if (M <= 0 || row_ptr[0] != 0 || item_cap < 0) return BSA_ERR_SHAPE;
+  for (int32_t i = 0; i < M; ++i)
+    if (row_ptr[i + 1] < row_ptr[i]) return BSA_ERR_SHAPE;
+  if (chunk <= 0) {  // about one ordinary row: the mean length, rounded up to 8
+    const int64_t mean = (static_cast<int64_t>(row_ptr[M]) + M - 1) / M;
+    chunk = static_cast<int32_t>(std::max<int64_t>(8, (mean + 7) / 8 * 8));
+  }
+  int64_t k = 0;
+  int32_t h = 0;
+  for (int32_t r = 0; r < M; ++r) {
+    const int32_t n = row_ptr[r + 1] - row_ptr[r];
+    heavy[r] = n > 2 * static_cast<int64_t>(chunk) ? 1 : 0;
+    if (!heavy[r]) continue;
+    const int32_t pieces = (n + chunk - 1) / chunk;
+    rows[3 * h] = r;
+    rows[3 * h + 1] = static_cast<int32_t>(k);
+    rows[3 * h + 2] = pieces;
+    ++h;
+    for (int32_t i = 0; i < pieces; ++i, ++k) {
+      if (k >= item_cap) continue;
+      const int32_t e0 = row_ptr[r] + i * chunk;
+      items[3 * k] = r;
+      items[3 * k + 1] = e0;
+      items[3 * k + 2] = std::min(e0 + chunk, row_ptr[r + 1]);
+    }
+  }
+  if (k > INT32_MAX) return BSA_ERR_SHAPE;
+  *n_items = static_cast<int32_t>(k);
+  *n_rows = h;
+  return k > item_cap ? BSA_ERR_BUFFER_TOO_SMALL : BSA_OK;
+}
+
 extern "C" const char* bsa_status_string(int32_t status) {
   switch (status) {
     case BSA_OK: return "BSA_OK";

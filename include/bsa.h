@@ -198,6 +198,72 @@ bsa_status bsa_forward_ex(const void* q, const void* k, const void* v, void* o, 
                           int32_t group, int32_t key_split, void* stream);
 
 /*
+ * bsa_plan_row_split -- a plan that splits the long rows of a CSR pattern
+ * across workgroups.  A banded pattern's global rows ([P3] local+global:
+ * the first and last query blocks select every block) are ten times longer
+ * than the others; walked by one workgroup each they end up alone at the end
+ * of the grid.  A row is heavy when it has more than 2 * chunk entries; its
+ * entries are cut, in order, into ceil(n / chunk) items of at most `chunk`.
+ *
+ * M         blocks (> 0).
+ * row_ptr   host int32[M + 1]: row_ptr of bsa_build_pattern (non-decreasing
+ *           from 0).
+ * chunk     entries per item (> 0), or <= 0 for about one ordinary row: the
+ *           mean row length rounded up to a multiple of 8, at least 8.
+ * heavy     host, caller-owned uint8[M]; written: 1 for a heavy row, else 0.
+ * items     host, caller-owned int32[3 * item_cap]; written: (row, first
+ *           entry, end entry) per item, entries as offsets into col_idx.
+ * item_cap  items' capacity in items (>= 0; nnz always suffices).
+ * n_items   host; required; receives the number of items (also when it
+ *           exceeds item_cap, with BSA_ERR_BUFFER_TOO_SMALL).
+ * rows      host, caller-owned int32[3 * M]; written: (row, first item, item
+ *           count) per heavy row.
+ * n_rows    host; required; receives the number of heavy rows.
+ * Errors: BSA_ERR_NULL_POINTER, BSA_ERR_SHAPE (M <= 0, row_ptr not
+ * non-decreasing from 0, item_cap < 0), BSA_ERR_BUFFER_TOO_SMALL.  Host only,
+ * synchronous.
+ */
+bsa_status bsa_plan_row_split(int32_t M, const int32_t* row_ptr, int32_t chunk, uint8_t* heavy,
+                              int32_t* items, int32_t item_cap, int32_t* n_items, int32_t* rows,
+                              int32_t* n_rows);
+
+/* Bytes of device workspace bsa_forward_split needs for n_items items: one
+ * float32 partial (O, m, l) per (batch, head, item, 32-row wave).  -1 for
+ * invalid arguments. */
+int64_t bsa_row_split_workspace_bytes(int32_t batch, int32_t heads, int32_t block_size,
+                                      int32_t head_dim, int32_t n_items);
+
+/*
+ * bsa_forward_split -- bsa_forward_ex (automatic shape) with the heavy rows of
+ * a bsa_plan_row_split plan spread over workgroups.  Same result as
+ * bsa_forward_ex up to floating-point summation order.  Three launches on
+ * `stream`: the forward over every other row; the plan's items, one
+ * one-block workgroup each, writing partial states to `workspace`; and a
+ * merge that combines each heavy row's partials as the online softmax
+ * combines two key ranges, then writes its O and LSE.  The
+ * call enqueues and returns without synchronising.
+ *
+ * Arguments as bsa_forward_ex (flags: BSA_FORWARD_CAUSAL only; one pattern
+ * for every head), plus device copies of the plan:
+ * heavy     device uint8[M]; items device int32[3 * n_items]; rows device
+ *           int32[3 * n_rows] -- from bsa_plan_row_split of the same row_ptr
+ *           (the kernels read them as given).  n_items == 0 runs bsa_forward.
+ * workspace device, caller-owned, 16-byte aligned, at least
+ *           bsa_row_split_workspace_bytes(batch, heads, block_size,
+ *           head_dim, n_items) bytes; its contents on entry do not matter.
+ * Errors: those of bsa_forward_ex; BSA_ERR_INVALID_ARGUMENT for the per-head
+ * flag; BSA_ERR_SHAPE for inconsistent counts; BSA_ERR_BUFFER_TOO_SMALL for
+ * a short workspace.  Calls that share a workspace must not overlap.
+ */
+bsa_status bsa_forward_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int32_t batch, int32_t heads, int32_t seq_len, int32_t head_dim,
+                             int32_t block_size, int32_t dtype, const int32_t* row_ptr,
+                             const int32_t* col_idx, int64_t nnz, float scale, int32_t flags,
+                             const uint8_t* heavy, const int32_t* items, int32_t n_items,
+                             const int32_t* rows, int32_t n_rows, void* workspace,
+                             int64_t workspace_bytes, void* stream);
+
+/*
  * bsa_transpose_pattern -- the CSC (column-major) form of a CSR pattern.
  *
  * For every K block j, the query blocks whose rows select it, ascending:
@@ -368,7 +434,7 @@ bsa_status bsa_decode_int8kv(const void* q, const int8_t* k_codes, const float* 
 const char* bsa_status_string(int32_t status);
 
 /* ABI version of this header: bump on any incompatible change. */
-#define BSA_ABI_VERSION 3
+#define BSA_ABI_VERSION 4
 int32_t bsa_abi_version(void);
 
 #ifdef __cplusplus

@@ -44,7 +44,7 @@ def test_library_has_gfx950_code_object():
 
 
 def test_abi_version_and_status_strings():
-    assert bsa.abi_version() == 3
+    assert bsa.abi_version() == 4
     for code in range(8):
         assert bsa.status_string(code).startswith("BSA_")
     assert bsa.status_string(99) == "BSA_ERR_UNKNOWN"

@@ -296,3 +296,81 @@ def test_pattern_order_errors():
     assert lib.bsa_pattern_order(2, ptr.ctypes.data_as(p32), out.ctypes.data_as(p32)) == 3
     assert lib.bsa_pattern_order(0, ptr.ctypes.data_as(p32), out.ctypes.data_as(p32)) == 3
     assert lib.bsa_pattern_order(2, None, out.ctypes.data_as(p32)) == 1
+
+
+def _plan_raw(ptr, chunk, item_cap=None):
+    lib = bsa._load()
+    p32 = ctypes.POINTER(ctypes.c_int32)
+    ptr = np.ascontiguousarray(ptr, dtype=np.int32)
+    M = ptr.size - 1
+    cap = int(ptr[-1]) if item_cap is None else item_cap
+    heavy = np.full(M, 7, np.uint8)
+    items = np.zeros(3 * max(cap, 1), np.int32)
+    rows = np.zeros(3 * M, np.int32)
+    n_items, n_rows = ctypes.c_int32(-1), ctypes.c_int32(-1)
+    st = lib.bsa_plan_row_split(M, ptr.ctypes.data_as(p32), chunk,
+                                heavy.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)),
+                                items.ctypes.data_as(p32), cap, ctypes.byref(n_items),
+                                rows.ctypes.data_as(p32), ctypes.byref(n_rows))
+    return st, heavy, items[:3 * max(n_items.value, 0)].reshape(-1, 3), \
+        rows[:3 * max(n_rows.value, 0)].reshape(-1, 3), n_items.value
+
+
+def test_row_split_plan_local_global():
+    # local+global at M = 128: rows 0 and M - 1 hold all 128 blocks, the rest
+    # 7..11 (mean 12.67 -> default chunk 16): two heavy rows of 8 items each
+    M = 128
+    rp, ci = bsa.build_pattern(64 * M, 64, mask=local_global_block_mask(M))
+    plan = bsa.plan_row_split(rp)
+    assert plan.heavy.numpy().nonzero()[0].tolist() == [0, M - 1]
+    assert plan.rows.tolist() == [[0, 0, 8], [M - 1, 8, 8]]
+    r = rp.numpy()
+    want = [[0, r[0] + 16 * i, r[0] + 16 * (i + 1)] for i in range(8)]
+    want += [[M - 1, r[M - 1] + 16 * i, r[M - 1] + 16 * (i + 1)] for i in range(8)]
+    assert plan.items.tolist() == want
+    # every entry of a heavy row lies in exactly one of its items
+    for row, first, count in plan.rows.tolist():
+        its = plan.items[first:first + count].numpy()
+        assert its[0, 1] == r[row] and its[-1, 2] == r[row + 1]
+        assert (its[1:, 1] == its[:-1, 2]).all()
+    # the log-linear pattern has no heavy row
+    assert bsa.plan_row_split(bsa.build_pattern(4096, 32)[0]) is None
+
+
+def test_row_split_plan_boundaries_and_errors():
+    # counts 20, 21, 3 with chunk 10: 20 = 2 chunk is not heavy, 21 is (3 items)
+    ptr = np.cumsum([0, 20, 21, 3])
+    st, heavy, items, rows, n = _plan_raw(ptr, 10)
+    assert st == 0 and heavy.tolist() == [0, 1, 0] and n == 3
+    assert items.tolist() == [[1, 20, 30], [1, 30, 40], [1, 40, 41]]
+    assert rows.tolist() == [[1, 0, 3]]
+    # default chunk: mean 44/3 -> 15 -> 16; nothing exceeds 32
+    st, heavy, items, rows, n = _plan_raw(ptr, 0)
+    assert st == 0 and heavy.tolist() == [0, 0, 0] and n == 0
+    # too few item slots: the count is still reported
+    st, _, _, _, n = _plan_raw(ptr, 10, item_cap=2)
+    assert st == 6 and n == 3
+    lib = bsa._load()
+    p32 = ctypes.POINTER(ctypes.c_int32)
+    bad = np.array([0, 5, 3], np.int32)
+    out8 = np.zeros(2, np.uint8)
+    buf = np.zeros(6, np.int32)
+    cnt = ctypes.c_int32(0)
+    args = lambda ptr_: (2, ptr_.ctypes.data_as(p32), 1,
+                         out8.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)),
+                         buf.ctypes.data_as(p32), 2, ctypes.byref(cnt), buf.ctypes.data_as(p32),
+                         ctypes.byref(cnt))
+    assert lib.bsa_plan_row_split(*args(bad)) == 3
+    a = list(args(np.array([0, 1, 2], np.int32)))
+    a[3] = None
+    assert lib.bsa_plan_row_split(*a) == 1
+
+
+def test_row_split_workspace_bytes():
+    lib = bsa._load()
+    # one float32 partial per (batch, head, item, 32-row wave): d = 128 holds
+    # 4 x 16 registers x 64 lanes + m and l per lane
+    per_wave = (4 * 16 * 64 + 2 * 64) * 4
+    assert lib.bsa_row_split_workspace_bytes(2, 16, 64, 128, 16) == 2 * 16 * 16 * 2 * per_wave
+    assert lib.bsa_row_split_workspace_bytes(1, 1, 32, 64, 3) == 3 * (2 * 16 * 64 + 2 * 64) * 4
+    assert lib.bsa_row_split_workspace_bytes(1, 1, 48, 64, 3) == -1
