@@ -149,3 +149,32 @@ def test_decode_sweep(seed):
     _check(_f64(lse), rl, dtype, "decode LSE " + what)
     _check(_f64(o8), r8, dtype, "int8 decode O " + what)
     _check(_f64(l8), rl8, dtype, "int8 decode LSE " + what)
+
+
+@pytest.mark.parametrize("seed", range(300, 316))
+def test_forward_row_split_sweep(seed):
+    """Random masks with a few dense rows, split with a random chunk size."""
+    c = _draw(seed)
+    rng = np.random.default_rng(seed)
+    dtype, bs, d, B, H = c["dtype"], c["bs"], c["d"], c["B"], c["H"]
+    M = int(rng.integers(6, 20))
+    N = bs * M
+    mask = random_block_mask(M, float(rng.uniform(0.05, 0.4)), seed)
+    for r in rng.choice(M, size=int(rng.integers(1, 4)), replace=False):
+        mask[r, :] = 1
+    causal = c["causal"]
+    rp, ci = bsa.build_pattern(N, bs, mask=mask, causal=causal)
+    chunk = int(rng.integers(1, 9))
+    plan = bsa.plan_row_split(rp, chunk)
+    q, k, v = make_qkv(B, H, N, d, dtype, 4000 + seed)
+    dev = torch.device("cuda")
+    o, lse = bsa.forward(q.to(dev), k.to(dev), v.to(dev), rp.to(dev), ci.to(dev), bs,
+                         c["scale"], causal=causal,
+                         split=None if plan is None else plan.to(dev))
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.block_sparse_attention(_f64(q), _f64(k), _f64(v), mask, bs,
+                                                   c["scale"], causal=causal)
+    what = f"seed {seed}: {c['dtype']} bs{bs} d{d} B{B} H{H} M{M} causal={causal} " \
+           f"chunk={chunk} items={0 if plan is None else plan.n_items}"
+    _check(_f64(o), o_ref, dtype, "O " + what)
+    _check(_f64(lse), lse_ref, dtype, "LSE " + what)
