@@ -164,3 +164,34 @@ def test_quantize_and_int8_decode_host_errors():
         1, FAKE, FAKE, FAKE, o.get("nnz", 1251), f(0.0), o.get("flags", 0), None)
     assert d8(ks=None) == 1 and d8(vs=None) == 1
     assert d8(flags=1) == 2 and d8(nnz=5) == 3
+
+
+def _fwd_split(**over):
+    """bsa_forward_split with a plan of 16 items over 2 heavy rows; every case
+    below fails validation before any HIP call."""
+    lib = bsa._load()
+    need = lib.bsa_row_split_workspace_bytes(1, 8, 32, 64, 16)
+    args = dict(flags=0, heavy=FAKE, items=FAKE, n_items=16, rows=FAKE, n_rows=2, ws=FAKE,
+                ws_bytes=need, nnz=1251)
+    args.update(over)
+    return lib.bsa_forward_split(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 4096, 64, 32, 1, FAKE, FAKE,
+                                 args["nnz"], ctypes.c_float(0.0), args["flags"], args["heavy"],
+                                 args["items"], args["n_items"], args["rows"], args["n_rows"],
+                                 args["ws"], args["ws_bytes"], None)
+
+
+def test_forward_split_rejects_bad_plans():
+    assert _fwd_split(flags=2) == 2                  # one plan cannot serve per-head patterns
+    assert _fwd_split(flags=4) == 2                  # unknown flag
+    assert _fwd_split(n_rows=0) == 3                 # items without heavy rows
+    assert _fwd_split(n_items=-1) == 3
+    assert _fwd_split(n_rows=129) == 3               # more heavy rows than rows
+    assert _fwd_split(n_items=1252) == 3             # more items than entries
+    for field in ("heavy", "items", "rows", "ws"):
+        assert _fwd_split(**{field: None}) == 1
+    assert _fwd_split(ws=FAKE + 4) == 2              # workspace not 16-byte aligned
+    lib = bsa._load()
+    need = lib.bsa_row_split_workspace_bytes(1, 8, 32, 64, 16)
+    assert _fwd_split(ws_bytes=need - 1) == 6        # workspace too small
+    assert lib.bsa_row_split_workspace_bytes(0, 8, 32, 64, 16) == -1
+    assert lib.bsa_row_split_workspace_bytes(1, 8, 32, 96, 16) == -1
