@@ -557,48 +557,57 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
 }
 
 // Finishes the rows split across workgroups: one workgroup per (batch*head,
-// heavy row), one wave per 32 query rows.  rows holds (row, first item, item
-// count) per heavy row; each lane merges the items' partial (O, m, l) as the
-// key slices merge theirs, normalises, and stores O and LSE.
+// heavy row, 32-column tile of O), one wave per 32 query rows.  rows holds
+// (row, first item, item count) per heavy row.  Each lane first reads every
+// item's (m, l) and takes their maximum, then sums the items' tile of O with
+// weights exp2(m_item - m_max): independent loads, not a chain of merges.
 template <typename T, int BS, int D>
 __global__ __launch_bounds__(kWave * (BS / kQRows)) void bsa_fwd_merge_kernel(
     FwdParams p, const int32_t* rows, int32_t n_rows) {
   constexpr int QW = BS / kQRows;
   constexpr int kPF = partial_bytes<D>() / 4;
-  __shared__ __attribute__((aligned(16))) unsigned char stage[QW][kQRows * D * sizeof(T)];
+  constexpr int kTiles = D / 32;
+  __shared__ __attribute__((aligned(16))) unsigned char stage[QW][kQRows * 32 * sizeof(T)];
   const int lane = threadIdx.x & (kWave - 1);
   const int qg = uniform(threadIdx.x / kWave);
-  const int bh = blockIdx.x / n_rows;
-  const int hr = blockIdx.x % n_rows;
+  const int dt = blockIdx.x % kTiles;
+  const int hr = (blockIdx.x / kTiles) % n_rows;
+  const int bh = blockIdx.x / (kTiles * n_rows);
   const int row = rows[3 * hr], first = rows[3 * hr + 1], count = rows[3 * hr + 2];
-  f32x16_t o[D / 32];
+  const float* base = p.partial + ((size_t)bh * p.n_items + first) * QW * kPF + (size_t)qg * kPF;
+  const size_t item_stride = (size_t)QW * kPF;
+  float m_max = -INFINITY;
+  for (int c = 0; c < count; ++c)
+    m_max = fmaxf(m_max, base[c * item_stride + kTiles * 16 * kWave + lane]);
+  f32x16_t o[kTiles];  // only tile dt is summed; the others stay zero
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16_t{};
-  float m2 = -INFINITY, lsum = 0.f;
-  for (int c = 0; c < count; ++c) {
-    const float* src = p.partial + ((size_t)bh * p.n_items + first + c) * QW * kPF +
-                       (size_t)qg * kPF;
-    const float mo = src[(D / 32) * 16 * kWave + lane];
-    const float lo = src[(D / 32) * 16 * kWave + kWave + lane];
-    const float m_new = fmaxf(m2, mo);
-    if (m_new == -INFINITY) continue;  // neither side has seen a key yet
-    const float a_self = fast_exp2(m2 - m_new);
-    const float a_other = fast_exp2(mo - m_new);
-    lsum = lsum * a_self + lo * a_other;
+  for (int t = 0; t < kTiles; ++t) o[t] = f32x16_t{};
+  float lsum = 0.f;
+  if (m_max != -INFINITY) {  // else no item has seen a key: O = 0, LSE = -inf
+    f32x16_t acc = f32x16_t{};
+#pragma unroll 4
+    for (int c = 0; c < count; ++c) {
+      const float* src = base + c * item_stride;
+      const float w = fast_exp2(src[kTiles * 16 * kWave + lane] - m_max);
+      lsum = fmaf(w, src[kTiles * 16 * kWave + kWave + lane], lsum);
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+      for (int r = 0; r < 16; ++r) acc[r] = fmaf(w, src[(dt * 16 + r) * kWave + lane], acc[r]);
+    }
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        o[dt][r] = o[dt][r] * a_self + src[(dt * 16 + r) * kWave + lane] * a_other;
-    m2 = m_new;
+    for (int t = 0; t < kTiles; ++t)
+      if (t == dt) o[t] = acc;
   }
   const float l_all = halves_sum(lsum);
   const float inv = l_all > 0.f ? 1.f / l_all : 0.f;
   const int q0 = row * BS + qg * kQRows;
-  store_rows_lds<T, D>(static_cast<T*>(p.o) + (size_t)bh * p.N * D + (size_t)q0 * D, o, inv,
-                       lane, (LDS_PTR(unsigned char))stage[qg]);
-  if (p.lse != nullptr && (lane >> 5) == 0) {
-    const float lse2 = l_all > 0.f ? m2 + log2f(l_all) : -INFINITY;
+  T* const dst = static_cast<T*>(p.o) + (size_t)bh * p.N * D + (size_t)q0 * D;
+  LDS_PTR(unsigned char) st = (LDS_PTR(unsigned char))stage[qg];
+  if (dt == 0) store_cols_lds<T, D, 0, 1>(dst, o, inv, lane, st);
+  if constexpr (kTiles > 1) if (dt == 1) store_cols_lds<T, D, 1, 1>(dst, o, inv, lane, st);
+  if constexpr (kTiles > 2) if (dt == 2) store_cols_lds<T, D, 2, 1>(dst, o, inv, lane, st);
+  if constexpr (kTiles > 3) if (dt == 3) store_cols_lds<T, D, 3, 1>(dst, o, inv, lane, st);
+  if (dt == 0 && p.lse != nullptr && (lane >> 5) == 0) {
+    const float lse2 = l_all > 0.f ? m_max + log2f(l_all) : -INFINITY;
     p.lse[(size_t)bh * p.N + q0 + (lane & 31)] = lse2 * 0.69314718055994530942f;
   }
 }
@@ -857,7 +866,7 @@ bsa_status forward_impl(const void* q, const void* k, const void* v, void* o, fl
   r = dtype == BSA_DTYPE_F32 ? dispatch<float>(ps, block_size, head_dim, st)
                              : dispatch<__bf16>(ps, block_size, head_dim, st);
   if (r != BSA_OK) return r;
-  const int64_t grid = (int64_t)batch * heads * plan->n_rows;
+  const int64_t grid = (int64_t)batch * heads * plan->n_rows * (head_dim / 32);
   return dtype == BSA_DTYPE_F32
              ? dispatch_merge<float>(ps, block_size, head_dim, plan->rows, plan->n_rows, grid, st)
              : dispatch_merge<__bf16>(ps, block_size, head_dim, plan->rows, plan->n_rows, grid, st);
