@@ -4,6 +4,8 @@
 
 The host pattern builder is plain C++ (g++); the kernels and their entry
 points (forward.hip, backward.hip, decode.hip) are HIP (hipcc --offload-arch=gfx950).
+Then tests/c/bsa_c_forward.c, a plain C program that drives the library
+through its C ABI, is compiled with gcc and linked against it (``C_DEMO``).
 Every build recompiles.
 """
 
@@ -20,10 +22,14 @@ INCLUDE = os.path.join(ROOT, "include")
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libbsa.so")
+C_DEMO_SRC = os.path.join(ROOT, "tests", "c", "bsa_c_forward.c")
+C_DEMO = os.path.join(PKG, "bsa_c_forward")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CXX = os.environ.get("CXX", "g++")
+CC = os.environ.get("CC", "gcc")
 
 # Packed fp32 VALU instructions are switched off for all device code.
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
@@ -61,6 +67,10 @@ def build(verbose: bool = False, extra_hip_flags=None) -> str:
     _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", pattern_o, *objs, "-o", tmp],
          verbose)
     shutil.move(tmp, LIB)
+    _run([CC, "-O2", "-std=c11", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+          f"-I{INCLUDE}", f"-I{ROCM}/include", C_DEMO_SRC, "-o", C_DEMO, f"-L{PKG}",
+          "-l:libbsa.so", f"-L{ROCM}/lib", "-lamdhip64",
+          f"-Wl,-rpath,$ORIGIN:{ROCM}/lib"], verbose)
     return LIB
 
 
