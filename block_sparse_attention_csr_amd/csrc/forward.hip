@@ -174,6 +174,18 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
   const T* K = static_cast<const T*>(p.k) + head;
   const T* V = static_cast<const T*>(p.v) + head;
 
+  // Several query blocks per workgroup: the loading wave of each block reads
+  // the first 64 entries of its CSR row (one per lane) before any Q load.
+  // The union is built from them, and the vector-memory counter drains in
+  // order, so issued after Q they would wait for all of Q first.
+  const bool loads_row = G > 1 && has_rows && qg == 0 && ks == 0;
+  int row_s = 0, row_e = 0, row_first = -1;
+  if (loads_row) {
+    row_s = row_ptr[qb];
+    row_e = row_ptr[qb + 1];
+    if (row_s + lane < row_e) row_first = p.col_idx[row_s + lane];
+  }
+
   typename O::template QOperand<D> qop;
   const int q0 = (has_rows ? qb : 0) * BS + qg * kQRows;
   // bf16, one query block per workgroup: the wave's 32 Q rows come in as
@@ -222,16 +234,17 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
   } else {
     for (int i = threadIdx.x; i < (G + 1) * MW; i += blockDim.x) bitmap[i] = 0;
     __syncthreads();
-    if (has_rows && qg == 0 && ks == 0) {
-      const int rs = row_ptr[qb];
-      const int re = row_ptr[qb + 1];
-      for (int t = rs + lane; t < re; t += kWave) {
-        const int j = p.col_idx[t];
+    if (loads_row) {
+      auto mark = [&](int j) {
         if (j >= 0 && j < M && (!causal || j <= qb)) {
           atomicOr(&bitmap[j >> 5], 1u << (j & 31));
           atomicOr(&bitmap[(1 + g) * MW + (j >> 5)], 1u << (j & 31));
         }
-      }
+      };
+      if (row_s + lane < row_e) mark(row_first);
+      // entries past the first 64 (long rows only: no load, and no wait on
+      // the Q loads, for the others)
+      for (int t = row_s + kWave + lane; t < row_e; t += kWave) mark(p.col_idx[t]);
     }
     __syncthreads();
     if (wave == 0) {  // ascending list of the union's blocks
