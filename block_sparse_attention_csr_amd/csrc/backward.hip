@@ -143,12 +143,27 @@ __device__ __forceinline__ float operand_dot(const typename Ops<T>::template QOp
 
 // Copies a CSR row / CSC column into the LDS entry list (wave 0) and returns
 // its length; the caller synchronises.
-__device__ __forceinline__ int load_list(int32_t* list, const int32_t* idx, int start, int end,
-                                         int wave, int lane) {
-  const int n = end - start;
-  if (wave == 0)
-    for (int t = lane; t < n; t += kWave) list[t] = idx[start + t];
-  return n;
+// A workgroup's list (CSR row or CSC column) in LDS, written by wave 0.  The
+// first 64 entries are loaded (`list_head`, one per lane) before the
+// operand loads and written after them (`list_store`): the vector-memory
+// counter drains in order, so loaded after the operands the list would wait
+// for all of them first.
+struct ListHead {
+  int start, n, first;
+};
+__device__ __forceinline__ ListHead list_head(const int32_t* idx, int start, int end, int wave,
+                                              int lane) {
+  ListHead h{start, end - start, -1};
+  if (wave == 0 && lane < h.n) h.first = idx[start + lane];
+  return h;
+}
+__device__ __forceinline__ int list_store(int32_t* list, const int32_t* idx, const ListHead& h,
+                                          int wave, int lane) {
+  if (wave == 0) {
+    if (lane < h.n) list[lane] = h.first;
+    for (int t = kWave + lane; t < h.n; t += kWave) list[t] = idx[h.start + t];
+  }
+  return h.n;
 }
 
 // ---------------------------------------------------------------- dQ (and D)
@@ -176,13 +191,14 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 0>::W)) void bsa_bwd_dq(B
   const int q0 = qb * BS + wave * kQRows;
   const int row = q0 + (lane & 31);
 
+  const ListHead lh = list_head(p.col_idx, p.row_ptr[qb], p.row_ptr[qb + 1], wave, lane);
   typename O::template QOperand<D> qop, dop, oop;
   O::template load_q<D>(qop, static_cast<const T*>(p.q) + head + (size_t)q0 * D, lane);
   O::template load_q<D>(dop, static_cast<const T*>(p.dout) + head + (size_t)q0 * D, lane);
   O::template load_q<D>(oop, static_cast<const T*>(p.o) + head + (size_t)q0 * D, lane);
   const float lse2 = p.lse[(size_t)bh * p.N + row] * kLog2e;
 
-  const int U = load_list(list, p.col_idx, p.row_ptr[qb], p.row_ptr[qb + 1], wave, lane);
+  const int U = list_store(list, p.col_idx, lh, wave, lane);
   __syncthreads();
 
   // D for this lane's row; the lane half h = 0 stores it for bsa_bwd_dkv.
@@ -326,11 +342,12 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 8 * BS>::W)) void bsa_bwd
   const float* del_h = p.delta + (size_t)bh * p.N;
   const int k0 = kb * BS + wave * kQRows;
 
+  const ListHead lh = list_head(p.row_idx, p.col_ptr[kb], p.col_ptr[kb + 1], wave, lane);
   typename O::template QOperand<D> kop, vop;
   O::template load_q<D>(kop, static_cast<const T*>(p.k) + head + (size_t)k0 * D, lane);
   O::template load_q<D>(vop, static_cast<const T*>(p.v) + head + (size_t)k0 * D, lane);
 
-  const int U = load_list(list, p.row_idx, p.col_ptr[kb], p.col_ptr[kb + 1], wave, lane);
+  const int U = list_store(list, p.row_idx, lh, wave, lane);
   __syncthreads();
 
   int chunk_base = -kWave, chunk = -1;
