@@ -141,13 +141,11 @@ __device__ __forceinline__ float operand_dot(const typename Ops<T>::template QOp
   return s;
 }
 
-// Copies a CSR row / CSC column into the LDS entry list (wave 0) and returns
-// its length; the caller synchronises.
-// A workgroup's list (CSR row or CSC column) in LDS, written by wave 0.  The
-// first 64 entries are loaded (`list_head`, one per lane) before the
-// operand loads and written after them (`list_store`): the vector-memory
-// counter drains in order, so loaded after the operands the list would wait
-// for all of them first.
+// A workgroup's list (CSR row or CSC column) in LDS, written by wave 0;
+// `list_store` returns its length and the caller synchronises.  The first 64
+// entries are loaded (`list_head`, one per lane) before the operand loads and
+// written after them: the vector-memory counter drains in order, so loaded
+// after the operands the list would wait for all of them first.
 struct ListHead {
   int start, n, first;
 };
