@@ -186,6 +186,22 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
     if (row_s + lane < row_e) row_first = p.col_idx[row_s + lane];
   }
 
+  // One query block per workgroup: the row's bounds, read before the Q
+  // copies below.  Read after them, these uniform loads could not go through
+  // the scalar cache (the copies' asm may write memory), and each vector load
+  // would wait for the Q copies as well (the counter drains in order).
+  int rs = 0;     // G == 1: the row's first entry in col_idx
+  int row_n = 0;  // G == 1: its entry count
+  if constexpr (G == 1) {
+    if (item >= 0) {  // the item's entries of its row
+      rs = p.split[3 * item + 1];
+      row_n = p.split[3 * item + 2] - rs;
+    } else {
+      rs = row_ptr[grp];
+      row_n = has_rows ? row_ptr[grp + 1] - rs : 0;
+    }
+  }
+
   typename O::template QOperand<D> qop;
   const int q0 = (has_rows ? qb : 0) * BS + qg * kQRows;
   // bf16, one query block per workgroup: the wave's 32 Q rows come in as
@@ -220,17 +236,10 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
   uint32_t* bitmap = reinterpret_cast<uint32_t*>(dyn + M);    // [(G + 1) * MW] (G > 1)
   const uint32_t* my_row = bitmap + (1 + g) * MW;
   int U;
-  int rs = 0;  // G == 1: the row's first entry in col_idx
   if constexpr (G == 1) {
     // Every wave reads the row from col_idx itself (64 entries at a time, in
     // entry_at): no LDS list and no barrier before the first copy.
-    if (item >= 0) {  // the item's entries of its row
-      rs = p.split[3 * item + 1];
-      U = p.split[3 * item + 2] - rs;
-    } else {
-      rs = row_ptr[grp];
-      U = has_rows ? row_ptr[grp + 1] - rs : 0;
-    }
+    U = row_n;
   } else {
     for (int i = threadIdx.x; i < (G + 1) * MW; i += blockDim.x) bitmap[i] = 0;
     __syncthreads();
