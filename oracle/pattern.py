@@ -225,36 +225,38 @@ def block_mask_from_csr(row_ptr, col_idx, M: int) -> np.ndarray:
 
 
 def local_global_token_mask(seq_len: int, local_window: int, global_tokens) -> np.ndarray:
-    """Token-level [N, N] bool mask: local window plus global tokens.
+    """Token-level [N, N] bool mask of the local + global rule.
 
-    [P3] "sparse pattern: Local + Global": token i sees tokens
-    [i - local_window, i + local_window] (clipped to the sequence); each global
-    token g sees every position (row g) and is seen by every position
-    (column g).  Negative global indices count from the end.
+    [P3] "sparse pattern: Local + Global" states the rule: a token attends to
+    every token at distance at most ``local_window`` from it, and a global
+    token both attends to and is attended by every position.  Here the band
+    is the set {(i, j) : |i - j| <= local_window}, formed by comparing the
+    row and column position vectors; each global token then sets its whole
+    row and column.  Negative global indices count from the end.
     """
-    mask = np.zeros((seq_len, seq_len), dtype=bool)
-    for i in range(seq_len):
-        start = max(0, i - local_window)
-        end = min(seq_len, i + local_window + 1)
-        mask[i, start:end] = True
-    for g in global_tokens:
-        g = int(g) % seq_len
-        mask[g, :] = True
-        mask[:, g] = True
+    pos = np.arange(seq_len)
+    mask = np.abs(pos[:, None] - pos[None, :]) <= local_window
+    rows = np.asarray([int(g) % seq_len for g in global_tokens], dtype=np.int64)
+    mask[rows, :] = True
+    mask[:, rows] = True
     return mask
 
 
 def token_mask_to_block_mask(token_mask: np.ndarray, block_size: int) -> np.ndarray:
-    """[P3] "Block-Sparse": a block is computed when more than half of its
-    token pairs are set.  The block count rounds up; a partial last block is
-    averaged over the tokens it has."""
-    seq_len = token_mask.shape[0]
-    num_blocks = (seq_len + block_size - 1) // block_size
-    out = np.zeros((num_blocks, num_blocks), dtype=np.uint8)
-    for i in range(num_blocks):
-        for j in range(num_blocks):
-            tile = token_mask[i * block_size:(i + 1) * block_size,
-                              j * block_size:(j + 1) * block_size]
-            if tile.mean() > 0.5:
-                out[i, j] = 1
-    return out
+    """Block mask of a token mask under the more-than-half rule.
+
+    [P3] "Block-Sparse": a (query block, key block) tile is computed when more
+    than half of its token pairs are set.  The token mask is padded with unset
+    entries up to a whole number of blocks, reshaped to
+    [blocks, block_size, blocks, block_size], and the set pairs of each tile
+    are counted; a tile is kept when twice its count exceeds the number of
+    real token pairs it covers (a partial last block covers fewer).
+    """
+    n = token_mask.shape[0]
+    nb = -(-n // block_size)
+    padded = np.zeros((nb * block_size, nb * block_size), dtype=np.int64)
+    padded[:n, :n] = token_mask
+    counts = padded.reshape(nb, block_size, nb, block_size).sum(axis=(1, 3))
+    extent = np.minimum(block_size, n - block_size * np.arange(nb))  # tokens per block
+    pairs = extent[:, None] * extent[None, :]
+    return (2 * counts > pairs).astype(np.uint8)

@@ -171,6 +171,25 @@ def test_local_global_token_to_block(golden):
     assert lg[0].all() and lg[-1].all() and lg[:, 0].all() and lg[:, -1].all()
 
 
+def test_token_to_block_partial_last_block():
+    # N = 100 at block 64: the last block holds 36 tokens, so its diagonal tile
+    # covers 36 * 36 = 1296 real pairs.  A band of half-width w sets
+    # 36 + 2 * sum_{t=1..w} (36 - t) of them: 646 at w = 10 (2 * 646 < 1296,
+    # dropped) and 696 at w = 11 (kept).  The first diagonal tile sets
+    # 64 + 2 * sum_{t=1..w} (64 - t) = 1340 of 4096 at w = 11 (dropped), and
+    # the off-diagonal tiles at most 66 of 2304.
+    tm10 = local_global_token_mask(100, 10, [])
+    tm11 = local_global_token_mask(100, 11, [])
+    assert int(tm11[64:, 64:].sum()) == 696 and int(tm10[64:, 64:].sum()) == 646
+    assert int(tm11[:64, :64].sum()) == 1340 and int(tm11[:64, 64:].sum()) == 66
+    assert np.array_equal(token_mask_to_block_mask(tm10, 64), np.zeros((2, 2), np.uint8))
+    assert np.array_equal(token_mask_to_block_mask(tm11, 64), np.array([[0, 0], [0, 1]], np.uint8))
+    # a global token sets its whole row and column, negative indices from the end
+    g = local_global_token_mask(100, 0, [0, -1])
+    assert g[0].all() and g[:, 0].all() and g[99].all() and g[:, 99].all()
+    assert int(g.sum()) == 100 + 4 * 98 + 2
+
+
 # ----------------------------------------------------------------------------- attention
 
 
