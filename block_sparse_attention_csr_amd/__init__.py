@@ -270,6 +270,16 @@ def plan_row_split(row_ptr, chunk: int = 0):
                         torch.from_numpy(rows[:3 * n_rows.value].reshape(-1, 3).copy()))
 
 
+def _on_stream(stream):
+    """Context in which new tensors belong to ``stream`` in torch's caching
+    allocator.  A buffer allocated on another stream and dropped when the
+    call returns (a workspace, ``delta``) could otherwise be handed to new
+    work while the kernels enqueued on ``stream`` still use it."""
+    import torch
+
+    return torch.cuda.stream(stream)
+
+
 def _check_buffer(t, name, shape, dtype, device):
     """A caller-supplied device buffer: the library writes or reads it through
     a raw pointer, so its size, type and place are checked here."""
@@ -343,16 +353,18 @@ def forward(q, k, v, row_ptr, col_idx, block_size: int, scale: float | None = No
         nnz = col_idx.numel()
     _check_csr(row_ptr, col_idx, q.device, _pattern_rows(N, int(block_size), H, per_head),
                int(nnz))
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
     if out is None:
-        out = torch.empty_like(q)
+        with _on_stream(stream):
+            out = torch.empty_like(q)
     else:
         _check_buffer(out, "out", q.shape, q.dtype, q.device)
     if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        with _on_stream(stream):
+            lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     else:
         _check_buffer(lse, "lse", (B, H, N), torch.float32, q.device)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
     lib = _load()
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N,
             d, int(block_size), _dtype_code(q), row_ptr.data_ptr(), col_idx.data_ptr(),
@@ -369,7 +381,8 @@ def forward(q, k, v, row_ptr, col_idx, block_size: int, scale: float | None = No
         if need < 0:
             raise ValueError("unsupported shape for a row-split plan")
         if workspace is None:
-            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+            with _on_stream(stream):
+                workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
         elif (not workspace.is_cuda or workspace.device != q.device
               or not workspace.is_contiguous() or workspace.numel() * workspace.element_size() < need):
             raise ValueError(f"workspace must be a contiguous tensor of >= {need} bytes on {q.device}")
@@ -455,15 +468,16 @@ def backward(q, k, v, o, lse, dout, row_ptr, col_idx, col_ptr, row_idx, block_si
     for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
         if t is not None:
             _check_buffer(t, name, q.shape, q.dtype, q.device)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(q) if dk is None else dk
-    dv = torch.empty_like(q) if dv is None else dv
-    if delta is None:
-        delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    else:
-        _check_buffer(delta, "delta", (B, H, N), torch.float32, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
+    with _on_stream(stream):
+        dq = torch.empty_like(q) if dq is None else dq
+        dk = torch.empty_like(q) if dk is None else dk
+        dv = torch.empty_like(q) if dv is None else dv
+        if delta is None:
+            delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        else:
+            _check_buffer(delta, "delta", (B, H, N), torch.float32, q.device)
     st = _load().bsa_backward(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, N, d,
@@ -478,8 +492,10 @@ def backward(q, k, v, o, lse, dout, row_ptr, col_idx, col_ptr, row_idx, block_si
     return dq, dk, dv
 
 
-def _decode_common(q, seqlens, row_ptr, col_idx, n_cap, block_size, per_head, nnz, out, lse):
-    """Checks shared by the decode entry points; returns (out, lse)."""
+def _decode_common(q, seqlens, row_ptr, col_idx, n_cap, block_size, per_head, nnz, out, lse,
+                   stream):
+    """Checks shared by the decode entry points; returns (out, lse), new ones
+    allocated on ``stream``."""
     import torch
 
     B, H, d = q.shape
@@ -488,11 +504,13 @@ def _decode_common(q, seqlens, row_ptr, col_idx, n_cap, block_size, per_head, nn
         raise ValueError(f"seqlens must be a contiguous int32 tensor of {B} entries on {q.device}")
     _check_csr(row_ptr, col_idx, q.device, _pattern_rows(n_cap, block_size, H, per_head), nnz)
     if out is None:
-        out = torch.empty_like(q)
+        with _on_stream(stream):
+            out = torch.empty_like(q)
     else:
         _check_buffer(out, "out", q.shape, q.dtype, q.device)
     if lse is None:
-        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+        with _on_stream(stream):
+            lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
     else:
         _check_buffer(lse, "lse", (B, H), torch.float32, q.device)
     return out, lse
@@ -527,10 +545,10 @@ def decode(q, k_cache, v_cache, seqlens, row_ptr, col_idx, block_size: int,
     n_cap = k_cache.shape[2]
     if nnz is None:
         nnz = col_idx.numel()
-    out, lse = _decode_common(q, seqlens, row_ptr, col_idx, n_cap, int(block_size), per_head,
-                              int(nnz), out, lse)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
+    out, lse = _decode_common(q, seqlens, row_ptr, col_idx, n_cap, int(block_size), per_head,
+                              int(nnz), out, lse, stream)
     st = _load().bsa_decode(
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(), lse.data_ptr(),
         B, H, n_cap, d, int(block_size), _dtype_code(q), seqlens.data_ptr(),
@@ -549,16 +567,18 @@ def quantize_kv(x, block_size: int, *, codes=None, scales=None, stream=None):
     if not x.is_cuda or not x.is_contiguous() or x.dim() != 4:
         raise ValueError("x must be a contiguous CUDA tensor [B, H, N, d]")
     B, H, N, d = x.shape
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
     if codes is None:
-        codes = torch.empty(x.shape, dtype=torch.int8, device=x.device)
+        with _on_stream(stream):
+            codes = torch.empty(x.shape, dtype=torch.int8, device=x.device)
     else:
         _check_buffer(codes, "codes", x.shape, torch.int8, x.device)
     if scales is None:
-        scales = torch.empty((B, H, N // block_size), dtype=torch.float32, device=x.device)
+        with _on_stream(stream):
+            scales = torch.empty((B, H, N // block_size), dtype=torch.float32, device=x.device)
     else:
         _check_buffer(scales, "scales", (B, H, N // block_size), torch.float32, x.device)
-    if stream is None:
-        stream = torch.cuda.current_stream(x.device)
     st = _load().bsa_quantize_kv(x.data_ptr(), codes.data_ptr(), scales.data_ptr(), B, H, N, d,
                                  int(block_size), _dtype_code(x), stream.cuda_stream)
     if st != BSA_OK:
@@ -590,10 +610,10 @@ def decode_int8kv(q, k_codes, k_scales, v_codes, v_scales, seqlens, row_ptr, col
         _check_buffer(t, name, (B, H, n_cap // block_size), torch.float32, q.device)
     if nnz is None:
         nnz = col_idx.numel()
-    out, lse = _decode_common(q, seqlens, row_ptr, col_idx, n_cap, int(block_size), per_head,
-                              int(nnz), out, lse)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
+    out, lse = _decode_common(q, seqlens, row_ptr, col_idx, n_cap, int(block_size), per_head,
+                              int(nnz), out, lse, stream)
     st = _load().bsa_decode_int8kv(
         q.data_ptr(), k_codes.data_ptr(), k_scales.data_ptr(), v_codes.data_ptr(),
         v_scales.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, n_cap, d, int(block_size),

@@ -760,9 +760,28 @@ size_t lds_for(int dtype, int bs, int d, int group, int ks, int M) {
 // over KS key-slice wave sets while the grid stays within two waves per SIMD
 // (the worked example, 1024 query blocks of one wave, runs 9.2 us with KS = 2
 // against 9.8 us with KS = 1).
+// Compute units of the current device (read once per device; 256 on an
+// MI355X, the figure used if the query fails).
+int64_t device_cus() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = -1;
+  if (dev >= 0) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) !=
+          hipSuccess ||
+      n <= 0)
+    n = 256;
+  if (dev >= 0) cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 void choose_shape(int64_t bhm, int bs, int d, int dtype, int M, int* group, int* key_split) {
-  constexpr int64_t kCus = 256;
-  constexpr int64_t kLargeGrid = 8 * 4 * kCus;  // 8 query waves per SIMD
+  const int64_t kCus = device_cus();
+  const int64_t kLargeGrid = 8 * 4 * kCus;  // 8 query waves per SIMD
   const int qw = bs / kQRows;
   auto fits = [&](int g, int ks) {
     const size_t b = lds_for(dtype, bs, d, g, ks, M);

@@ -92,3 +92,47 @@ def test_decode_and_quantiser_reject_bad_buffers(dev):
     od, ld = bsa.decode_int8kv(q, k8, ks, v8, vs, sl, rp, ci, bs)
     torch.cuda.synchronize()
     assert torch.isfinite(od.float()).all() and torch.isfinite(ld).all()
+
+
+def test_side_stream_scratch_is_not_reused_early(dev):
+    """forward(split=...) and backward enqueued on a side stream while the
+    current stream keeps allocating and writing: the binding allocates the
+    row-split workspace, delta and the outputs on the side stream, so the
+    caching allocator cannot hand them to the current stream's work while the
+    side stream's kernels still use them.  Results match the oracle."""
+    import numpy as np
+
+    import oracle
+    from synthetic_inputs import local_global_block_mask
+
+    B, H, M, bs, d = 2, 2, 16, 64, 128
+    N = M * bs
+    mask = local_global_block_mask(M)
+    q, k, v = make_qkv(B, H, N, d, torch.bfloat16, 5)
+    g = make_qkv(B, H, N, d, torch.bfloat16, 6)[0]
+    rp, ci = bsa.build_pattern(N, bs, mask=mask)
+    cp, ri = bsa.transpose_pattern(rp, ci)
+    plan = bsa.plan_row_split(rp, 4)
+    assert plan is not None
+    qd, kd, vd, gd = (t.to(dev) for t in (q, k, v, g))
+    rpd, cid, cpd, rid = (t.to(dev) for t in (rp, ci, cp, ri))
+    pland = plan.to(dev)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    # hold the side stream so its kernels are still queued when the
+    # function returns and the temporaries it allocated are dropped
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(int(5e7))
+    o, lse = bsa.forward(qd, kd, vd, rpd, cid, bs, split=pland, stream=side)
+    dq, dk, dv = bsa.backward(qd, kd, vd, o, lse, gd, rpd, cid, cpd, rid, bs, stream=side)
+    # the current stream meanwhile allocates and overwrites fresh memory
+    junk = [torch.full((1 << 20,), float("nan"), device=dev) for _ in range(64)]
+    torch.cuda.synchronize()
+    del junk
+    f = lambda t: t.float().cpu().numpy().astype(np.float64)
+    o_ref, lse_ref = oracle.block_sparse_attention(f(q), f(k), f(v), mask, bs)
+    assert np.abs(f(o) - o_ref).max() <= 2e-2 and np.abs(f(lse) - lse_ref).max() <= 2e-2
+    ref = oracle.block_sparse_attention_backward(f(q), f(k), f(v), f(g), mask, bs)
+    for got, want in zip((dq, dk, dv), ref[:3]):
+        assert np.abs(f(got) - want).max() <= 2e-2 * max(1.0, float(np.abs(want).max()))

@@ -18,6 +18,7 @@ import torch
 
 import block_sparse_attention_csr_amd as bsa
 import oracle
+from workgroup_shapes import refused_cases, runnable_cases
 from synthetic_inputs import (WORKLOADS, local_global_block_mask, make_qkv, random_block_mask,
                               workload_block_mask)
 
@@ -228,17 +229,11 @@ def test_nan_propagates_only_to_rows_that_see_it():
             assert np.isfinite(rows).all(), qb
 
 
-SHAPES = [(1, 1), (1, 2), (1, 4), (1, 8), (2, 1), (2, 2), (2, 4), (4, 1), (4, 2)]
-
-
-@pytest.mark.parametrize("group,key_split", SHAPES)
-@pytest.mark.parametrize("dt,bs,d", [(dt, bs, d) for dt in ("bf16", "f32") for bs in (32, 64)
-                                     for d in (64, 128)])
+@pytest.mark.parametrize("dt,bs,d,group,key_split", runnable_cases())
 def test_every_workgroup_shape(dt, bs, d, group, key_split):
-    """bsa_forward_ex: every (group, key_split) computes the oracle's result,
-    on a ragged case (M = 11 query blocks is a multiple of no group size)."""
-    if (bs // 32) * group * key_split > 8:
-        pytest.skip("more than 8 waves per workgroup")
+    """bsa_forward_ex: every (group, key_split) the library runs computes the
+    oracle's result, on a ragged case (M = 11 query blocks is a multiple of no
+    group size)."""
     dtype = torch.bfloat16 if dt == "bf16" else torch.float32
     B, H, M = 2, 3, 11
     N = bs * M
@@ -246,26 +241,38 @@ def test_every_workgroup_shape(dt, bs, d, group, key_split):
     mask = random_block_mask(M, 0.35, 17)
     dev = torch.device("cuda")
     rp, ci = bsa.build_pattern(N, bs, mask=mask)
-    try:
-        o, lse = bsa.forward(q.to(dev), k.to(dev), v.to(dev), rp.to(dev), ci.to(dev), bs,
-                             group=group, key_split=key_split)
-    except bsa.BsaError as e:
-        assert e.status == 2
-        pytest.skip(f"shape needs more LDS than a workgroup has: {e}")
+    o, lse = bsa.forward(q.to(dev), k.to(dev), v.to(dev), rp.to(dev), ci.to(dev), bs,
+                         group=group, key_split=key_split)
     torch.cuda.synchronize()
     o_ref, lse_ref = oracle.block_sparse_attention(_f64(q), _f64(k), _f64(v), mask, bs)
     _compare(_f64(o), _f64(lse), o_ref, lse_ref, dtype, f"{dt} bs{bs} d{d} G{group} KS{key_split}")
 
 
-@pytest.mark.parametrize("group,key_split", SHAPES)
-@pytest.mark.parametrize("dt,bs,d", [("bf16", 32, 64), ("f32", 64, 128), ("bf16", 64, 128)])
+@pytest.mark.parametrize("dt,bs,d,group,key_split", refused_cases())
+def test_refused_workgroup_shapes(dt, bs, d, group, key_split):
+    """Shapes that are not instantiated, or whose LDS ring does not fit a
+    workgroup, are refused with BSA_ERR_INVALID_ARGUMENT (status 2) before any
+    launch; so are shapes of more than 8 waves."""
+    dtype = torch.bfloat16 if dt == "bf16" else torch.float32
+    B, H, M = 1, 1, 11
+    N = bs * M
+    q, k, v = make_qkv(B, H, N, d, dtype, 17)
+    dev = torch.device("cuda")
+    rp, ci = bsa.build_pattern(N, bs)
+    for g, ks in ((group, key_split), (8, 2)):
+        with pytest.raises(bsa.BsaError) as e:
+            bsa.forward(q.to(dev), k.to(dev), v.to(dev), rp.to(dev), ci.to(dev), bs,
+                        group=g, key_split=ks)
+        assert e.value.status == 2
+
+
+@pytest.mark.parametrize("dt,bs,d,group,key_split",
+                         runnable_cases([("bf16", 32, 64), ("f32", 64, 128), ("bf16", 64, 128)]))
 def test_hand_made_csr_empty_rows_and_out_of_range_entries(dt, bs, d, group, key_split):
     """A CSR not from bsa_build_pattern: a row with no entry and a row with
     only entries outside [0, M) get O = 0 and LSE = -inf (no NaN, the failure
     the log-linear page traces to empty rows); entries outside [0, M) inside a
     row are skipped; every other row matches the oracle."""
-    if (bs // 32) * group * key_split > 8:
-        pytest.skip("more than 8 waves per workgroup")
     dtype = torch.bfloat16 if dt == "bf16" else torch.float32
     B, H, M = 2, 2, 11
     N = bs * M
@@ -278,12 +285,8 @@ def test_hand_made_csr_empty_rows_and_out_of_range_entries(dt, bs, d, group, key
     ci = torch.tensor([j for r in rows for j in r], dtype=torch.int32)
     q, k, v = make_qkv(B, H, N, d, dtype, 29)
     dev = torch.device("cuda")
-    try:
-        o, lse = bsa.forward(q.to(dev), k.to(dev), v.to(dev), rp.to(dev), ci.to(dev), bs,
-                             group=group, key_split=key_split)
-    except bsa.BsaError as e:
-        assert e.status == 2
-        pytest.skip(f"shape needs more LDS than a workgroup has: {e}")
+    o, lse = bsa.forward(q.to(dev), k.to(dev), v.to(dev), rp.to(dev), ci.to(dev), bs,
+                         group=group, key_split=key_split)
     torch.cuda.synchronize()
     o, lse = _f64(o), _f64(lse)
     eff = np.zeros((M, M), np.uint8)
