@@ -23,7 +23,7 @@ __all__ = [
     "BsaError", "build_pattern", "forward", "backward", "transpose_pattern", "status_string",
     "abi_version", "library_path", "PatternCache", "BSA_OK", "stack_head_patterns",
     "pattern_order", "decode", "quantize_kv", "decode_int8kv", "attention", "plan_row_split",
-    "RowSplitPlan",
+    "RowSplitPlan", "backward_noalloc",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -105,6 +105,11 @@ def _load():
     lib.bsa_transpose_pattern.argtypes = [i32, p32, p32, i64, p32, p32]
     lib.bsa_transpose_pattern.restype = i32
     lib.bsa_backward.argtypes = [vp] * 10 + [i32] * 6 + [vp] * 6 + [i64, ctypes.c_float, i32, vp]
+    lib.bsa_backward_noalloc.argtypes = ([vp] * 9 + [i32] * 6 + [vp] * 6
+                                         + [i64, ctypes.c_float, i32, vp])
+    lib.bsa_backward_noalloc.restype = i32
+    lib.bsa_backward_noalloc_max_rows.argtypes = []
+    lib.bsa_backward_noalloc_max_rows.restype = i64
     lib.bsa_pattern_order.argtypes = [i32, p32, p32]
     lib.bsa_pattern_order.restype = i32
     lib.bsa_backward.restype = i32
@@ -489,6 +494,44 @@ def backward(q, k, v, o, lse, dout, row_ptr, col_idx, col_ptr, row_idx, block_si
         stream.cuda_stream)
     if st != BSA_OK:
         raise BsaError(st, "bsa_backward")
+    return dq, dk, dv
+
+
+def backward_noalloc(q, k, v, o, lse, dout, row_ptr, col_idx, col_ptr, row_idx,
+                     block_size: int, dq, dk, dv, scale: float | None = None, *,
+                     causal: bool = False, stream=None, row_order=None, col_order=None):
+    """``backward`` through bsa_backward_noalloc: the caller passes dq, dk
+    and dv, and D goes to the library's static device scratch instead of a
+    workspace, so the call allocates nothing on the device.  Calls that
+    overlap on one GPU share that scratch and must be ordered by the caller."""
+    import torch
+
+    if not q.is_cuda or q.dim() != 4:
+        raise ValueError("q must be a CUDA tensor [B, H, N, d]")
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq),
+                    ("dk", dk), ("dv", dv)):
+        _check_buffer(t, name, q.shape, q.dtype, q.device)
+    B, H, N, d = q.shape
+    _check_buffer(lse, "lse", (B, H, N), torch.float32, q.device)
+    rows = _pattern_rows(N, int(block_size), H, False)
+    _check_csr(row_ptr, col_idx, q.device, rows, col_idx.numel())
+    _check_csr(col_ptr, row_idx, q.device, rows, col_idx.numel(), ("col_ptr", "row_idx"))
+    for t in (row_order, col_order):
+        if t is not None and (t.dtype != torch.int32 or not t.is_cuda
+                              or t.numel() != row_ptr.numel() - 1):
+            raise ValueError("row_order / col_order must be int32 CUDA tensors of M entries")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = _load().bsa_backward_noalloc(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, int(block_size), _dtype_code(q),
+        row_ptr.data_ptr(), col_idx.data_ptr(), col_ptr.data_ptr(), row_idx.data_ptr(),
+        None if row_order is None else row_order.data_ptr(),
+        None if col_order is None else col_order.data_ptr(), int(col_idx.numel()),
+        0.0 if scale is None else float(scale), FORWARD_CAUSAL if causal else 0,
+        stream.cuda_stream)
+    if st != BSA_OK:
+        raise BsaError(st, "bsa_backward_noalloc")
     return dq, dk, dv
 
 

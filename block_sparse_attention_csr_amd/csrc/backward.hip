@@ -29,6 +29,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include <cmath>
 #include <cstdint>
 #include <type_traits>
@@ -524,14 +526,22 @@ bsa_status dispatch_bwd(const BwdParams& p, int bs, int d, bool causal, hipStrea
 
 }  // namespace
 
-extern "C" bsa_status bsa_backward(const void* q, const void* k, const void* v, const void* o,
-                                   const float* lse, const void* dout, void* dq, void* dk,
-                                   void* dv, float* delta, int32_t batch, int32_t heads,
-                                   int32_t seq_len, int32_t head_dim, int32_t block_size,
-                                   int32_t dtype, const int32_t* row_ptr, const int32_t* col_idx,
-                                   const int32_t* col_ptr, const int32_t* row_idx,
-                                   const int32_t* row_order, const int32_t* col_order,
-                                   int64_t nnz, float scale, int32_t flags, void* stream) {
+// Scratch of the allocation-free backward: D (one float per query row), in
+// device memory the code object itself holds.  Every GPU the library runs
+// on keeps its own copy until the process ends.
+constexpr int64_t kScratchRows = int64_t{1} << 22;  // 16 MiB of float
+static __device__ __align__(256) float scratch[kScratchRows];
+
+namespace {
+
+bsa_status backward_impl(const void* q, const void* k, const void* v, const void* o,
+                         const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                         float* delta, int32_t batch, int32_t heads, int32_t seq_len,
+                         int32_t head_dim, int32_t block_size, int32_t dtype,
+                         const int32_t* row_ptr, const int32_t* col_idx, const int32_t* col_ptr,
+                         const int32_t* row_idx, const int32_t* row_order,
+                         const int32_t* col_order, int64_t nnz, float scale, int32_t flags,
+                         void* stream) {
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr ||
       dout == nullptr || dq == nullptr || dk == nullptr || dv == nullptr || delta == nullptr ||
       row_ptr == nullptr || col_idx == nullptr || col_ptr == nullptr || row_idx == nullptr)
@@ -581,4 +591,63 @@ extern "C" bsa_status bsa_backward(const void* q, const void* k, const void* v, 
   (void)hipGetLastError();
   if (dtype == BSA_DTYPE_F32) return dispatch_bwd<float>(p, block_size, head_dim, causal, st);
   return dispatch_bwd<__bf16>(p, block_size, head_dim, causal, st);
+}
+
+// The device address of `scratch` on each device (looked up once per device,
+// with that device current).  In host code the array's name is only a
+// host-side stand-in, never a device address.
+std::atomic<void*> scratch_ptr[64];
+
+bsa_status scratch_on_current_device(float** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return BSA_ERR_HIP;
+  if (dev < 0 || dev >= 64) return BSA_ERR_INVALID_ARGUMENT;
+  void* ptr = scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return BSA_ERR_HIP;
+    }
+    scratch_ptr[dev].store(ptr, std::memory_order_release);
+  }
+  *out = static_cast<float*>(ptr);
+  return BSA_OK;
+}
+
+}  // namespace
+
+extern "C" bsa_status bsa_backward(const void* q, const void* k, const void* v, const void* o,
+                                   const float* lse, const void* dout, void* dq, void* dk,
+                                   void* dv, float* delta, int32_t batch, int32_t heads,
+                                   int32_t seq_len, int32_t head_dim, int32_t block_size,
+                                   int32_t dtype, const int32_t* row_ptr, const int32_t* col_idx,
+                                   const int32_t* col_ptr, const int32_t* row_idx,
+                                   const int32_t* row_order, const int32_t* col_order,
+                                   int64_t nnz, float scale, int32_t flags, void* stream) {
+  return backward_impl(q, k, v, o, lse, dout, dq, dk, dv, delta, batch, heads, seq_len, head_dim,
+                       block_size, dtype, row_ptr, col_idx, col_ptr, row_idx, row_order,
+                       col_order, nnz, scale, flags, stream);
+}
+
+extern "C" int64_t bsa_backward_noalloc_max_rows(void) { return kScratchRows; }
+
+extern "C" bsa_status bsa_backward_noalloc(const void* q, const void* k, const void* v,
+                                           const void* o, const float* lse, const void* dout,
+                                           void* dq, void* dk, void* dv, int32_t batch,
+                                           int32_t heads, int32_t seq_len, int32_t head_dim,
+                                           int32_t block_size, int32_t dtype,
+                                           const int32_t* row_ptr, const int32_t* col_idx,
+                                           const int32_t* col_ptr, const int32_t* row_idx,
+                                           const int32_t* row_order, const int32_t* col_order,
+                                           int64_t nnz, float scale, int32_t flags,
+                                           void* stream) {
+  if (batch > 0 && heads > 0 && seq_len > 0 &&
+      (int64_t)batch * heads * seq_len > kScratchRows)
+    return BSA_ERR_BUFFER_TOO_SMALL;
+  float* delta = nullptr;
+  const bsa_status st = scratch_on_current_device(&delta);
+  if (st != BSA_OK) return st;
+  return backward_impl(q, k, v, o, lse, dout, dq, dk, dv, delta, batch, heads, seq_len, head_dim,
+                       block_size, dtype, row_ptr, col_idx, col_ptr, row_idx, row_order,
+                       col_order, nnz, scale, flags, stream);
 }

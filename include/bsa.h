@@ -345,6 +345,37 @@ bsa_status bsa_backward(const void* q, const void* k, const void* v, const void*
 bsa_status bsa_pattern_order(int32_t M, const int32_t* ptr, int32_t* order);
 
 /*
+ * bsa_backward_noalloc -- bsa_backward without the caller's delta workspace,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same arguments, computation and results as bsa_backward, minus `delta`:
+ * D (one float per query row, batch * heads * seq_len of them) goes to a
+ * scratch array the library's code object holds in device memory, 16 MiB
+ * per GPU (bsa_backward_noalloc_max_rows() = 4194304 rows), kept until the
+ * process ends.  The call allocates nothing: no hipMalloc, no hipFree.  Its
+ * first call on a device looks up that device's scratch address once.
+ * Every call on one GPU shares that GPU's scratch, so calls that overlap on
+ * one GPU (other streams, other host threads) race and must be ordered by
+ * the caller; D is written in full before it is read, so nothing needs
+ * clearing between calls.
+ * Errors: as bsa_backward, plus BSA_ERR_BUFFER_TOO_SMALL when
+ * batch * heads * seq_len exceeds the scratch, and BSA_ERR_HIP when the
+ * scratch address cannot be looked up.
+ */
+bsa_status bsa_backward_noalloc(const void* q, const void* k, const void* v, const void* o,
+                                const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                                int32_t batch, int32_t heads, int32_t seq_len, int32_t head_dim,
+                                int32_t block_size, int32_t dtype, const int32_t* row_ptr,
+                                const int32_t* col_idx, const int32_t* col_ptr,
+                                const int32_t* row_idx, const int32_t* row_order,
+                                const int32_t* col_order, int64_t nnz, float scale, int32_t flags,
+                                void* stream);
+
+/* Query rows (batch * heads * seq_len) the scratch of bsa_backward_noalloc holds. */
+int64_t bsa_backward_noalloc_max_rows(void);
+
+/*
  * bsa_decode -- one new token per sequence against a block-aligned KV cache.
  *
  * The KV cache of sequence b holds L_b = seqlens[b] tokens; the new token is
