@@ -159,6 +159,45 @@ class Case:
                          split=self.split, workspace=self.workspace)
 
 
+class Int8KvCase:
+    """The forward on int8 K/V with per-block scales (bsa_forward_int8kv):
+    the workload's K and V quantised once (bsa_quantize_kv, untimed); a step
+    is one forward launch on the codes."""
+
+    def __init__(self, name, seed, device, causal=False):
+        import torch
+
+        import block_sparse_attention_csr_amd as bsa
+        from synthetic_inputs import WORKLOADS, make_qkv
+
+        assert not causal
+        self.bsa = bsa
+        self.w = w = WORKLOADS[name]
+        q, k, v = make_qkv(w.B, w.H, w.N, w.d, w.torch_dtype, seed)
+        self.q = q.to(device)
+        kd, vd = k.to(device), v.to(device)
+        self.kc, self.ks = bsa.quantize_kv(kd, w.block_size)
+        self.vc, self.vs = bsa.quantize_kv(vd, w.block_size)
+        del kd, vd
+        self.out = torch.empty_like(self.q)
+        self.lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=device)
+        rp, ci = bsa.build_pattern(w.N, w.block_size)
+        self.rp, self.ci, self.nnz = rp.to(device), ci.to(device), int(ci.numel())
+        torch.cuda.synchronize()
+        self.flops = 4.0 * w.block_size ** 2 * w.d * self.nnz * w.B * w.H
+        rows = w.B * w.H * w.N
+        # Q read and O written in bf16, K and V read as int8 codes plus one
+        # float32 scale per block each, LSE written
+        self.compulsory_bytes = (2.0 * 2 + 2.0 * 1) * rows * w.d + 4.0 * rows \
+            + 2.0 * 4 * w.B * w.H * w.M
+        self.bf16_bytes = 4.0 * 2 * rows * w.d + 4.0 * rows
+
+    def step(self):
+        w = self.w
+        self.bsa.forward_int8kv(self.q, self.kc, self.ks, self.vc, self.vs, self.rp, self.ci,
+                                w.block_size, out=self.out, lse=self.lse, nnz=self.nnz)
+
+
 class DecodeCase:
     """One decode step: a new token for each of B sequences against a KV cache
     of capacity N (cached lengths uniform on [1, N]), log-linear pattern."""
@@ -571,12 +610,14 @@ def workload_line(name, args, device):
     return line
 
 
-def side_line(name, args, device, causal, backward=False):
+def side_line(name, args, device, causal, backward=False, int8_kv=False):
     """A graph-timed line for another workload (the saturating B = 32 shape,
-    or its causal forward) reported beside the headline."""
+    its causal forward, its backward or its forward on int8 K/V) reported
+    beside the headline."""
     import torch
 
-    sat = (BackwardCase if backward else Case)(name, args.seed, device, causal=causal)
+    cls = BackwardCase if backward else Int8KvCase if int8_kv else Case
+    sat = cls(name, args.seed, device, causal=causal)
     for _ in range(5):
         sat.step()
     sat_steps = max(10, min(100, args.steps // 10))
@@ -584,8 +625,8 @@ def side_line(name, args, device, causal, backward=False):
     s_launch = time_events_per_launch(sat, sat_steps)
     s_step = s_graph if s_graph is not None else time_eager(sat, sat_steps)
     s_kernel = s_evt if s_evt is not None else s_launch
-    s_traffic = None if causal or backward else load_traffic(name)
-    s_mfma = None if causal or backward else load_mfma(name)
+    s_traffic = None if causal or backward or int8_kv else load_traffic(name)
+    s_mfma = None if causal or backward or int8_kv else load_mfma(name)
     line = {
         "value": round(sat.flops / s_step / 1e12, 3),
         "unit": "TFLOP/s",
@@ -598,7 +639,13 @@ def side_line(name, args, device, causal, backward=False):
         "traffic_over_algorithmic": None if s_traffic is None
         else round(s_traffic / sat.compulsory_bytes, 3),
     }
-    if not backward and not causal:
+    if int8_kv:
+        line["kv"] = "int8 codes + one float32 scale per block (bsa_quantize_kv), converted to bf16 in LDS"
+        line["compulsory_bytes_per_launch"] = sat.compulsory_bytes
+        line["bytes_vs_bf16_kv"] = round(sat.compulsory_bytes / sat.bf16_bytes, 4)
+        line["roofline"] = roofline_of(sat.flops, sat.compulsory_bytes, s_kernel,
+                                       PEAK_BF16_TFLOPS, None, None, "bsa_fwd_kernel (int8 K/V)")
+    elif not backward and not causal:
         line["mfma_flop_counted_per_launch"] = s_mfma
         line["mfma_counted_over_algorithmic"] = (None if s_mfma is None
                                                  else round(s_mfma / sat.flops, 4))
@@ -733,6 +780,8 @@ def main(argv=None):
                                                         causal=True)
         result["backward_worked_example_b32"] = side_line("worked_example_b32", args, device,
                                                           causal=False, backward=True)
+        result["int8kv_worked_example_b32"] = side_line("worked_example_b32", args, device,
+                                                        causal=False, int8_kv=True)
         for name in ("local_global", "random_mask", "long"):
             result[name] = workload_line(name, args, device)
         result["decode_worked_example"] = decode_line("decode_worked_example", args, device)

@@ -23,7 +23,7 @@ __all__ = [
     "BsaError", "build_pattern", "forward", "backward", "transpose_pattern", "status_string",
     "abi_version", "library_path", "PatternCache", "BSA_OK", "stack_head_patterns",
     "pattern_order", "decode", "quantize_kv", "decode_int8kv", "attention", "plan_row_split",
-    "RowSplitPlan", "backward_noalloc",
+    "RowSplitPlan", "backward_noalloc", "forward_int8kv",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -105,6 +105,9 @@ def _load():
     lib.bsa_transpose_pattern.argtypes = [i32, p32, p32, i64, p32, p32]
     lib.bsa_transpose_pattern.restype = i32
     lib.bsa_backward.argtypes = [vp] * 10 + [i32] * 6 + [vp] * 6 + [i64, ctypes.c_float, i32, vp]
+    lib.bsa_forward_int8kv.argtypes = ([vp] * 7 + [i32] * 5 + [vp, vp, i64, ctypes.c_float]
+                                       + [i32] * 3 + [vp])
+    lib.bsa_forward_int8kv.restype = i32
     lib.bsa_backward_noalloc.argtypes = ([vp] * 9 + [i32] * 6 + [vp] * 6
                                          + [i64, ctypes.c_float, i32, vp])
     lib.bsa_backward_noalloc.restype = i32
@@ -403,6 +406,54 @@ def forward(q, k, v, row_ptr, col_idx, block_size: int, scale: float | None = No
         st = lib.bsa_forward(*args, stream.cuda_stream)
     if st != BSA_OK:
         raise BsaError(st, "bsa_forward")
+    return out, lse
+
+
+def forward_int8kv(q, k_codes, k_scales, v_codes, v_scales, row_ptr, col_idx, block_size: int,
+                   scale: float | None = None, *, out=None, lse=None, nnz: int | None = None,
+                   stream=None, group: int = 0, key_split: int = 0, causal: bool = False,
+                   per_head: bool = False):
+    """``forward`` on int8 K/V with per-block scales (bsa_forward_int8kv).
+
+    q: bfloat16 CUDA [B, H, N, d]; k_codes, v_codes: int8 [B, H, N, d];
+    k_scales, v_scales: float32 [B, H, N / block_size] (as ``quantize_kv``
+    writes them).  Returns (o bfloat16 [B, H, N, d], lse float32 [B, H, N]).
+    """
+    import torch
+
+    if not q.is_cuda or not q.is_contiguous() or q.dim() != 4 or q.dtype != torch.bfloat16:
+        raise ValueError("q must be a contiguous bfloat16 CUDA tensor [B, H, N, d]")
+    B, H, N, d = q.shape
+    for name, t in (("k_codes", k_codes), ("v_codes", v_codes)):
+        _check_buffer(t, name, q.shape, torch.int8, q.device)
+    if int(block_size) <= 0 or N % int(block_size) != 0:
+        raise ValueError("N must be a positive multiple of block_size")
+    for name, t in (("k_scales", k_scales), ("v_scales", v_scales)):
+        _check_buffer(t, name, (B, H, N // int(block_size)), torch.float32, q.device)
+    if nnz is None:
+        nnz = col_idx.numel()
+    _check_csr(row_ptr, col_idx, q.device, _pattern_rows(N, int(block_size), H, per_head),
+               int(nnz))
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    if out is None:
+        with _on_stream(stream):
+            out = torch.empty_like(q)
+    else:
+        _check_buffer(out, "out", q.shape, q.dtype, q.device)
+    if lse is None:
+        with _on_stream(stream):
+            lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    else:
+        _check_buffer(lse, "lse", (B, H, N), torch.float32, q.device)
+    flags = (FORWARD_CAUSAL if causal else 0) | (FORWARD_PATTERN_PER_HEAD if per_head else 0)
+    st = _load().bsa_forward_int8kv(
+        q.data_ptr(), k_codes.data_ptr(), k_scales.data_ptr(), v_codes.data_ptr(),
+        v_scales.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d, int(block_size),
+        row_ptr.data_ptr(), col_idx.data_ptr(), int(nnz), 0.0 if scale is None else float(scale),
+        flags, int(group), int(key_split), stream.cuda_stream)
+    if st != BSA_OK:
+        raise BsaError(st, "bsa_forward_int8kv")
     return out, lse
 
 

@@ -84,7 +84,29 @@ struct FwdParams {
   const int32_t* split;
   int32_t n_items;
   float* partial;
+  // int8 K/V (bsa_forward_int8kv): k and v hold int8 codes, and these one
+  // float32 scale per (batch * head, block); NULL for bf16 / float32 K/V.
+  const float* k_scale;
+  const float* v_scale;
 };
+
+// Sixteen int8 codes (four words) as sixteen bf16 values, in order, in two
+// 16-byte groups.  A code is an integer in [-128, 127]: its float32 value
+// has at most 8 significant bits, so its upper half is its exact bf16.
+__device__ __forceinline__ void codes_to_bf16(const u32x4_t& w, u32x4_t& lo, u32x4_t& hi) {
+  uint32_t b[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float f[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) f[k] = (float)(int)(int8_t)(w[i] >> (8 * k));
+    b[2 * i] = __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
+    b[2 * i + 1] =
+        __builtin_amdgcn_perm(__float_as_uint(f[3]), __float_as_uint(f[2]), 0x07060302u);
+  }
+  lo = u32x4_t{b[0], b[1], b[2], b[3]};
+  hi = u32x4_t{b[4], b[5], b[6], b[7]};
+}
 
 // Partial state of a key-slice wave, stored for the merge: O^T in accumulator
 // order [reg][lane], then m and l per lane.
@@ -99,8 +121,11 @@ constexpr int half_partial_bytes() {
   return (D / 64) * 16 * kWave * 4 + 2 * kWave * 4;
 }
 
-// Compile-time shape of one kernel instantiation.
-template <typename T, int BS, int D, int G, int KS>
+// Compile-time shape of one kernel instantiation.  KV8: K and V are int8
+// codes; each entry lands as int8 in one of NB8 slots (copies NB8 - 1
+// entries ahead) and is converted to bf16 into the one tile buffer the math
+// reads.
+template <typename T, int BS, int D, int G, int KS, bool KV8 = false>
 struct Cfg {
   using L = TileLayout<T, BS, D>;
   static constexpr int QW = BS / kQRows;  // query waves per query block
@@ -114,16 +139,26 @@ struct Cfg {
   // workgroups per CU, else two (prefetch distance 1).  Key-split shapes keep
   // two: their slices already run KS entries ahead together, and the smaller
   // footprint keeps a whole small grid resident at once.
-  static constexpr int NB = KS == 1 && 3 * kSliceBytes <= 48 * 1024 ? 3 : 2;
+  static constexpr int kEntry8 = kEntry / 2;       // int8 K then V of one entry
+  static constexpr int kSlice8 = KS * kEntry8;
+  static constexpr int kPartsTile8 = BS * D / (kWave * 16);  // 1 KB parts of an int8 tile
+  static_assert(!KV8 || (2 * kPartsTile8) % SW == 0, "int8 entry parts split evenly");
+  static constexpr int kParts8 = 2 * kPartsTile8 / SW;       // per wave per entry
+  static constexpr int NB8 = KS == 1 && 2 * kSliceBytes + kSlice8 <= 48 * 1024 ? 3 : 2;
+  // KV8: buf0 is the bf16 tile buffer, buf1 int8 slots 0 and 1, buf2 slot 2.
+  static constexpr int NB = KV8 ? 2 : (KS == 1 && 3 * kSliceBytes <= 48 * 1024 ? 3 : 2);
+  static constexpr int kBuf2 = KV8 ? (NB8 == 3 ? kSlice8 : 16) : (NB == 3 ? kSliceBytes : 16);
+  static constexpr int kLdsBytes = 2 * kSliceBytes + kBuf2;
   // Shapes whose buffers do not fit a workgroup's LDS are not instantiated.
-  static constexpr bool kValid = NB * kSliceBytes + 1024 <= 160 * 1024 &&
+  static constexpr bool kValid = (!KV8 || std::is_same<T, __bf16>::value) &&
+                                 kLdsBytes + 1024 <= 160 * 1024 &&
                                  (KS - 1) * SW * partial_bytes<D>() <= kSliceBytes &&
                                  (KS != 2 || 2 * SW * half_partial_bytes<D>() <= kSliceBytes);
 };
 
-template <typename T, int BS, int D, int G, int KS, bool CAUSAL>
-__global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_kernel(FwdParams p) {
-  using C = Cfg<T, BS, D, G, KS>;
+template <typename T, int BS, int D, int G, int KS, bool CAUSAL, bool KV8 = false>
+__global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS, KV8>::W)) void bsa_fwd_kernel(FwdParams p) {
+  using C = Cfg<T, BS, D, G, KS, KV8>;
   using L = typename C::L;
   using O = Ops<T>;
   constexpr int QW = C::QW;
@@ -135,7 +170,7 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
   // copy in flight into one buffer from the reads of another.
   __shared__ __attribute__((aligned(16))) unsigned char buf0[C::kSliceBytes];
   __shared__ __attribute__((aligned(16))) unsigned char buf1[C::kSliceBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char buf2[NB == 3 ? C::kSliceBytes : 16];
+  __shared__ __attribute__((aligned(16))) unsigned char buf2[C::kBuf2];
   extern __shared__ __attribute__((aligned(16))) int32_t dyn[];  // entry list | bitmaps
   __shared__ int32_t union_size;
 
@@ -173,6 +208,10 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
   const T* Q = static_cast<const T*>(p.q) + head;
   const T* K = static_cast<const T*>(p.k) + head;
   const T* V = static_cast<const T*>(p.v) + head;
+  const int8_t* K8 = static_cast<const int8_t*>(p.k) + head;  // (KV8)
+  const int8_t* V8 = static_cast<const int8_t*>(p.v) + head;
+  const float* const ksc = KV8 ? p.k_scale + (size_t)bh * M : nullptr;  // (KV8) per block
+  const float* const vsc = KV8 ? p.v_scale + (size_t)bh * M : nullptr;
 
   // Several query blocks per workgroup: the loading wave of each block reads
   // the first 64 entries of its CSR row (one per lane) before any Q load.
@@ -213,7 +252,8 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
   using QL = TileLayout<T, kQRows, D>;
   constexpr bool kStageQ = G == 1 && std::is_same<T, __bf16>::value &&
                            C::W * QL::kTileBytes <= C::kSliceBytes;
-  unsigned char* const q_stage = (NB == 3 ? buf2 : buf1) + (ks * QW + qg) * QL::kTileBytes;
+  unsigned char* const q_stage =
+      (KV8 ? buf0 : NB == 3 ? buf2 : buf1) + (ks * QW + qg) * QL::kTileBytes;
   if constexpr (kStageQ) {
     const uint32_t dst = (uint32_t)(uintptr_t)(LDS_PTR(unsigned char))q_stage;
 #pragma unroll
@@ -287,7 +327,9 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
   int chunk_base = -64;
   int chunk = -1;
   uint64_t chunk_mine = 0;
-  auto entry_at = [&](int step, bool& mine) -> int {  // block of this slice's step, or -1
+  float chunk_ks = 0.f, chunk_vs = 0.f;  // (KV8) the entries' K and V scales
+  auto entry_at = [&](int step, bool& mine, float* sk = nullptr,
+                      float* sv = nullptr) -> int {  // block of this slice's step, or -1
     const int t = step * KS + ks;
     if (t >= U) {
       mine = false;
@@ -302,9 +344,18 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
       if constexpr (G > 1)
         sel = sel && ((my_row[chunk >> 5] >> (chunk & 31)) & 1u) != 0;
       chunk_mine = __builtin_amdgcn_ballot_w64(sel);
+      if constexpr (KV8) {
+        const bool in_range = chunk >= 0 && chunk < M;
+        chunk_ks = in_range ? ksc[chunk] : 0.f;
+        chunk_vs = in_range ? vsc[chunk] : 0.f;
+      }
     }
     const int l = t - chunk_base;
     mine = ((chunk_mine >> l) & 1ull) != 0;
+    if constexpr (KV8) {
+      *sk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, chunk_ks), l));
+      *sv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, chunk_vs), l));
+    }
     return __builtin_amdgcn_readlane(chunk, l);
   };
 
@@ -331,6 +382,38 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
       lds_dma16(base, (uint32_t)dma_off[c], dst + part * kWave * 16);
     }
   };
+  // (KV8) copies of an entry's int8 codes as they are: part c of this wave
+  // is part ws + c SW of the entry (1 KB; K tile parts first).
+  auto issue8 = [&](int j, uint32_t slot) {  // slot: LDS byte address
+    const int key0 = (j < 0 || j >= M ? 0 : j) * BS;
+    const uint32_t dst = slot + ks * C::kEntry8;
+#pragma unroll
+    for (int c = 0; c < C::kParts8; ++c) {
+      const int part = ws + c * SW;
+      const int8_t* base = (part < C::kPartsTile8 ? K8 : V8) + (size_t)key0 * D;
+      lds_dma16(base, (uint32_t)((part % C::kPartsTile8) * kWave * 16 + lane * 16),
+                dst + part * kWave * 16);
+    }
+  };
+  // (KV8) this wave's parts of the entry in `slot`, converted to bf16 into
+  // the tile buffer buf0 in the bf16 layout: lane i holds codes 16 i .. of
+  // its part, sixteen consecutive features of one row.
+  auto convert = [&](uint32_t slot) {
+#pragma unroll
+    for (int c = 0; c < C::kParts8; ++c) {
+      const int part = ws + c * SW;
+      const int e0 = (part % C::kPartsTile8) * kWave * 16 + lane * 16;  // element of the tile
+      const int row = e0 / D, f0 = e0 % D;
+      const u32x4_t w = *(LDS_PTR(const u32x4_t))(uintptr_t)(slot + ks * C::kEntry8 +
+                                                             part * kWave * 16 + lane * 16);
+      u32x4_t lo, hi;
+      codes_to_bf16(w, lo, hi);
+      LDS_PTR(unsigned char) dst = (LDS_PTR(unsigned char))buf0 + ks * C::kEntry +
+                                   (part < C::kPartsTile8 ? 0 : L::kTileBytes);
+      *(LDS_PTR(u32x4_t))(dst + L::chunk_offset(row, f0 / 8)) = lo;
+      *(LDS_PTR(u32x4_t))(dst + L::chunk_offset(row, f0 / 8 + 1)) = hi;
+    }
+  };
 
   typename O::template Offsets<BS, D> off;
   off.init(lane, ks * C::kEntry);
@@ -349,8 +432,19 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
   // `diag`: the entry is this wave's own query block under causal masking.
   // Its 32-key steps after the wave's 32 rows are skipped, the step level
   // with them is masked above the diagonal (the keys after each query).
-  auto compute = [&](unsigned char* buf, bool diag) {
+  // KV8: the tile holds the codes, so the scores are sk (q . code): sk folds
+  // into the score factor; and the product runs on P sv, sv folded into the
+  // exponent, while the row sum takes P = (P sv) / sv.  A zero scale (an
+  // all-zero block, codes 0) may take any value: 1.
+  auto compute = [&](unsigned char* buf, bool diag, float sk = 1.f, float sv = 1.f) {
     LDS_PTR(unsigned char) tile = (LDS_PTR(unsigned char))buf;
+    const float c2k = KV8 ? c2 * (sk > 0.f ? sk : 1.f) : c2;
+    float lsv = 0.f, isv = 1.f;
+    if constexpr (KV8) {
+      const float sve = sv > 0.f ? sv : 1.f;
+      lsv = __builtin_amdgcn_logf(sve);
+      isv = __builtin_amdgcn_rcpf(sve);
+    }
     f32x16_t sc[KSTEPS];
 #pragma unroll
     for (int st = 0; st < KSTEPS; ++st) sc[st] = O::template scores<BS, D>(qop, off, tile, 0, st);
@@ -367,7 +461,7 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
       float mx = sc[st][0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) mx = __builtin_elementwise_maximum(mx, sc[st][r]);
-      mx = halves_max(mx) * c2;
+      mx = halves_max(mx) * c2k;
       if (first) {  // O and l are still zero: no rescale
         m2 = mx;
         first = false;
@@ -380,8 +474,9 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
         for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sc[st][r] = fast_exp2(fmaf(sc[st][r], c2, -m2));
-      lsum += O::template accumulate<BS, D>(o, sc[st], off, tile, 0, st);
+      for (int r = 0; r < 16; ++r) sc[st][r] = fast_exp2(fmaf(sc[st][r], c2k, KV8 ? lsv - m2 : -m2));
+      const float ps = O::template accumulate<BS, D>(o, sc[st], off, tile, 0, st);
+      lsum = KV8 ? fmaf(ps, isv, lsum) : lsum + ps;
     }
   };
 
@@ -396,50 +491,112 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
   // 1's copies land over them).  Uncoupled, the slices no longer wait for
   // each other at every entry (worked example 1-2% faster, graph-timed).
   constexpr bool kSliceBarrier = G > 1 || SW > 1;
-  int jq[NB];   // blocks of steps i .. i + NB - 1
-  bool mq[NB];  // whether this wave computes them
-#pragma unroll
-  for (int e = 0; e < NB; ++e) jq[e] = entry_at(e, mq[e]);
-  // The Q loads were issued long ago; waiting for them here, before the first
-  // copy, tells the compiler they are complete (it does not see the copies
-  // and would otherwise wait on the vector-memory counter inside the loop).
-  wait_vm_lgkm0<0>();
-  if constexpr (kStageQ) {  // lane (query r, half h) takes chunks 2c + h of row r
-    LDS_PTR(const unsigned char) qs = (LDS_PTR(const unsigned char))q_stage;
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c)
-      qop.r[c] = *(LDS_PTR(const u32x4_t))(qs + QL::chunk_offset(lane & 31, 2 * c + (lane >> 5)));
-  }
-  // The first copies, for the steps there are (none for a row with no entry).
-  if (niter > 0) issue(jq[0], buf0);
-  if (NB == 3 && niter > 1) issue(jq[1], buf1);
-  auto buffer = [&](auto b_c) -> unsigned char* {
-    constexpr int b = decltype(b_c)::value;
-    if constexpr (b == 0) return buf0;
-    else if constexpr (b == 1) return buf1;
-    else return buf2;
-  };
-  auto step = [&](int i, auto b_c) {
-    constexpr int b = decltype(b_c)::value;
-    if (NB == 3 && i + 1 < niter) wait_vm_lgkm0<C::kParts>();
-    else wait_vm_lgkm0<0>();
-    if (kSliceBarrier || i == 0) raw_barrier();
-    const bool mine = mq[0];
-    const bool diag = causal && jq[0] == qb;
-#pragma unroll
-    for (int e = 0; e + 1 < NB; ++e) {
-      jq[e] = jq[e + 1];
-      mq[e] = mq[e + 1];
+  if constexpr (!KV8) {
+    int jq[NB];   // blocks of steps i .. i + NB - 1
+    bool mq[NB];  // whether this wave computes them
+  #pragma unroll
+    for (int e = 0; e < NB; ++e) jq[e] = entry_at(e, mq[e]);
+    // The Q loads were issued long ago; waiting for them here, before the first
+    // copy, tells the compiler they are complete (it does not see the copies
+    // and would otherwise wait on the vector-memory counter inside the loop).
+    wait_vm_lgkm0<0>();
+    if constexpr (kStageQ) {  // lane (query r, half h) takes chunks 2c + h of row r
+      LDS_PTR(const unsigned char) qs = (LDS_PTR(const unsigned char))q_stage;
+  #pragma unroll
+      for (int c = 0; c < D / 16; ++c)
+        qop.r[c] = *(LDS_PTR(const u32x4_t))(qs + QL::chunk_offset(lane & 31, 2 * c + (lane >> 5)));
     }
-    jq[NB - 1] = entry_at(i + NB, mq[NB - 1]);
-    if (i + NB - 1 < niter) issue(jq[NB - 2], buffer(std::integral_constant<int, (b + NB - 1) % NB>{}));
-    if (mine) compute(buffer(b_c), diag);
-  };
-  for (int i = 0; i < niter; i += NB) {
-    step(i, std::integral_constant<int, 0>{});
-    if (i + 1 < niter) step(i + 1, std::integral_constant<int, 1>{});
-    if constexpr (NB == 3)
-      if (i + 2 < niter) step(i + 2, std::integral_constant<int, 2>{});
+    // The first copies, for the steps there are (none for a row with no entry).
+    if (niter > 0) issue(jq[0], buf0);
+    if (NB == 3 && niter > 1) issue(jq[1], buf1);
+    auto buffer = [&](auto b_c) -> unsigned char* {
+      constexpr int b = decltype(b_c)::value;
+      if constexpr (b == 0) return buf0;
+      else if constexpr (b == 1) return buf1;
+      else return buf2;
+    };
+    auto step = [&](int i, auto b_c) {
+      constexpr int b = decltype(b_c)::value;
+      if (NB == 3 && i + 1 < niter) wait_vm_lgkm0<C::kParts>();
+      else wait_vm_lgkm0<0>();
+      if (kSliceBarrier || i == 0) raw_barrier();
+      const bool mine = mq[0];
+      const bool diag = causal && jq[0] == qb;
+  #pragma unroll
+      for (int e = 0; e + 1 < NB; ++e) {
+        jq[e] = jq[e + 1];
+        mq[e] = mq[e + 1];
+      }
+      jq[NB - 1] = entry_at(i + NB, mq[NB - 1]);
+      if (i + NB - 1 < niter) issue(jq[NB - 2], buffer(std::integral_constant<int, (b + NB - 1) % NB>{}));
+      if (mine) compute(buffer(b_c), diag);
+    };
+    for (int i = 0; i < niter; i += NB) {
+      step(i, std::integral_constant<int, 0>{});
+      if (i + 1 < niter) step(i + 1, std::integral_constant<int, 1>{});
+      if constexpr (NB == 3)
+        if (i + 2 < niter) step(i + 2, std::integral_constant<int, 2>{});
+    }
+  } else {
+    // int8 entries land in NB8 slots, copies NB8 - 1 entries ahead.  Step i:
+    // every wave waits for its own copies of entry i; a barrier (entry i has
+    // landed, every wave is done with the tile buffer); the copies of entry
+    // i + NB8 - 1 go into the slot entry i - 1 was converted from; entry i is
+    // converted into the tile buffer; a barrier; the math.  One-wave slices
+    // convert and read only their own parts: their own waits suffice.
+    constexpr int NB8 = C::NB8;
+    int jq[NB8];
+    bool mq[NB8];
+    float skq[NB8], svq[NB8];
+#pragma unroll
+    for (int e = 0; e < NB8; ++e) jq[e] = entry_at(e, mq[e], &skq[e], &svq[e]);
+    wait_vm_lgkm0<0>();
+    if constexpr (kStageQ) {
+      LDS_PTR(const unsigned char) qs = (LDS_PTR(const unsigned char))q_stage;
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c)
+        qop.r[c] = *(LDS_PTR(const u32x4_t))(qs + QL::chunk_offset(lane & 31, 2 * c + (lane >> 5)));
+    }
+    const uint32_t slots01 = (uint32_t)(uintptr_t)(LDS_PTR(unsigned char))buf1;
+    const uint32_t slot2 = (uint32_t)(uintptr_t)(LDS_PTR(unsigned char))buf2;
+    auto slot = [&](auto b_c) -> uint32_t {  // LDS byte address of int8 slot b
+      constexpr int b = decltype(b_c)::value;
+      if constexpr (b < 2) return slots01 + b * C::kSlice8;
+      else return slot2;
+    };
+    if (niter > 0) issue8(jq[0], slot(std::integral_constant<int, 0>{}));
+    if (NB8 == 3 && niter > 1) issue8(jq[1], slot(std::integral_constant<int, 1>{}));
+    auto step8 = [&](int i, auto b_c) {
+      constexpr int b = decltype(b_c)::value;
+      if (NB8 == 3 && i + 1 < niter) wait_vm_lgkm0<C::kParts8>();
+      else wait_vm_lgkm0<0>();
+      if (kSliceBarrier || i == 0) raw_barrier();
+      const bool mine = mq[0];
+      const bool diag = causal && jq[0] == qb;
+      const float sk = skq[0], sv = svq[0];
+#pragma unroll
+      for (int e = 0; e + 1 < NB8; ++e) {
+        jq[e] = jq[e + 1];
+        mq[e] = mq[e + 1];
+        skq[e] = skq[e + 1];
+        svq[e] = svq[e + 1];
+      }
+      jq[NB8 - 1] = entry_at(i + NB8, mq[NB8 - 1], &skq[NB8 - 1], &svq[NB8 - 1]);
+      if (i + NB8 - 1 < niter)
+        issue8(jq[NB8 - 2], slot(std::integral_constant<int, (b + NB8 - 1) % NB8>{}));
+      convert(slot(b_c));
+      if constexpr (kSliceBarrier) {
+        wait_lgkm0();
+        raw_barrier();
+      }
+      if (mine) compute(buf0, diag, sk, sv);
+    };
+    for (int i = 0; i < niter; i += NB8) {
+      step8(i, std::integral_constant<int, 0>{});
+      if (i + 1 < niter) step8(i + 1, std::integral_constant<int, 1>{});
+      if constexpr (NB8 == 3)
+        if (i + 2 < niter) step8(i + 2, std::integral_constant<int, 2>{});
+    }
   }
 
   // No copy may still be landing in the ring once it is reused below (the
@@ -557,7 +714,8 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
   constexpr int kStage = kQRows * kRowB;          // a wave's 32 rows
   constexpr int kPerBuf = C::kSliceBytes / kStage;
   constexpr int kStoreWaves = KS > 1 ? SW : C::W;
-  constexpr bool kStaged = kPerBuf >= 1 && kStoreWaves <= (NB == 3 ? 2 : 1) * kPerBuf;
+  // (staged through buf1, then buf2 for a three-buffer ring, or buf0 for int8 K/V)
+  constexpr bool kStaged = kPerBuf >= 1 && kStoreWaves <= (KV8 || NB == 3 ? 2 : 1) * kPerBuf;
   if constexpr (kStaged && KS == 1) __syncthreads();  // every wave is done with the ring
   if (!has_rows) return;
   const float l_all = halves_sum(lsum);
@@ -566,7 +724,8 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS>::W)) void bsa_fwd_ker
   const int row = q0 + (lane & 31);
   if constexpr (kStaged) {
     const int wv = KS > 1 ? ws : wave;  // index among the storing waves
-    unsigned char* region = (NB == 3 && wv >= kPerBuf ? buf2 : buf1) + (wv % kPerBuf) * kStage;
+    unsigned char* region =
+        (wv < kPerBuf ? buf1 : KV8 ? buf0 : buf2) + (wv % kPerBuf) * kStage;
     store_rows_lds<T, D>(static_cast<T*>(p.o) + head + (size_t)q0 * D, o, inv, lane,
                          (LDS_PTR(unsigned char))region);
   } else {
@@ -647,27 +806,28 @@ size_t dynamic_lds_bytes(int group, int M) {
   return 4 * ((size_t)M + words);
 }
 
-template <typename T, int BS, int D, int G, int KS>
+template <typename T, int BS, int D, int G, int KS, bool KV8 = false>
 constexpr size_t static_lds_bytes() {  // 0 for a shape that is not instantiated
-  using C = Cfg<T, BS, D, G, KS>;
-  return C::kValid ? (size_t)C::NB * C::kSliceBytes + 16 : 0;
+  using C = Cfg<T, BS, D, G, KS, KV8>;
+  return C::kValid ? (size_t)C::kLdsBytes + 16 : 0;
 }
 
-template <typename T, int BS, int D, int G, int KS, bool CAUSAL>
+template <typename T, int BS, int D, int G, int KS, bool CAUSAL, bool KV8>
 bsa_status launch_kernel(const FwdParams& p, hipStream_t stream) {
-  using C = Cfg<T, BS, D, G, KS>;
+  using C = Cfg<T, BS, D, G, KS, KV8>;
   if constexpr (!C::kValid) {
     return BSA_ERR_INVALID_ARGUMENT;
   } else {
+  constexpr size_t kStatic = static_lds_bytes<T, BS, D, G, KS, KV8>();
   const size_t dyn = dynamic_lds_bytes(G, p.M);
-  if (dyn + static_lds_bytes<T, BS, D, G, KS>() > kMaxLds) return BSA_ERR_INVALID_ARGUMENT;
-  if (dyn + static_lds_bytes<T, BS, D, G, KS>() > 64 * 1024) {
+  if (dyn + kStatic > kMaxLds) return BSA_ERR_INVALID_ARGUMENT;
+  if (dyn + kStatic > 64 * 1024) {
     static std::atomic<uint64_t> raised{0};  // per instantiation, one bit per device
     uint64_t bit;
     if (due_on_device(raised, &bit)) {
-      if (hipFuncSetAttribute(reinterpret_cast<const void*>(&bsa_fwd_kernel<T, BS, D, G, KS, CAUSAL>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize,
-                              static_cast<int>(kMaxLds - static_lds_bytes<T, BS, D, G, KS>())) !=
+      if (hipFuncSetAttribute(
+              reinterpret_cast<const void*>(&bsa_fwd_kernel<T, BS, D, G, KS, CAUSAL, KV8>),
+              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kMaxLds - kStatic)) !=
           hipSuccess)
         return BSA_ERR_HIP;
       mark_done(raised, bit);
@@ -675,26 +835,39 @@ bsa_status launch_kernel(const FwdParams& p, hipStream_t stream) {
   }
   const dim3 block(kWave * C::W);
   const dim3 grid(p.num_wg);
-  hipLaunchKernelGGL((bsa_fwd_kernel<T, BS, D, G, KS, CAUSAL>), grid, block, dyn, stream, p);
+  hipLaunchKernelGGL((bsa_fwd_kernel<T, BS, D, G, KS, CAUSAL, KV8>), grid, block, dyn, stream,
+                     p);
   return hipGetLastError() == hipSuccess ? BSA_OK : BSA_ERR_HIP;
   }
 }
 
 template <typename T, int BS, int D, int G, int KS>
 bsa_status launch(const FwdParams& p, hipStream_t stream) {
-  return p.causal != 0 ? launch_kernel<T, BS, D, G, KS, true>(p, stream)
-                       : launch_kernel<T, BS, D, G, KS, false>(p, stream);
+  if (p.k_scale != nullptr) {  // int8 K/V: bf16 only
+    if constexpr (std::is_same<T, __bf16>::value)
+      return p.causal != 0 ? launch_kernel<T, BS, D, G, KS, true, true>(p, stream)
+                           : launch_kernel<T, BS, D, G, KS, false, true>(p, stream);
+    else
+      return BSA_ERR_INVALID_ARGUMENT;
+  }
+  return p.causal != 0 ? launch_kernel<T, BS, D, G, KS, true, false>(p, stream)
+                       : launch_kernel<T, BS, D, G, KS, false, false>(p, stream);
 }
 
 // Static LDS of a shape, or 0 when the shape is not instantiated.
-template <typename T, int BS, int D>
-size_t shape_lds(int group, int key_split) {
-  if (group == 1 && key_split == 1) return static_lds_bytes<T, BS, D, 1, 1>();
-  if (group == 1 && key_split == 2) return static_lds_bytes<T, BS, D, 1, 2>();
-  if (group == 1 && key_split == 4) return static_lds_bytes<T, BS, D, 1, 4>();
-  if (group == 2 && key_split == 1) return static_lds_bytes<T, BS, D, 2, 1>();
-  if (group == 4 && key_split == 1) return static_lds_bytes<T, BS, D, 4, 1>();
+template <typename T, int BS, int D, bool KV8>
+size_t shape_lds_kv(int group, int key_split) {
+  if (group == 1 && key_split == 1) return static_lds_bytes<T, BS, D, 1, 1, KV8>();
+  if (group == 1 && key_split == 2) return static_lds_bytes<T, BS, D, 1, 2, KV8>();
+  if (group == 1 && key_split == 4) return static_lds_bytes<T, BS, D, 1, 4, KV8>();
+  if (group == 2 && key_split == 1) return static_lds_bytes<T, BS, D, 2, 1, KV8>();
+  if (group == 4 && key_split == 1) return static_lds_bytes<T, BS, D, 4, 1, KV8>();
   return 0;
+}
+template <typename T, int BS, int D>
+size_t shape_lds(int group, int key_split, bool kv8) {
+  return kv8 ? shape_lds_kv<T, BS, D, true>(group, key_split)
+             : shape_lds_kv<T, BS, D, false>(group, key_split);
 }
 
 template <typename T, int BS, int D>
@@ -741,25 +914,21 @@ int64_t split_workspace_bytes(int64_t bh, int bs, int d, int64_t n_items) {
   return bh * n_items * (bs / kQRows) * per_wave;
 }
 
-// Total LDS of a shape for (dtype, bs, d), or 0 when it is not instantiated.
-size_t lds_for(int dtype, int bs, int d, int group, int ks, int M) {
+// Total LDS of a shape for (dtype, bs, d, int8 K/V), or 0 when it is not
+// instantiated.
+size_t lds_for(int dtype, int bs, int d, int group, int ks, int M, bool kv8 = false) {
   size_t st = 0;
   if (dtype == BSA_DTYPE_F32) {
-    if (bs == 32) st = d == 64 ? shape_lds<float, 32, 64>(group, ks) : shape_lds<float, 32, 128>(group, ks);
-    else st = d == 64 ? shape_lds<float, 64, 64>(group, ks) : shape_lds<float, 64, 128>(group, ks);
+    if (kv8) return 0;
+    if (bs == 32) st = d == 64 ? shape_lds<float, 32, 64>(group, ks, false) : shape_lds<float, 32, 128>(group, ks, false);
+    else st = d == 64 ? shape_lds<float, 64, 64>(group, ks, false) : shape_lds<float, 64, 128>(group, ks, false);
   } else {
-    if (bs == 32) st = d == 64 ? shape_lds<__bf16, 32, 64>(group, ks) : shape_lds<__bf16, 32, 128>(group, ks);
-    else st = d == 64 ? shape_lds<__bf16, 64, 64>(group, ks) : shape_lds<__bf16, 64, 128>(group, ks);
+    if (bs == 32) st = d == 64 ? shape_lds<__bf16, 32, 64>(group, ks, kv8) : shape_lds<__bf16, 32, 128>(group, ks, kv8);
+    else st = d == 64 ? shape_lds<__bf16, 64, 64>(group, ks, kv8) : shape_lds<__bf16, 64, 128>(group, ks, kv8);
   }
   return st == 0 ? 0 : st + dynamic_lds_bytes(group, M);
 }
 
-// Workgroup shape.  Large grids: G query blocks per workgroup share their K/V
-// tiles (4 blocks of 32 rows, or 2 of 64).  Smaller grids: one query block
-// per workgroup, which has the shortest critical path, with each CSR row split
-// over KS key-slice wave sets while the grid stays within two waves per SIMD
-// (the worked example, 1024 query blocks of one wave, runs 9.2 us with KS = 2
-// against 9.8 us with KS = 1).
 // Compute units of the current device (read once per device; 256 on an
 // MI355X, the figure used if the query fails).
 int64_t device_cus() {
@@ -779,12 +948,19 @@ int64_t device_cus() {
   return n;
 }
 
-void choose_shape(int64_t bhm, int bs, int d, int dtype, int M, int* group, int* key_split) {
+// Workgroup shape.  Large grids: G query blocks per workgroup share their K/V
+// tiles (4 blocks of 32 rows, or 2 of 64).  Smaller grids: one query block
+// per workgroup, which has the shortest critical path, with each CSR row split
+// over KS key-slice wave sets while the grid stays within two waves per SIMD
+// (the worked example, 1024 query blocks of one wave, runs 9.2 us with KS = 2
+// against 9.8 us with KS = 1).
+void choose_shape(int64_t bhm, int bs, int d, int dtype, int M, int* group, int* key_split,
+                  bool kv8 = false) {
   const int64_t kCus = device_cus();
   const int64_t kLargeGrid = 8 * 4 * kCus;  // 8 query waves per SIMD
   const int qw = bs / kQRows;
   auto fits = [&](int g, int ks) {
-    const size_t b = lds_for(dtype, bs, d, g, ks, M);
+    const size_t b = lds_for(dtype, bs, d, g, ks, M, kv8);
     return b != 0 && b <= kMaxLds;
   };
   int g = 1, ks = 1;
@@ -820,7 +996,8 @@ bsa_status forward_impl(const void* q, const void* k, const void* v, void* o, fl
                         int32_t block_size, int32_t dtype, const int32_t* row_ptr,
                         const int32_t* col_idx, int64_t nnz, float scale, int32_t flags,
                         int32_t group, int32_t key_split, void* stream,
-                        const SplitPlan* plan = nullptr) {
+                        const SplitPlan* plan = nullptr, const float* k_scale = nullptr,
+                        const float* v_scale = nullptr) {
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || row_ptr == nullptr ||
       col_idx == nullptr)
     return BSA_ERR_NULL_POINTER;
@@ -857,6 +1034,11 @@ bsa_status forward_impl(const void* q, const void* k, const void* v, void* o, fl
   p.split = nullptr;
   p.n_items = 0;
   p.partial = nullptr;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  const bool kv8 = k_scale != nullptr;
+  if (kv8 && (v_scale == nullptr || dtype != BSA_DTYPE_BF16 || plan != nullptr))
+    return BSA_ERR_INVALID_ARGUMENT;
   const bool split = plan != nullptr && plan->n_items > 0;
   if (plan != nullptr) {
     if (per_head) return BSA_ERR_INVALID_ARGUMENT;  // the plan is of one shared pattern
@@ -878,14 +1060,14 @@ bsa_status forward_impl(const void* q, const void* k, const void* v, void* o, fl
   }
   if (group == 0 && key_split == 0) {
     choose_shape((int64_t)batch * heads * M, block_size, head_dim, dtype, (int)M, &p.group,
-                 &p.key_split);
+                 &p.key_split, kv8);
   } else {
     const int qw = block_size / kQRows;
     if (qw * group * key_split > kMaxWaves) return BSA_ERR_INVALID_ARGUMENT;
     p.group = group;
     p.key_split = key_split;
   }
-  const size_t lds = lds_for(dtype, block_size, head_dim, p.group, p.key_split, (int)M);
+  const size_t lds = lds_for(dtype, block_size, head_dim, p.group, p.key_split, (int)M, kv8);
   if (lds == 0 || lds > kMaxLds) return BSA_ERR_INVALID_ARGUMENT;
   const int64_t ngroups = (M + p.group - 1) / p.group;
   const int64_t num_wg = (int64_t)batch * heads * ngroups;
@@ -960,4 +1142,18 @@ extern "C" bsa_status bsa_forward_split(const void* q, const void* k, const void
   const SplitPlan plan{heavy, items, n_items, rows, n_rows, workspace, workspace_bytes};
   return forward_impl(q, k, v, o, lse, batch, heads, seq_len, head_dim, block_size, dtype,
                       row_ptr, col_idx, nnz, scale, flags, 0, 0, stream, &plan);
+}
+
+extern "C" bsa_status bsa_forward_int8kv(const void* q, const int8_t* k_codes,
+                                         const float* k_scales, const int8_t* v_codes,
+                                         const float* v_scales, void* o, float* lse,
+                                         int32_t batch, int32_t heads, int32_t seq_len,
+                                         int32_t head_dim, int32_t block_size,
+                                         const int32_t* row_ptr, const int32_t* col_idx,
+                                         int64_t nnz, float scale, int32_t flags, int32_t group,
+                                         int32_t key_split, void* stream) {
+  if (k_scales == nullptr || v_scales == nullptr) return BSA_ERR_NULL_POINTER;
+  return forward_impl(q, k_codes, v_codes, o, lse, batch, heads, seq_len, head_dim, block_size,
+                      BSA_DTYPE_BF16, row_ptr, col_idx, nnz, scale, flags, group, key_split,
+                      stream, nullptr, k_scales, v_scales);
 }

@@ -398,6 +398,11 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt((n & 0xF) | (0x7 << 4) | (0x0 << 8) | ((n >> 4) << 14));
 }
 
+// s_waitcnt: LDS/scalar count == 0, vector-memory count left as it is.
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
+}
+
 // Direct-to-LDS copy of 16 bytes per lane: lane i reads sbase + voff (its
 // own offset) and the data lands at LDS byte address m0 + 16 i.  Written as
 // asm so that the compiler does not add waits for these copies in front of

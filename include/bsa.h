@@ -345,6 +345,35 @@ bsa_status bsa_backward(const void* q, const void* k, const void* v, const void*
 bsa_status bsa_pattern_order(int32_t M, const int32_t* ptr, int32_t* order);
 
 /*
+ * bsa_forward_int8kv -- bsa_forward on int8 K and V with one scale per block.
+ *
+ * The log-linear page's section 6.3 keeps K and V in int8 with one scale per
+ * block and computes attention in 16-bit floating point.  This is the
+ * forward of bsa_forward_ex with K_p = k_codes[p] * k_scales[p / bs] and
+ * V_p = v_codes[p] * v_scales[p / bs] (per batch and head), as
+ * bsa_quantize_kv writes them.  The codes convert exactly to bf16 on the way
+ * into the matrix cores; the K scale multiplies the scores and the V scale
+ * the softmax weights of its block, so the arithmetic is that of the bf16
+ * forward on the dequantised values.  K and V move half the bytes of bf16.
+ *
+ * q, o, lse  as for bsa_forward, bf16 (q and o) only.
+ * k_codes, v_codes    device int8 [batch, heads, seq_len, head_dim],
+ *            16-byte aligned.
+ * k_scales, v_scales  device float32 [batch, heads, seq_len / block_size].
+ * row_ptr, col_idx, nnz, scale  as for bsa_forward.
+ * flags      0, BSA_FORWARD_CAUSAL and/or BSA_FORWARD_PATTERN_PER_HEAD.
+ * group, key_split   0, 0 (the library chooses) or a workgroup shape, as for
+ *            bsa_forward_ex.
+ * Errors as for bsa_forward_ex; NULL scales: BSA_ERR_NULL_POINTER.
+ */
+bsa_status bsa_forward_int8kv(const void* q, const int8_t* k_codes, const float* k_scales,
+                              const int8_t* v_codes, const float* v_scales, void* o, float* lse,
+                              int32_t batch, int32_t heads, int32_t seq_len, int32_t head_dim,
+                              int32_t block_size, const int32_t* row_ptr, const int32_t* col_idx,
+                              int64_t nnz, float scale, int32_t flags, int32_t group,
+                              int32_t key_split, void* stream);
+
+/*
  * bsa_backward_noalloc -- bsa_backward without the caller's delta workspace,
  * for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc).
