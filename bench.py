@@ -77,7 +77,10 @@ def parse_args(argv=None):
                    help="time the causal forward (keys after each query hidden; the pattern "
                         "built causal) instead of the plain one")
     p.add_argument("--int8-kv", action="store_true",
-                   help="with a decode workload: decode on the int8 cache (bsa_decode_int8kv)")
+                   help="decode on the int8 cache (bsa_decode_int8kv) for a decode workload; "
+                        "the forward on int8 K/V (bsa_forward_int8kv) for a forward one")
+    p.add_argument("--backward", action="store_true",
+                   help="time the backward (dQ, dK, dV) of the workload instead of its forward")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run 5 device-to-device copies of 1 GiB (reference kernel for "
                         "scaling HBM byte counters) and exit")
@@ -168,11 +171,12 @@ class Int8KvCase:
         import torch
 
         import block_sparse_attention_csr_amd as bsa
-        from synthetic_inputs import WORKLOADS, make_qkv
+        from synthetic_inputs import WORKLOADS, make_qkv, workload_block_mask
 
         assert not causal
         self.bsa = bsa
         self.w = w = WORKLOADS[name]
+        self.mask = workload_block_mask(w, seed)
         q, k, v = make_qkv(w.B, w.H, w.N, w.d, w.torch_dtype, seed)
         self.q = q.to(device)
         kd, vd = k.to(device), v.to(device)
@@ -181,7 +185,7 @@ class Int8KvCase:
         del kd, vd
         self.out = torch.empty_like(self.q)
         self.lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=device)
-        rp, ci = bsa.build_pattern(w.N, w.block_size)
+        rp, ci = bsa.build_pattern(w.N, w.block_size, mask=self.mask)
         self.rp, self.ci, self.nnz = rp.to(device), ci.to(device), int(ci.numel())
         torch.cuda.synchronize()
         self.flops = 4.0 * w.block_size ** 2 * w.d * self.nnz * w.B * w.H
@@ -191,6 +195,11 @@ class Int8KvCase:
         self.compulsory_bytes = (2.0 * 2 + 2.0 * 1) * rows * w.d + 4.0 * rows \
             + 2.0 * 4 * w.B * w.H * w.M
         self.bf16_bytes = 4.0 * 2 * rows * w.d + 4.0 * rows
+        self.split = None
+        t0 = time.perf_counter()
+        self.step()
+        torch.cuda.synchronize()
+        self.first_step_ms = (time.perf_counter() - t0) * 1e3
 
     def step(self):
         w = self.w
@@ -625,8 +634,9 @@ def side_line(name, args, device, causal, backward=False, int8_kv=False):
     s_launch = time_events_per_launch(sat, sat_steps)
     s_step = s_graph if s_graph is not None else time_eager(sat, sat_steps)
     s_kernel = s_evt if s_evt is not None else s_launch
-    s_traffic = None if causal or backward or int8_kv else load_traffic(name)
-    s_mfma = None if causal or backward or int8_kv else load_mfma(name)
+    record = name + ("_int8kv" if int8_kv else "")
+    s_traffic = None if causal or backward else load_traffic(record)
+    s_mfma = None if causal or backward else load_mfma(record)
     line = {
         "value": round(sat.flops / s_step / 1e12, 3),
         "unit": "TFLOP/s",
@@ -644,7 +654,8 @@ def side_line(name, args, device, causal, backward=False, int8_kv=False):
         line["compulsory_bytes_per_launch"] = sat.compulsory_bytes
         line["bytes_vs_bf16_kv"] = round(sat.compulsory_bytes / sat.bf16_bytes, 4)
         line["roofline"] = roofline_of(sat.flops, sat.compulsory_bytes, s_kernel,
-                                       PEAK_BF16_TFLOPS, None, None, "bsa_fwd_kernel (int8 K/V)")
+                                       PEAK_BF16_TFLOPS, s_traffic, s_mfma,
+                                       "bsa_fwd_kernel (int8 K/V)")
     elif not backward and not causal:
         line["mfma_flop_counted_per_launch"] = s_mfma
         line["mfma_counted_over_algorithmic"] = (None if s_mfma is None
@@ -695,8 +706,25 @@ def main(argv=None):
             **line}), flush=True)
         return 0
 
-    case = Case(args.workload, args.seed, device, causal=args.causal,
-                row_split=not args.no_row_split)
+    if args.backward:
+        # The backward of a forward workload on its own (profiling).
+        line = side_line(args.workload, args, device, causal=args.causal, backward=True)
+        from synthetic_inputs import WORKLOADS
+
+        w = WORKLOADS[args.workload]
+        print(json.dumps({
+            "metric": "backward " + METRIC, "value": line.pop("value"), "unit": line.pop("unit"),
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": line.pop("ms_per_step"), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded)",
+            "config": {"workload": w.name, "description": w.description, "pass": "backward"},
+            **line}), flush=True)
+        return 0
+    if args.int8_kv:
+        case = Int8KvCase(args.workload, args.seed, device)
+    else:
+        case = Case(args.workload, args.seed, device, causal=args.causal,
+                    row_split=not args.no_row_split)
     w = case.w
     for _ in range(args.warmup):
         case.step()
@@ -717,10 +745,12 @@ def main(argv=None):
     # Kernel duration: HIP events around the graph replay on its stream (the
     # launches run back to back), else the per-launch event pairs.
     kernel_s = graph_evt_s if graph_evt_s is not None else launch_s
-    traffic = None if args.causal else load_traffic(args.workload)
-    mfma_counted = None if args.causal else load_mfma(args.workload)
+    record = args.workload + ("_int8kv" if args.int8_kv else "")
+    traffic = None if args.causal else load_traffic(record)
+    mfma_counted = None if args.causal else load_mfma(record)
     roof = roofline_of(case.flops, case.compulsory_bytes, kernel_s, peak_flops, traffic,
-                       mfma_counted, "bsa_fwd_kernel")
+                       mfma_counted, "bsa_fwd_kernel (int8 K/V)" if args.int8_kv
+                       else "bsa_fwd_kernel")
     roof["per_launch_event_us"] = launch_s * 1e6
     if args.workload == "worked_example":
         # 16.9 MB of inputs and outputs stay in the L2s and the 256 MB MALL
@@ -757,6 +787,7 @@ def main(argv=None):
             "workload": w.name, "description": w.description, "B": w.B, "H": w.H, "N": w.N,
             "d": w.d, "block_size": w.block_size, "nnz_per_head": case.nnz,
             "pattern": w.pattern, "causal": bool(args.causal), "parallelism": "single GPU",
+            "kv": "int8 codes + per-block float32 scales" if args.int8_kv else w.dtype,
             "timing": "HIP graph of K launches" if graph_s is not None else "eager",
             "row_split": None if case.split is None else {
                 "heavy_rows_per_head": case.split.n_rows, "items_per_head": case.split.n_items,

@@ -135,18 +135,20 @@ struct Cfg {
   static constexpr int kSliceBytes = KS * kEntry;  // one buffer for every slice
   static_assert(L::kCopies % SW == 0, "entry parts must split evenly over a slice's waves");
   static constexpr int kParts = L::kCopies / SW;  // 1 KB copies per wave per entry
-  // Three tile buffers (prefetch distance 2) while they leave room for three
-  // workgroups per CU, else two (prefetch distance 1).  Key-split shapes keep
-  // two: their slices already run KS entries ahead together, and the smaller
-  // footprint keeps a whole small grid resident at once.
   static constexpr int kEntry8 = kEntry / 2;       // int8 K then V of one entry
   static constexpr int kSlice8 = KS * kEntry8;
   static constexpr int kPartsTile8 = BS * D / (kWave * 16);  // 1 KB parts of an int8 tile
   static_assert(!KV8 || (2 * kPartsTile8) % SW == 0, "int8 entry parts split evenly");
   static constexpr int kParts8 = 2 * kPartsTile8 / SW;       // per wave per entry
-  static constexpr int NB8 = KS == 1 && 2 * kSliceBytes + kSlice8 <= 48 * 1024 ? 3 : 2;
+  static constexpr int NB8 = KS == 1 && 2 * kSliceBytes + kSlice8 <= 40 * 1024 ? 3 : 2;
+  // Three tile buffers (prefetch distance 2) while they leave room for four
+  // workgroups per CU, else two (prefetch distance 1): at block 64 and d = 64
+  // three 16 KB buffers (48 KB, three workgroups per CU) made the random mask
+  // 6.5% slower than two (four per CU).  Key-split shapes keep two: their
+  // slices already run KS entries ahead together, and the smaller footprint
+  // keeps a whole small grid resident at once.
   // KV8: buf0 is the bf16 tile buffer, buf1 int8 slots 0 and 1, buf2 slot 2.
-  static constexpr int NB = KV8 ? 2 : (KS == 1 && 3 * kSliceBytes <= 48 * 1024 ? 3 : 2);
+  static constexpr int NB = KV8 ? 2 : (KS == 1 && 3 * kSliceBytes <= 40 * 1024 ? 3 : 2);
   static constexpr int kBuf2 = KV8 ? (NB8 == 3 ? kSlice8 : 16) : (NB == 3 ? kSliceBytes : 16);
   static constexpr int kLdsBytes = 2 * kSliceBytes + kBuf2;
   // Shapes whose buffers do not fit a workgroup's LDS are not instantiated.
