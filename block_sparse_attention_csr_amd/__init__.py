@@ -496,15 +496,17 @@ def pattern_order(ptr):
 
 def backward(q, k, v, o, lse, dout, row_ptr, col_idx, col_ptr, row_idx, block_size: int,
              scale: float | None = None, *, causal: bool = False, dq=None, dk=None, dv=None,
-             delta=None, stream=None, row_order=None, col_order=None):
+             delta=None, stream=None, row_order=None, col_order=None, per_head: bool = False):
     """Gradients (dq, dk, dv) of ``forward`` for the upstream gradient ``dout``.
 
     q, k, v, o, dout: CUDA [B, H, N, d] tensors of one dtype; lse the
     forward's LSE; row_ptr/col_idx the forward's device CSR and
     col_ptr/row_idx its device CSC (``transpose_pattern``); row_order /
     col_order optional device copies of ``pattern_order`` of the two (the
-    blocks are then taken longest first).  Enqueued on the current stream
-    (or ``stream``), not synchronised.
+    blocks are then taken longest first).  ``per_head``: row_ptr and col_ptr
+    are [H, M + 1] (``stack_head_patterns`` of each head's CSR, and of each
+    head's ``transpose_pattern``); no orders then.  Enqueued on the current
+    stream (or ``stream``), not synchronised.
     """
     import torch
 
@@ -514,9 +516,11 @@ def backward(q, k, v, o, lse, dout, row_ptr, col_idx, col_ptr, row_idx, block_si
         _check_buffer(t, name, q.shape, q.dtype, q.device)
     B, H, N, d = q.shape
     _check_buffer(lse, "lse", (B, H, N), torch.float32, q.device)
-    rows = _pattern_rows(N, int(block_size), H, False)
+    rows = _pattern_rows(N, int(block_size), H, per_head)
     _check_csr(row_ptr, col_idx, q.device, rows, col_idx.numel())
     _check_csr(col_ptr, row_idx, q.device, rows, col_idx.numel(), ("col_ptr", "row_idx"))
+    if per_head and (row_order is not None or col_order is not None):
+        raise ValueError("work orders are of one shared pattern: none with per_head")
     for t in (row_order, col_order):
         if t is not None and (t.dtype != torch.int32 or not t.is_cuda
                               or t.numel() != row_ptr.numel() - 1):
@@ -541,7 +545,8 @@ def backward(q, k, v, o, lse, dout, row_ptr, col_idx, col_ptr, row_idx, block_si
         col_ptr.data_ptr(), row_idx.data_ptr(),
         None if row_order is None else row_order.data_ptr(),
         None if col_order is None else col_order.data_ptr(), int(col_idx.numel()),
-        0.0 if scale is None else float(scale), FORWARD_CAUSAL if causal else 0,
+        0.0 if scale is None else float(scale),
+        (FORWARD_CAUSAL if causal else 0) | (FORWARD_PATTERN_PER_HEAD if per_head else 0),
         stream.cuda_stream)
     if st != BSA_OK:
         raise BsaError(st, "bsa_backward")
@@ -550,7 +555,8 @@ def backward(q, k, v, o, lse, dout, row_ptr, col_idx, col_ptr, row_idx, block_si
 
 def backward_noalloc(q, k, v, o, lse, dout, row_ptr, col_idx, col_ptr, row_idx,
                      block_size: int, dq, dk, dv, scale: float | None = None, *,
-                     causal: bool = False, stream=None, row_order=None, col_order=None):
+                     causal: bool = False, stream=None, row_order=None, col_order=None,
+                     per_head: bool = False):
     """``backward`` through bsa_backward_noalloc: the caller passes dq, dk
     and dv, and D goes to the library's static device scratch instead of a
     workspace, so the call allocates nothing on the device.  Calls that
@@ -564,9 +570,11 @@ def backward_noalloc(q, k, v, o, lse, dout, row_ptr, col_idx, col_ptr, row_idx,
         _check_buffer(t, name, q.shape, q.dtype, q.device)
     B, H, N, d = q.shape
     _check_buffer(lse, "lse", (B, H, N), torch.float32, q.device)
-    rows = _pattern_rows(N, int(block_size), H, False)
+    rows = _pattern_rows(N, int(block_size), H, per_head)
     _check_csr(row_ptr, col_idx, q.device, rows, col_idx.numel())
     _check_csr(col_ptr, row_idx, q.device, rows, col_idx.numel(), ("col_ptr", "row_idx"))
+    if per_head and (row_order is not None or col_order is not None):
+        raise ValueError("work orders are of one shared pattern: none with per_head")
     for t in (row_order, col_order):
         if t is not None and (t.dtype != torch.int32 or not t.is_cuda
                               or t.numel() != row_ptr.numel() - 1):
@@ -579,7 +587,8 @@ def backward_noalloc(q, k, v, o, lse, dout, row_ptr, col_idx, col_ptr, row_idx,
         row_ptr.data_ptr(), col_idx.data_ptr(), col_ptr.data_ptr(), row_idx.data_ptr(),
         None if row_order is None else row_order.data_ptr(),
         None if col_order is None else col_order.data_ptr(), int(col_idx.numel()),
-        0.0 if scale is None else float(scale), FORWARD_CAUSAL if causal else 0,
+        0.0 if scale is None else float(scale),
+        (FORWARD_CAUSAL if causal else 0) | (FORWARD_PATTERN_PER_HEAD if per_head else 0),
         stream.cuda_stream)
     if st != BSA_OK:
         raise BsaError(st, "bsa_backward_noalloc")
@@ -721,13 +730,13 @@ def decode_int8kv(q, k_codes, k_scales, v_codes, v_scales, seqlens, row_ptr, col
 
 def attention(q, k, v, row_ptr, col_idx, col_ptr, row_idx, block_size: int,
               scale: float | None = None, *, causal: bool = False, row_order=None,
-              col_order=None):
+              col_order=None, per_head: bool = False):
     """Block-sparse attention as a differentiable torch operation: ``forward``
     on the way in, ``backward`` (with the saved O and LSE) on the way back.
     The pattern tensors are device int32 CSR / CSC (and optional work orders,
     see ``pattern_order``).  Returns O."""
     return _Attention.apply(q, k, v, row_ptr, col_idx, col_ptr, row_idx, int(block_size),
-                            scale, bool(causal), row_order, col_order)
+                            scale, bool(causal), row_order, col_order, bool(per_head))
 
 
 def _make_attention_fn():
@@ -736,21 +745,22 @@ def _make_attention_fn():
     class _AttentionFn(torch.autograd.Function):
         @staticmethod
         def forward(ctx, q, k, v, row_ptr, col_idx, col_ptr, row_idx, block_size, scale, causal,
-                    row_order, col_order):
+                    row_order, col_order, per_head):
             q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
-            o, lse = forward(q, k, v, row_ptr, col_idx, block_size, scale, causal=causal)
+            o, lse = forward(q, k, v, row_ptr, col_idx, block_size, scale, causal=causal,
+                             per_head=per_head)
             ctx.save_for_backward(q, k, v, o, lse, row_ptr, col_idx, col_ptr, row_idx)
-            ctx.cfg = (block_size, scale, causal, row_order, col_order)
+            ctx.cfg = (block_size, scale, causal, row_order, col_order, per_head)
             return o
 
         @staticmethod
         def backward(ctx, do):
             q, k, v, o, lse, row_ptr, col_idx, col_ptr, row_idx = ctx.saved_tensors
-            block_size, scale, causal, row_order, col_order = ctx.cfg
+            block_size, scale, causal, row_order, col_order, per_head = ctx.cfg
             dq, dk, dv = backward(q, k, v, o, lse, do.contiguous(), row_ptr, col_idx, col_ptr,
                                   row_idx, block_size, scale, causal=causal,
-                                  row_order=row_order, col_order=col_order)
-            return dq, dk, dv, None, None, None, None, None, None, None, None, None
+                                  row_order=row_order, col_order=col_order, per_head=per_head)
+            return dq, dk, dv, None, None, None, None, None, None, None, None, None, None
 
     return _AttentionFn
 

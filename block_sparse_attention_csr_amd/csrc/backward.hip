@@ -62,6 +62,8 @@ struct BwdParams {
   int32_t M;
   int32_t N;
   int32_t num_wg;  // batch * heads * M
+  int32_t heads;
+  int32_t ptr_stride;  // row_ptr / col_ptr entries per head: M + 1 (one pattern per head) or 0
   float scale;
   float scale_log2;
 };
@@ -143,27 +145,18 @@ __device__ __forceinline__ float operand_dot(const typename Ops<T>::template QOp
   return s;
 }
 
-// A workgroup's list (CSR row or CSC column) in LDS, written by wave 0;
-// `list_store` returns its length and the caller synchronises.  The first 64
-// entries are loaded (`list_head`, one per lane) before the operand loads and
-// written after them: the vector-memory counter drains in order, so loaded
-// after the operands the list would wait for all of them first.
+// A workgroup's list (CSR row or CSC column): each wave reads it from the
+// index array itself, 64 entries at a time, one per lane.  The first 64 are
+// loaded before the operand loads: the vector-memory counter drains in
+// order, so loaded after the operands the first copies would wait for all of
+// them.  Later chunks (lists longer than 64 entries) are loaded when reached.
 struct ListHead {
   int start, n, first;
 };
-__device__ __forceinline__ ListHead list_head(const int32_t* idx, int start, int end, int wave,
-                                              int lane) {
+__device__ __forceinline__ ListHead list_head(const int32_t* idx, int start, int end, int lane) {
   ListHead h{start, end - start, -1};
-  if (wave == 0 && lane < h.n) h.first = idx[start + lane];
+  if (lane < h.n) h.first = idx[start + lane];
   return h;
-}
-__device__ __forceinline__ int list_store(int32_t* list, const int32_t* idx, const ListHead& h,
-                                          int wave, int lane) {
-  if (wave == 0) {
-    if (lane < h.n) list[lane] = h.first;
-    for (int t = kWave + lane; t < h.n; t += kWave) list[t] = idx[h.start + t];
-  }
-  return h.n;
 }
 
 // ---------------------------------------------------------------- dQ (and D)
@@ -178,28 +171,27 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 0>::W)) void bsa_bwd_dq(B
   __shared__ __attribute__((aligned(16))) unsigned char buf0[C::kStage];
   __shared__ __attribute__((aligned(16))) unsigned char buf1[C::kStage];
   __shared__ __attribute__((aligned(16))) unsigned char buf2[NB == 3 ? C::kStage : 16];
-  extern __shared__ __attribute__((aligned(16))) int32_t list[];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = uniform(threadIdx.x / kWave);  // 32-row query group
   const int M = p.M;
   int bh, qb;
   block_of(xcd_remap(blockIdx.x, p.num_wg), M, p.num_wg, p.row_order, p.row_ptr, bh, qb);
+  const int32_t* const row_ptr = p.row_ptr + (size_t)(bh % p.heads) * p.ptr_stride;
   const size_t head = (size_t)bh * p.N * D;
   const T* K = static_cast<const T*>(p.k) + head;
   const T* V = static_cast<const T*>(p.v) + head;
   const int q0 = qb * BS + wave * kQRows;
   const int row = q0 + (lane & 31);
 
-  const ListHead lh = list_head(p.col_idx, p.row_ptr[qb], p.row_ptr[qb + 1], wave, lane);
+  const ListHead lh = list_head(p.col_idx, row_ptr[qb], row_ptr[qb + 1], lane);
   typename O::template QOperand<D> qop, dop, oop;
   O::template load_q<D>(qop, static_cast<const T*>(p.q) + head + (size_t)q0 * D, lane);
   O::template load_q<D>(dop, static_cast<const T*>(p.dout) + head + (size_t)q0 * D, lane);
   O::template load_q<D>(oop, static_cast<const T*>(p.o) + head + (size_t)q0 * D, lane);
   const float lse2 = p.lse[(size_t)bh * p.N + row] * kLog2e;
 
-  const int U = list_store(list, p.col_idx, lh, wave, lane);
-  __syncthreads();
+  const int U = lh.n;
 
   // D for this lane's row; the lane half h = 0 stores it for bsa_bwd_dkv.
   const float dsum = halves_sum(operand_dot<T, D>(dop, oop));
@@ -215,7 +207,7 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 0>::W)) void bsa_bwd_dq(B
     if ((t & ~(kWave - 1)) != chunk_base) {
       chunk_base = t & ~(kWave - 1);
       const int idx = chunk_base + lane;
-      chunk = idx < U ? list[idx] : -1;
+      chunk = chunk_base == 0 ? lh.first : idx < U ? p.col_idx[lh.start + idx] : -1;
       chunk_sel = __builtin_amdgcn_ballot_w64(chunk >= 0 && chunk < M && (!CAUSAL || chunk <= qb));
     }
     use = ((chunk_sel >> (t - chunk_base)) & 1ull) != 0;
@@ -274,7 +266,7 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 0>::W)) void bsa_bwd_dq(B
   bool mq[NB];
 #pragma unroll
   for (int e = 0; e < NB; ++e) jq[e] = entry_at(e, mq[e]);
-  wait_vm_lgkm0<0>();  // Q, dO, O, LSE loads and the list are complete
+  wait_vm_lgkm0<0>();  // Q, dO, O, LSE loads and the first entries are complete
   // The first copies, for the entries there are (none for an empty list).
   if (U > 0) issue(jq[0], buf0);
   if (NB == 3 && U > 1) issue(jq[1], buf1);
@@ -328,13 +320,13 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 8 * BS>::W)) void bsa_bwd
   __shared__ __attribute__((aligned(16))) unsigned char buf0[C::kStage];
   __shared__ __attribute__((aligned(16))) unsigned char buf1[C::kStage];
   __shared__ __attribute__((aligned(16))) unsigned char buf2[NB == 3 ? C::kStage : 16];
-  extern __shared__ __attribute__((aligned(16))) int32_t list[];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = uniform(threadIdx.x / kWave);  // 32-key group
   const int M = p.M;
   int bh, kb;
   block_of(xcd_remap(blockIdx.x, p.num_wg), M, p.num_wg, p.col_order, p.col_ptr, bh, kb);
+  const int32_t* const col_ptr = p.col_ptr + (size_t)(bh % p.heads) * p.ptr_stride;
   const size_t head = (size_t)bh * p.N * D;
   const T* Qh = static_cast<const T*>(p.q) + head;
   const T* dOh = static_cast<const T*>(p.dout) + head;
@@ -342,13 +334,12 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 8 * BS>::W)) void bsa_bwd
   const float* del_h = p.delta + (size_t)bh * p.N;
   const int k0 = kb * BS + wave * kQRows;
 
-  const ListHead lh = list_head(p.row_idx, p.col_ptr[kb], p.col_ptr[kb + 1], wave, lane);
+  const ListHead lh = list_head(p.row_idx, col_ptr[kb], col_ptr[kb + 1], lane);
   typename O::template QOperand<D> kop, vop;
   O::template load_q<D>(kop, static_cast<const T*>(p.k) + head + (size_t)k0 * D, lane);
   O::template load_q<D>(vop, static_cast<const T*>(p.v) + head + (size_t)k0 * D, lane);
 
-  const int U = list_store(list, p.row_idx, lh, wave, lane);
-  __syncthreads();
+  const int U = lh.n;
 
   int chunk_base = -kWave, chunk = -1;
   uint64_t chunk_sel = 0;
@@ -360,7 +351,7 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 8 * BS>::W)) void bsa_bwd
     if ((t & ~(kWave - 1)) != chunk_base) {
       chunk_base = t & ~(kWave - 1);
       const int idx = chunk_base + lane;
-      chunk = idx < U ? list[idx] : -1;
+      chunk = chunk_base == 0 ? lh.first : idx < U ? p.row_idx[lh.start + idx] : -1;
       chunk_sel = __builtin_amdgcn_ballot_w64(chunk >= 0 && chunk < M && (!CAUSAL || chunk >= kb));
     }
     use = ((chunk_sel >> (t - chunk_base)) & 1ull) != 0;
@@ -488,10 +479,8 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 8 * BS>::W)) void bsa_bwd
 
 template <typename T, int BS, int D, bool CAUSAL>
 bsa_status launch_bwd(const BwdParams& p, hipStream_t stream) {
-  const size_t list_bytes = 4 * (size_t)p.M;
   const dim3 grid(p.num_wg);
   const dim3 block(kWave * (BS / kQRows));
-  if (list_bytes > 16 * 1024) return BSA_ERR_SHAPE;  // M > 4096 blocks: list does not fit
   // Shapes with more than 64 KB of LDS need the per-kernel limit raised, once
   // per device.
   static std::atomic<uint64_t> raised{0};
@@ -502,16 +491,16 @@ bsa_status launch_bwd(const BwdParams& p, hipStream_t stream) {
     for (const void* f : kernels) {
       hipFuncAttributes attr;
       if (hipFuncGetAttributes(&attr, f) != hipSuccess) return BSA_ERR_HIP;
-      if (attr.sharedSizeBytes + 16 * 1024 > 64 * 1024 &&
+      if (attr.sharedSizeBytes > 64 * 1024 &&
           hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
                               static_cast<int>(160 * 1024 - attr.sharedSizeBytes)) != hipSuccess)
         return BSA_ERR_HIP;
     }
     mark_done(raised, bit);
   }
-  hipLaunchKernelGGL((bsa_bwd_dq<T, BS, D, CAUSAL>), grid, block, list_bytes, stream, p);
+  hipLaunchKernelGGL((bsa_bwd_dq<T, BS, D, CAUSAL>), grid, block, 0, stream, p);
   if (hipGetLastError() != hipSuccess) return BSA_ERR_HIP;
-  hipLaunchKernelGGL((bsa_bwd_dkv<T, BS, D, CAUSAL>), grid, block, list_bytes, stream, p);
+  hipLaunchKernelGGL((bsa_bwd_dkv<T, BS, D, CAUSAL>), grid, block, 0, stream, p);
   return hipGetLastError() == hipSuccess ? BSA_OK : BSA_ERR_HIP;
 }
 
@@ -549,11 +538,16 @@ bsa_status backward_impl(const void* q, const void* k, const void* v, const void
   if (dtype != BSA_DTYPE_F32 && dtype != BSA_DTYPE_BF16) return BSA_ERR_INVALID_ARGUMENT;
   if (block_size != 32 && block_size != 64) return BSA_ERR_INVALID_ARGUMENT;
   if (head_dim != 64 && head_dim != 128) return BSA_ERR_INVALID_ARGUMENT;
-  if ((flags & ~BSA_FORWARD_CAUSAL) != 0) return BSA_ERR_INVALID_ARGUMENT;
+  if ((flags & ~(BSA_FORWARD_CAUSAL | BSA_FORWARD_PATTERN_PER_HEAD)) != 0)
+    return BSA_ERR_INVALID_ARGUMENT;
+  const bool per_head = (flags & BSA_FORWARD_PATTERN_PER_HEAD) != 0;
+  // one pattern per head: the work orders are of one shared pattern
+  if (per_head && (row_order != nullptr || col_order != nullptr)) return BSA_ERR_INVALID_ARGUMENT;
   if (batch <= 0 || heads <= 0 || seq_len <= 0 || seq_len % block_size != 0) return BSA_ERR_SHAPE;
   if (!(scale == scale) || std::isinf(scale)) return BSA_ERR_INVALID_ARGUMENT;
   const int64_t M = seq_len / block_size;
-  if (nnz < M || nnz > M * M || M > 4096) return BSA_ERR_SHAPE;
+  const int64_t patterns = per_head ? heads : 1;
+  if (nnz < patterns * M || nnz > patterns * M * M) return BSA_ERR_SHAPE;
   const int64_t num_wg = (int64_t)batch * heads * M;
   if ((int64_t)batch * heads * seq_len > INT32_MAX || num_wg > INT32_MAX) return BSA_ERR_SHAPE;
   const uintptr_t align = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
@@ -584,6 +578,8 @@ bsa_status backward_impl(const void* q, const void* k, const void* v, const void
   p.M = static_cast<int32_t>(M);
   p.N = seq_len;
   p.num_wg = static_cast<int32_t>(num_wg);
+  p.heads = heads;
+  p.ptr_stride = per_head ? static_cast<int32_t>(M + 1) : 0;
   p.scale = scale > 0.f ? scale : 1.0f / std::sqrt(static_cast<float>(head_dim));
   p.scale_log2 = p.scale * kLog2e;
   const bool causal = (flags & BSA_FORWARD_CAUSAL) != 0;

@@ -299,23 +299,27 @@ bsa_status bsa_transpose_pattern(int32_t M, const int32_t* row_ptr, const int32_
  * delta    device, caller-owned float32 [batch, heads, seq_len]: workspace
  *          (receives D).
  * row_ptr, col_idx  device copies of the forward's CSR pattern;
- * col_ptr, row_idx  device copies of its bsa_transpose_pattern.
+ * col_ptr, row_idx  device copies of its bsa_transpose_pattern.  With
+ *          BSA_FORWARD_PATTERN_PER_HEAD both are [heads, M + 1] offsets into
+ *          one index array each (head h's CSC the transpose of head h's CSR).
  * row_order, col_order  device int32[M] or NULL: bsa_pattern_order of the
  *          CSR (row_ptr) and of the CSC (col_ptr).  With them each kernel
  *          starts its long blocks first (the anchors' columns and dense rows
  *          hold every block; started last they would run alone at the end);
  *          NULL takes blocks in ascending order.  The result is the same
  *          either way.  An order must be a permutation of 0 .. M-1 (the
- *          kernels read it as given).
+ *          kernels read it as given).  Both NULL with one pattern per head.
  * nnz      the pattern's entry count (host).
  * scale    as for bsa_forward (<= 0: 1 / sqrt(head_dim)).
- * flags    0 or BSA_FORWARD_CAUSAL (the forward's causal masking).
+ * flags    0, BSA_FORWARD_CAUSAL (the forward's causal masking) and/or
+ *          BSA_FORWARD_PATTERN_PER_HEAD (one pattern per head, as for
+ *          bsa_forward_ex).
  * stream   a hipStream_t or NULL; two launches are enqueued (dQ and D,
  *          then dK and dV), without synchronising.
  *
- * Supported: dtype BF16 or F32, block_size 32 or 64, head_dim 64 or 128,
- * M = seq_len / block_size <= 4096.  Errors as for bsa_forward; unknown
- * flags (including BSA_FORWARD_PATTERN_PER_HEAD) are BSA_ERR_INVALID_ARGUMENT.
+ * Supported: dtype BF16 or F32, block_size 32 or 64, head_dim 64 or 128.
+ * Errors as for bsa_forward; unknown flags, and orders with
+ * BSA_FORWARD_PATTERN_PER_HEAD, are BSA_ERR_INVALID_ARGUMENT.
  */
 bsa_status bsa_backward(const void* q, const void* k, const void* v, const void* o,
                         const float* lse, const void* dout, void* dq, void* dk, void* dv,

@@ -214,3 +214,70 @@ def test_backward_largest_block_count_invariants():
     tol = 2.0 ** -8 * N ** 0.5
     assert e_dv <= tol
     assert e_dk <= tol
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dt,bs,d", [("bf16", 32, 64), ("bf16", 64, 128), ("f32", 64, 64)])
+def test_backward_per_head_patterns(dt, bs, d, causal):
+    """One pattern per head (the log-linear page's section 2.2 speaks of
+    per-head patterns): row_ptr and col_ptr are [H, M + 1], each head's CSC
+    the transpose of its CSR; dQ, dK, dV against the oracle with [H, M, M]
+    masks, through bsa_backward and bsa_backward_noalloc."""
+    dtype = torch.bfloat16 if dt == "bf16" else torch.float32
+    B, H, M = 2, 4, 10
+    N = bs * M
+    q, k, v = make_qkv(B, H, N, d, dtype, 91)
+    do = make_qkv(B, H, N, d, dtype, 92)[0]
+    masks = [random_block_mask(M, 0.3 + 0.15 * h, 93 + h) for h in range(H)]
+    csrs = [bsa.build_pattern(N, bs, mask=m, causal=causal) for m in masks]
+    cscs = [bsa.transpose_pattern(rp, ci) for rp, ci in csrs]
+    rp, ci = bsa.stack_head_patterns(csrs)
+    cp, ri = bsa.stack_head_patterns(cscs)
+    dev = torch.device("cuda")
+    t = [x.to(dev) for x in (q, k, v, do)]
+    pat = [x.to(dev) for x in (rp, ci, cp, ri)]
+    o, lse = bsa.forward(t[0], t[1], t[2], pat[0], pat[1], bs, causal=causal, per_head=True)
+    grads = bsa.backward(t[0], t[1], t[2], o, lse, t[3], *pat, bs, causal=causal, per_head=True)
+    out = [torch.empty_like(t[0]) for _ in range(3)]
+    grads2 = bsa.backward_noalloc(t[0], t[1], t[2], o, lse, t[3], *pat, bs, *out, causal=causal,
+                                  per_head=True)
+    torch.cuda.synchronize()
+    ref = oracle.block_sparse_attention_backward(_f64(q), _f64(k), _f64(v), _f64(do),
+                                                 np.stack(masks), bs, causal=causal)
+    for name, got, want, again in zip(("dQ", "dK", "dV"), grads, ref[:3], grads2):
+        _check(f"{name} {dt} bs{bs} d{d} causal={causal}", got, want, dtype)
+        assert torch.equal(got, again), name
+    with pytest.raises(ValueError):  # orders are of one shared pattern
+        bsa.backward(t[0], t[1], t[2], o, lse, t[3], *pat, bs, per_head=True,
+                     row_order=torch.zeros(M, dtype=torch.int32, device=dev))
+
+
+def test_backward_more_than_4096_blocks_sampled():
+    """M = 8192 query blocks (N = 262144 at block 32), beyond what an LDS entry
+    list held: a banded pattern of independent groups of four blocks, so that
+    the gradients of the tokens of one group equal the dense backward of that
+    128-token segment alone.  Sampled groups (first, middle, last) against
+    the oracle on their segment."""
+    B, H, d, bs, M = 1, 1, 64, 32, 8192
+    N = M * bs
+    q, k, v = make_qkv(B, H, N, d, torch.bfloat16, 97)
+    do = make_qkv(B, H, N, d, torch.bfloat16, 98)[0]
+    i = np.arange(M)
+    rows = [list(range(4 * (r // 4), 4 * (r // 4) + 4)) for r in range(M)]
+    rp = torch.tensor(np.concatenate([[0], np.cumsum([len(r) for r in rows])]), dtype=torch.int32)
+    ci = torch.tensor([j for r in rows for j in r], dtype=torch.int32)
+    cp, ri = bsa.transpose_pattern(rp, ci)
+    dev = torch.device("cuda")
+    t = [x.to(dev) for x in (q, k, v, do)]
+    pat = [x.to(dev) for x in (rp, ci, cp, ri)]
+    o, lse = bsa.forward(t[0], t[1], t[2], pat[0], pat[1], bs)
+    dq, dk, dv = bsa.backward(t[0], t[1], t[2], o, lse, t[3], *pat, bs)
+    torch.cuda.synchronize()
+    assert len(i) == M
+    ones = np.ones((4, 4), np.uint8)
+    for g in (0, 1, M // 8, M // 4 - 1):
+        seg = slice(g * 128, (g + 1) * 128)
+        f = lambda x: _f64(x[:, :, seg])
+        ref = oracle.block_sparse_attention_backward(f(q), f(k), f(v), f(do), ones, bs)
+        for name, got, want in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref[:3]):
+            _check(f"{name} group {g}", got[:, :, seg], want, torch.bfloat16)
