@@ -124,15 +124,20 @@ constexpr int half_partial_bytes() {
 // Compile-time shape of one kernel instantiation.  KV8: K and V are int8
 // codes; each entry lands as int8 in one of NB8 slots (copies NB8 - 1
 // entries ahead) and is converted to bf16 into the one tile buffer the math
-// reads.
-template <typename T, int BS, int D, int G, int KS, bool KV8 = false>
+// reads.  RING: a one-block, one-slice shape keeps the two-entry ring (the
+// row-split pass: few workgroups, each with a long run of entries).
+template <typename T, int BS, int D, int G, int KS, bool KV8 = false, bool RING = false>
 struct Cfg {
   using L = TileLayout<T, BS, D>;
   static constexpr int QW = BS / kQRows;  // query waves per query block
   static constexpr int SW = QW * G;       // waves per key slice
   static constexpr int W = SW * KS;       // waves per workgroup
   static constexpr int kEntry = L::kEntryBytes;
-  static constexpr int kSliceBytes = KS * kEntry;  // one buffer for every slice
+  // bf16 at block 64 with one query block and one key slice: one K slot and
+  // one V slot (a tile each), not two whole entries (see the kernel's loop).
+  static constexpr bool kSingle =
+      std::is_same<T, __bf16>::value && !KV8 && !RING && BS == 64 && G == 1 && KS == 1;
+  static constexpr int kSliceBytes = kSingle ? L::kTileBytes : KS * kEntry;  // per buffer
   static_assert(L::kCopies % SW == 0, "entry parts must split evenly over a slice's waves");
   static constexpr int kParts = L::kCopies / SW;  // 1 KB copies per wave per entry
   static constexpr int kEntry8 = kEntry / 2;       // int8 K then V of one entry
@@ -148,7 +153,7 @@ struct Cfg {
   // slices already run KS entries ahead together, and the smaller footprint
   // keeps a whole small grid resident at once.
   // KV8: buf0 is the bf16 tile buffer, buf1 int8 slots 0 and 1, buf2 slot 2.
-  static constexpr int NB = KV8 ? 2 : (KS == 1 && 3 * kSliceBytes <= 40 * 1024 ? 3 : 2);
+  static constexpr int NB = KV8 || kSingle ? 2 : (KS == 1 && 3 * kSliceBytes <= 40 * 1024 ? 3 : 2);
   static constexpr int kBuf2 = KV8 ? (NB8 == 3 ? kSlice8 : 16) : (NB == 3 ? kSliceBytes : 16);
   static constexpr int kLdsBytes = 2 * kSliceBytes + kBuf2;
   // Shapes whose buffers do not fit a workgroup's LDS are not instantiated.
@@ -158,9 +163,11 @@ struct Cfg {
                                  (KS != 2 || 2 * SW * half_partial_bytes<D>() <= kSliceBytes);
 };
 
-template <typename T, int BS, int D, int G, int KS, bool CAUSAL, bool KV8 = false>
-__global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS, KV8>::W)) void bsa_fwd_kernel(FwdParams p) {
-  using C = Cfg<T, BS, D, G, KS, KV8>;
+template <typename T, int BS, int D, int G, int KS, bool CAUSAL, bool KV8 = false,
+          bool RING = false>
+__global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS, KV8, RING>::W)) void bsa_fwd_kernel(
+    FwdParams p) {
+  using C = Cfg<T, BS, D, G, KS, KV8, RING>;
   using L = typename C::L;
   using O = Ops<T>;
   constexpr int QW = C::QW;
@@ -438,8 +445,17 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS, KV8>::W)) void bsa_fw
   // into the score factor; and the product runs on P sv, sv folded into the
   // exponent, while the row sum takes P = (P sv) / sv.  A zero scale (an
   // all-zero block, codes 0) may take any value: 1.
-  auto compute = [&](unsigned char* buf, bool diag, float sk = 1.f, float sv = 1.f) {
-    LDS_PTR(unsigned char) tile = (LDS_PTR(unsigned char))buf;
+  // The scores of an entry whose K tile sits at byte `kpos` of `ktile`.
+  auto scores_of = [&](unsigned char* ktile, int kpos, f32x16_t (&sc)[KSTEPS]) {
+    LDS_PTR(unsigned char) tile = (LDS_PTR(unsigned char))ktile;
+#pragma unroll
+    for (int st = 0; st < KSTEPS; ++st) sc[st] = O::template scores<BS, D>(qop, off, tile, kpos, st);
+  };
+  // Softmax and P.V of an entry from its scores; its V tile sits at byte
+  // `vpos` + (a tile) of `vtile` (as in a K-then-V entry at `vpos`).
+  auto softmax_pv = [&](f32x16_t (&sc)[KSTEPS], unsigned char* vtile, int vpos, bool diag,
+                        float sk, float sv) {
+    LDS_PTR(unsigned char) tile = (LDS_PTR(unsigned char))vtile;
     const float c2k = KV8 ? c2 * (sk > 0.f ? sk : 1.f) : c2;
     float lsv = 0.f, isv = 1.f;
     if constexpr (KV8) {
@@ -447,9 +463,6 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS, KV8>::W)) void bsa_fw
       lsv = __builtin_amdgcn_logf(sve);
       isv = __builtin_amdgcn_rcpf(sve);
     }
-    f32x16_t sc[KSTEPS];
-#pragma unroll
-    for (int st = 0; st < KSTEPS; ++st) sc[st] = O::template scores<BS, D>(qop, off, tile, 0, st);
 #pragma unroll
     for (int st = 0; st < KSTEPS; ++st) {
       if (diag && st > qg) continue;
@@ -477,9 +490,14 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS, KV8>::W)) void bsa_fw
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) sc[st][r] = fast_exp2(fmaf(sc[st][r], c2k, KV8 ? lsv - m2 : -m2));
-      const float ps = O::template accumulate<BS, D>(o, sc[st], off, tile, 0, st);
+      const float ps = O::template accumulate<BS, D>(o, sc[st], off, tile, vpos, st);
       lsum = KV8 ? fmaf(ps, isv, lsum) : lsum + ps;
     }
+  };
+  auto compute = [&](unsigned char* buf, bool diag, float sk = 1.f, float sv = 1.f) {
+    f32x16_t sc[KSTEPS];
+    scores_of(buf, 0, sc);
+    softmax_pv(sc, buf, 0, diag, sk, sv);
   };
 
   // ---- pipeline: entry i computes from buffer i % NB while the copies of
@@ -493,7 +511,57 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS, KV8>::W)) void bsa_fw
   // 1's copies land over them).  Uncoupled, the slices no longer wait for
   // each other at every entry (worked example 1-2% faster, graph-timed).
   constexpr bool kSliceBarrier = G > 1 || SW > 1;
-  if constexpr (!KV8) {
+  if constexpr (C::kSingle) {
+    // One K slot (buf0) and one V slot (buf1), each a tile.  Step i: every
+    // wave waits for its copies of K[i] and its reads of V[i-1]; a barrier;
+    // the copies of V[i]; the scores of entry i (K slot); every wave waits
+    // for its copies of V[i] and its K reads; a barrier; the copies of
+    // K[i+1]; softmax and P.V of entry i (V slot).  Each copy lands while
+    // the other half of the step runs.  Half the LDS of a two-entry ring lets
+    // twice the workgroups share a CU, so one query block per workgroup
+    // (no wave idles on another row's entries) keeps two waves per SIMD.
+    constexpr int kTile = L::kTileBytes;
+    constexpr int kPartsT = kPartsPerTile / SW;  // 1 KB copies per wave per tile
+    int toff[kPartsT];
+#pragma unroll
+    for (int c = 0; c < kPartsT; ++c) {
+      const int slot = (ws + c * SW) * kWave + lane;
+      const int row = slot / L::kChunksPerRow;
+      toff[c] = row * L::kRowBytes + (((slot % L::kChunksPerRow) ^ L::swz(row)) << 4);
+    }
+    const uint32_t kslot = (uint32_t)(uintptr_t)(LDS_PTR(unsigned char))buf0;
+    const uint32_t vslot = (uint32_t)(uintptr_t)(LDS_PTR(unsigned char))buf1;
+    auto issue_tile = [&](const T* src, int j, uint32_t dst) {
+      const int key0 = (j < 0 || j >= M ? 0 : j) * BS;  // a missing entry copies block 0 (unused)
+#pragma unroll
+      for (int c = 0; c < kPartsT; ++c)
+        lds_dma16(src + (size_t)key0 * D, (uint32_t)toff[c], dst + (ws + c * SW) * kWave * 16);
+    };
+    bool m0, m1;
+    int j0 = entry_at(0, m0);
+    wait_vm_lgkm0<0>();  // the Q loads (see the ring below)
+    if (niter > 0) issue_tile(K, j0, kslot);
+    if constexpr (kStageQ) {  // Q sits in the V slot: read before step 0's barrier
+      LDS_PTR(const unsigned char) qs = (LDS_PTR(const unsigned char))q_stage;
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c)
+        qop.r[c] = *(LDS_PTR(const u32x4_t))(qs + QL::chunk_offset(lane & 31, 2 * c + (lane >> 5)));
+    }
+    for (int i = 0; i < niter; ++i) {
+      const int j1 = entry_at(i + 1, m1);
+      wait_vm_lgkm0<0>();
+      raw_barrier();
+      issue_tile(V, j0, vslot);
+      f32x16_t sc[KSTEPS];
+      if (m0) scores_of(buf0, 0, sc);
+      wait_vm_lgkm0<0>();
+      raw_barrier();
+      if (i + 1 < niter) issue_tile(K, j1, kslot);
+      if (m0) softmax_pv(sc, buf1, -kTile, causal && j0 == qb, 1.f, 1.f);
+      j0 = j1;
+      m0 = m1;
+    }
+  } else if constexpr (!KV8) {
     int jq[NB];   // blocks of steps i .. i + NB - 1
     bool mq[NB];  // whether this wave computes them
   #pragma unroll
@@ -808,19 +876,19 @@ size_t dynamic_lds_bytes(int group, int M) {
   return 4 * ((size_t)M + words);
 }
 
-template <typename T, int BS, int D, int G, int KS, bool KV8 = false>
+template <typename T, int BS, int D, int G, int KS, bool KV8 = false, bool RING = false>
 constexpr size_t static_lds_bytes() {  // 0 for a shape that is not instantiated
-  using C = Cfg<T, BS, D, G, KS, KV8>;
+  using C = Cfg<T, BS, D, G, KS, KV8, RING>;
   return C::kValid ? (size_t)C::kLdsBytes + 16 : 0;
 }
 
-template <typename T, int BS, int D, int G, int KS, bool CAUSAL, bool KV8>
+template <typename T, int BS, int D, int G, int KS, bool CAUSAL, bool KV8, bool RING = false>
 bsa_status launch_kernel(const FwdParams& p, hipStream_t stream) {
-  using C = Cfg<T, BS, D, G, KS, KV8>;
+  using C = Cfg<T, BS, D, G, KS, KV8, RING>;
   if constexpr (!C::kValid) {
     return BSA_ERR_INVALID_ARGUMENT;
   } else {
-  constexpr size_t kStatic = static_lds_bytes<T, BS, D, G, KS, KV8>();
+  constexpr size_t kStatic = static_lds_bytes<T, BS, D, G, KS, KV8, RING>();
   const size_t dyn = dynamic_lds_bytes(G, p.M);
   if (dyn + kStatic > kMaxLds) return BSA_ERR_INVALID_ARGUMENT;
   if (dyn + kStatic > 64 * 1024) {
@@ -828,7 +896,7 @@ bsa_status launch_kernel(const FwdParams& p, hipStream_t stream) {
     uint64_t bit;
     if (due_on_device(raised, &bit)) {
       if (hipFuncSetAttribute(
-              reinterpret_cast<const void*>(&bsa_fwd_kernel<T, BS, D, G, KS, CAUSAL, KV8>),
+              reinterpret_cast<const void*>(&bsa_fwd_kernel<T, BS, D, G, KS, CAUSAL, KV8, RING>),
               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kMaxLds - kStatic)) !=
           hipSuccess)
         return BSA_ERR_HIP;
@@ -837,7 +905,7 @@ bsa_status launch_kernel(const FwdParams& p, hipStream_t stream) {
   }
   const dim3 block(kWave * C::W);
   const dim3 grid(p.num_wg);
-  hipLaunchKernelGGL((bsa_fwd_kernel<T, BS, D, G, KS, CAUSAL, KV8>), grid, block, dyn, stream,
+  hipLaunchKernelGGL((bsa_fwd_kernel<T, BS, D, G, KS, CAUSAL, KV8, RING>), grid, block, dyn, stream,
                      p);
   return hipGetLastError() == hipSuccess ? BSA_OK : BSA_ERR_HIP;
   }
@@ -851,6 +919,11 @@ bsa_status launch(const FwdParams& p, hipStream_t stream) {
                            : launch_kernel<T, BS, D, G, KS, false, true>(p, stream);
     else
       return BSA_ERR_INVALID_ARGUMENT;
+  }
+  if constexpr (Cfg<T, BS, D, G, KS>::kSingle) {
+    if (p.split != nullptr)  // the row-split pass keeps the two-entry ring
+      return p.causal != 0 ? launch_kernel<T, BS, D, G, KS, true, false, true>(p, stream)
+                           : launch_kernel<T, BS, D, G, KS, false, false, true>(p, stream);
   }
   return p.causal != 0 ? launch_kernel<T, BS, D, G, KS, true, false>(p, stream)
                        : launch_kernel<T, BS, D, G, KS, false, false>(p, stream);
@@ -957,7 +1030,7 @@ int64_t device_cus() {
 // (the worked example, 1024 query blocks of one wave, runs 9.2 us with KS = 2
 // against 9.8 us with KS = 1).
 void choose_shape(int64_t bhm, int bs, int d, int dtype, int M, int* group, int* key_split,
-                  bool kv8 = false) {
+                  bool kv8 = false, bool banded = false) {
   const int64_t kCus = device_cus();
   const int64_t kLargeGrid = 8 * 4 * kCus;  // 8 query waves per SIMD
   const int qw = bs / kQRows;
@@ -967,7 +1040,14 @@ void choose_shape(int64_t bhm, int bs, int d, int dtype, int M, int* group, int*
   };
   int g = 1, ks = 1;
   if (bhm * qw >= kLargeGrid) {
-    g = bs == 32 ? 4 : 2;
+    // bf16 at block 64 keeps one query block per workgroup: its one-tile K
+    // and V slots already hold two waves per SIMD, while two rows per
+    // workgroup make each wave idle through the entries only the other row
+    // selects (29% of the steps of the log-linear pattern at M = 512, 42% of
+    // a Bernoulli(0.3) mask's at M = 32).  A banded pattern (dense rows taken
+    // by a row split) is the exception: neighbouring rows share nearly every
+    // block, and two rows per workgroup halve its copies.
+    g = bs == 32 ? 4 : (dtype == BSA_DTYPE_BF16 && !kv8 && !banded ? 1 : 2);
     if (!fits(g, 1)) g = 1;
   } else {
     while (ks < 4 && qw * ks * 2 <= kMaxWaves && bhm * qw * ks * 2 <= 2 * 4 * kCus &&
@@ -1062,7 +1142,7 @@ bsa_status forward_impl(const void* q, const void* k, const void* v, void* o, fl
   }
   if (group == 0 && key_split == 0) {
     choose_shape((int64_t)batch * heads * M, block_size, head_dim, dtype, (int)M, &p.group,
-                 &p.key_split, kv8);
+                 &p.key_split, kv8, split);
   } else {
     const int qw = block_size / kQRows;
     if (qw * group * key_split > kMaxWaves) return BSA_ERR_INVALID_ARGUMENT;
