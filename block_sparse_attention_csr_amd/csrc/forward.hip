@@ -435,9 +435,9 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS, KV8, RING>::W)) void 
   bool first = true;     // no block computed yet by this wave
   const float c2 = p.scale_log2;
 
-  // One entry: all S^T tiles are issued first; each 32-key step then runs its
-  // softmax (VALU) while the MFMAs of the later steps are still in flight,
-  // and its P.V while the next step's softmax runs.
+  // One entry: all S^T tiles are issued first (the steps' MFMA chains
+  // interleaved); then one running-max update for the whole entry, and each
+  // 32-key step's exponentials (VALU) run beside the previous step's P.V.
   // `diag`: the entry is this wave's own query block under causal masking.
   // Its 32-key steps after the wave's 32 rows are skipped, the step level
   // with them is masked above the diagonal (the keys after each query).
@@ -448,8 +448,12 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS, KV8, RING>::W)) void 
   // The scores of an entry whose K tile sits at byte `kpos` of `ktile`.
   auto scores_of = [&](unsigned char* ktile, int kpos, f32x16_t (&sc)[KSTEPS]) {
     LDS_PTR(unsigned char) tile = (LDS_PTR(unsigned char))ktile;
+    if constexpr (std::is_same<T, __bf16>::value) {
+      O::template scores_steps<BS, D, KSTEPS>(qop, off, tile, kpos, sc);
+    } else {
 #pragma unroll
-    for (int st = 0; st < KSTEPS; ++st) sc[st] = O::template scores<BS, D>(qop, off, tile, kpos, st);
+      for (int st = 0; st < KSTEPS; ++st) sc[st] = O::template scores<BS, D>(qop, off, tile, kpos, st);
+    }
   };
   // Softmax and P.V of an entry from its scores; its V tile sits at byte
   // `vpos` + (a tile) of `vtile` (as in a K-then-V entry at `vpos`).
@@ -463,31 +467,40 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS, KV8, RING>::W)) void 
       lsv = __builtin_amdgcn_logf(sve);
       isv = __builtin_amdgcn_rcpf(sve);
     }
+    // One running-max update per entry, over all of its 32-key steps: one
+    // ballot and one (rarely taken) rescale branch per entry, and the steps'
+    // exponentials and P.V products in one straight run of code.
+    if (diag) {  // keys after each query of the diagonal step are masked
+      const int qrow = lane & 31;
+      const int h = lane >> 5;
+#pragma unroll
+      for (int st = 0; st < KSTEPS; ++st)
+        if (st == qg)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (8 * (r / 4) + 4 * h + (r % 4) > qrow) sc[st][r] = -INFINITY;
+    }
+    float mx = sc[0][0];
+#pragma unroll
+    for (int st = 0; st < KSTEPS; ++st)
+      if (st == 0 || !diag || st <= qg)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = __builtin_elementwise_maximum(mx, sc[st][r]);
+    mx = halves_max(mx) * c2k;
+    if (first) {  // O and l are still zero: no rescale
+      m2 = mx;
+      first = false;
+    } else if (__builtin_amdgcn_ballot_w64(mx > m2 + kLazyRescale) != 0) {
+      const float m_new = fmaxf(m2, mx);
+      const float alpha = fast_exp2(m2 - m_new);
+      m2 = m_new;
+      lsum *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
+    }
 #pragma unroll
     for (int st = 0; st < KSTEPS; ++st) {
       if (diag && st > qg) continue;
-      if (diag && st == qg) {
-        const int qrow = lane & 31;
-        const int h = lane >> 5;
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (8 * (r / 4) + 4 * h + (r % 4) > qrow) sc[st][r] = -INFINITY;
-      }
-      float mx = sc[st][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = __builtin_elementwise_maximum(mx, sc[st][r]);
-      mx = halves_max(mx) * c2k;
-      if (first) {  // O and l are still zero: no rescale
-        m2 = mx;
-        first = false;
-      } else if (__builtin_amdgcn_ballot_w64(mx > m2 + kLazyRescale) != 0) {
-        const float m_new = fmaxf(m2, mx);
-        const float alpha = fast_exp2(m2 - m_new);
-        m2 = m_new;
-        lsum *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
-      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) sc[st][r] = fast_exp2(fmaf(sc[st][r], c2k, KV8 ? lsv - m2 : -m2));
       const float ps = O::template accumulate<BS, D>(o, sc[st], off, tile, vpos, st);

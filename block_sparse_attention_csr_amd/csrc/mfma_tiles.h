@@ -170,6 +170,30 @@ struct Ops<__bf16> {
     return s;
   }
 
+  // S^T of all NS 32-key steps of the entry with the steps' chains
+  // interleaved: feature chunk c of every step, then chunk c + 1, so that
+  // independent accumulators alternate and each K read has more MFMAs ahead
+  // of its use to land.
+  template <int BS, int D, int NS>
+  static __device__ __forceinline__ void scores_steps(const QOperand<D>& q,
+                                                      const Offsets<BS, D>& off,
+                                                      LDS_PTR(unsigned char) lds, int entry,
+                                                      f32x16_t (&s)[NS]) {
+    using L = TileLayout<__bf16, BS, D>;
+#pragma unroll
+    for (int st = 0; st < NS; ++st) s[st] = f32x16_t{};
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        const u32x4_t k = *(LDS_PTR(const u32x4_t))(lds + off.k[c] + entry +
+                                                    st * kKeyStep * L::kRowBytes);
+        s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, k),
+                                                        __builtin_bit_cast(bf16x8_t, q.r[c]),
+                                                        s[st], 0, 0, 0);
+      }
+  }
+
   // V^T operand of step st, 16-key sub-step sc, feature tile dt: lane
   // (feature = 32 dt + lane % 32, half h) holds V[key][feature] for keys
   // kappa(h, j) = 32 st + 16 sc + 8 (j / 4) + 4 h + j % 4, j = 0..7: two
