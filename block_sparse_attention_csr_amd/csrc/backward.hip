@@ -68,16 +68,19 @@ struct BwdParams {
   float scale_log2;
 };
 
-// (batch*head, block) of a workgroup.  Workgroup ids run XCD by XCD (each XCD
-// one contiguous range of HX heads, so one head's blocks share an L2).  With
-// an order array (bsa_pattern_order: the long blocks -- more than twice the
-// mean entry count -- first, then the rest ascending), a range starts with
-// the long blocks of all its heads, then takes the rest head by head.
-__device__ __forceinline__ void block_of(int wg, int M, int num_wg, const int32_t* order,
-                                         const int32_t* ptr, int& bh, int& blk) {
+// (batch*head, group) of a workgroup: group k holds the G blocks
+// order[kG .. kG + G) (or kG .. kG + G without an order array; blocks past M
+// are absent).  Workgroup ids run XCD by XCD (each XCD one contiguous range
+// of HX heads, so one head's blocks share an L2).  With an order array
+// (bsa_pattern_order: the long blocks -- more than twice the mean entry
+// count -- first, then the rest ascending), a range starts with the groups
+// that hold long blocks, for all its heads, then takes the rest head by head.
+__device__ __forceinline__ void group_of(int wg, int M, int G, int num_wg, const int32_t* order,
+                                         const int32_t* ptr, int& bh, int& grp) {
+  const int NG = (M + G - 1) / G;
   if (order == nullptr) {
-    blk = wg % M;
-    bh = wg / M;
+    grp = wg % NG;
+    bh = wg / NG;
     return;
   }
   // Number of long blocks: the leading entries of `order` whose count exceeds
@@ -93,32 +96,101 @@ __device__ __forceinline__ void block_of(int wg, int M, int num_wg, const int32_
     if (is_long(mid)) lo = mid + 1;
     else hi = mid;
   }
-  const int nlong = lo;
-  const int bhs = num_wg / M;
+  const int nlong = (lo + G - 1) / G;  // groups holding a long block
+  const int bhs = num_wg / NG;
   const int hx = (bhs + kNumXcd - 1) / kNumXcd;
-  const int gidx = wg / (hx * M);
-  const int r = wg % (hx * M);
+  const int gidx = wg / (hx * NG);
+  const int r = wg % (hx * NG);
   const int nh = bhs - gidx * hx < hx ? bhs - gidx * hx : hx;
-  if (r < nlong * nh) {  // long blocks, rank by rank over the range's heads
+  if (r < nlong * nh) {  // long groups, rank by rank over the range's heads
     bh = gidx * hx + r % nh;
-    blk = order[r / nh];
+    grp = r / nh;
   } else {               // the rest, head by head
     const int rr = r - nlong * nh;
-    bh = gidx * hx + rr / (M - nlong);
-    blk = order[nlong + rr % (M - nlong)];
+    bh = gidx * hx + rr / (NG - nlong);
+    grp = nlong + rr % (NG - nlong);
   }
 }
 
+// Block g of group grp, or -1 past the last block.
+__device__ __forceinline__ int group_block(int grp, int g, int G, int M, const int32_t* order) {
+  const int k = grp * G + g;
+  return k >= M ? -1 : order != nullptr ? order[k] : k;
+}
+
+// The union of a workgroup's G lists (G > 1), ascending, built in LDS:
+// bitmap[0, MW) marks the union and bitmap[(1 + g) MW, ...) block g's own
+// list (with the causal bound applied: dir < 0 keeps j <= blk, dir > 0 keeps
+// j >= blk).  The block's `loader` wave marks its entries; wave 0 then writes
+// the union into `list`.  Returns the union's size.
+template <int G>
+__device__ int build_union(const int32_t* idx, int s, int e, bool loader, int g, int blk,
+                           int dir, int M, int32_t* list, uint32_t* bitmap, int32_t* size,
+                           int lane, int wave) {
+  const int MW = (M + 31) / 32;
+  for (int i = threadIdx.x; i < (G + 1) * MW; i += blockDim.x) bitmap[i] = 0;
+  __syncthreads();
+  if (loader) {
+    for (int t = s + lane; t < e; t += kWave) {
+      const int j = idx[t];
+      if (j >= 0 && j < M && (dir == 0 || (dir < 0 ? j <= blk : j >= blk))) {
+        atomicOr(&bitmap[j >> 5], 1u << (j & 31));
+        atomicOr(&bitmap[(1 + g) * MW + (j >> 5)], 1u << (j & 31));
+      }
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    int base = 0;
+    for (int w0 = 0; w0 < MW; w0 += kWave) {
+      const int w = w0 + lane;
+      uint32_t bits = w < MW ? bitmap[w] : 0u;
+      const int cnt = __builtin_popcount(bits);
+      int incl = cnt;
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int t = __shfl_up(incl, off);
+        if (lane >= off) incl += t;
+      }
+      int pos = base + incl - cnt;
+      while (bits != 0u) {
+        list[pos++] = w * 32 + __builtin_ctz(bits);
+        bits &= bits - 1;
+      }
+      base += __shfl(incl, kWave - 1);
+    }
+    if (lane == 0) *size = base;
+  }
+  __syncthreads();
+  return uniform(*size);
+}
+
+// Dynamic LDS of a G-block workgroup: the union list (M ints) and G + 1
+// bitmaps; none for one block.
+inline size_t union_lds_bytes(int G, int M) {
+  return G == 1 ? 0 : 4 * ((size_t)M + (size_t)(G + 1) * ((M + 31) / 32));
+}
+
 // Ring depth and copy split of a backward kernel whose stage holds two tiles
-// of BS rows (plus `extra` bytes).
-template <typename T, int BS, int D, int kExtraBytes>
+// of BS rows (plus `extra` bytes), for G blocks per workgroup.  One wave per
+// workgroup (block 32, G = 1) keeps a two-stage ring: half the LDS of three
+// stages lets more of those one-wave workgroups share a CU (5% faster at the
+// worked example's B = 32).  Otherwise three stages within 48 KB, else two
+// (four stages measured 3% slower at B = 32: the steps are not waiting on
+// their copies).
+template <typename T, int BS, int D, int kExtraBytes, int G = 1>
 struct BwdCfg {
   using L = TileLayout<T, BS, D>;
-  static constexpr int W = BS / kQRows;
+  static constexpr int QW = BS / kQRows;  // waves per block
+  static constexpr int W = G * QW;
   static constexpr int kStage = L::kEntryBytes + kExtraBytes;
-  static constexpr int NB = 3 * kStage <= 48 * 1024 ? 3 : 2;
+  static constexpr int NB = W == 1 ? 2 : 3 * kStage <= 48 * 1024 ? 3 : 2;
+  static_assert(NB <= 4, "the kernels handle rings of up to four stages");
   static_assert(L::kCopies % W == 0, "stage copies must split evenly over the waves");
   static constexpr int kParts = L::kCopies / W;
+  // the epilogue stages each wave's 32 rows (D features) through the ring
+  static constexpr int kRowsStage = kQRows * D * (int)sizeof(T);
+  static constexpr int kPerBuf = kStage / kRowsStage;
+  static_assert(kPerBuf >= 1 && W <= NB * kPerBuf, "output stages fit the ring");
 };
 
 // Per-lane dot product of two row operands (the lane's features of one row);
@@ -145,6 +217,25 @@ __device__ __forceinline__ float operand_dot(const typename Ops<T>::template QOp
   return s;
 }
 
+// The two score tiles of a step, a from the stage's first tile with operand
+// qa and b from its second tile with qb: interleaved MFMA chains for bf16
+// with block 64 or d = 128 (backward of the long workload 11% faster; at
+// block 32 and d = 64 the plain order measured 1% faster).
+template <typename T, int BS, int D>
+__device__ __forceinline__ void score_pair(const typename Ops<T>::template QOperand<D>& qa,
+                                           const typename Ops<T>::template QOperand<D>& qb,
+                                           const typename Ops<T>::template Offsets<BS, D>& off,
+                                           LDS_PTR(unsigned char) tile, int st, f32x16_t& a,
+                                           f32x16_t& b) {
+  using L = TileLayout<T, BS, D>;
+  if constexpr (std::is_same<T, __bf16>::value && (BS == 64 || D == 128)) {
+    Ops<T>::template scores_pair<BS, D>(qa, qb, off, tile, 0, L::kTileBytes, st, a, b);
+  } else {
+    a = Ops<T>::template scores<BS, D>(qa, off, tile, 0, st);
+    b = Ops<T>::template scores<BS, D>(qb, off, tile, L::kTileBytes, st);
+  }
+}
+
 // A workgroup's list (CSR row or CSC column): each wave reads it from the
 // index array itself, 64 entries at a time, one per lane.  The first 64 are
 // loaded before the operand loads: the vector-memory counter drains in
@@ -160,9 +251,11 @@ __device__ __forceinline__ ListHead list_head(const int32_t* idx, int start, int
 }
 
 // ---------------------------------------------------------------- dQ (and D)
-template <typename T, int BS, int D, bool CAUSAL>
-__global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 0>::W)) void bsa_bwd_dq(BwdParams p) {
-  using C = BwdCfg<T, BS, D, 0>;
+// G query blocks per workgroup (G > 1): they share each K/V stage of the
+// union of their rows; a wave computes the entries its own row selects.
+template <typename T, int BS, int D, int G, bool CAUSAL>
+__global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 0, G>::W)) void bsa_bwd_dq(BwdParams p) {
+  using C = BwdCfg<T, BS, D, 0, G>;
   using L = typename C::L;
   using O = Ops<T>;
   constexpr int NB = C::NB;
@@ -170,32 +263,48 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 0>::W)) void bsa_bwd_dq(B
 
   __shared__ __attribute__((aligned(16))) unsigned char buf0[C::kStage];
   __shared__ __attribute__((aligned(16))) unsigned char buf1[C::kStage];
-  __shared__ __attribute__((aligned(16))) unsigned char buf2[NB == 3 ? C::kStage : 16];
+  __shared__ __attribute__((aligned(16))) unsigned char buf2[NB >= 3 ? C::kStage : 16];
+  __shared__ __attribute__((aligned(16))) unsigned char buf3[NB >= 4 ? C::kStage : 16];
+  extern __shared__ __attribute__((aligned(16))) int32_t dyn[];  // (G > 1) union list | bitmaps
+  __shared__ int32_t union_size;
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = uniform(threadIdx.x / kWave);  // 32-row query group
+  const int wave = uniform(threadIdx.x / kWave);
+  const int qg = wave % C::QW;  // 32-row query group of the block
+  const int g = wave / C::QW;   // block of the workgroup
   const int M = p.M;
-  int bh, qb;
-  block_of(xcd_remap(blockIdx.x, p.num_wg), M, p.num_wg, p.row_order, p.row_ptr, bh, qb);
+  int bh, grp;
+  group_of(xcd_remap(blockIdx.x, p.num_wg), M, G, p.num_wg, p.row_order, p.row_ptr, bh, grp);
+  const int blk = group_block(grp, g, G, M, p.row_order);
+  const bool has = blk >= 0;
+  const int qb = has ? blk : 0;
   const int32_t* const row_ptr = p.row_ptr + (size_t)(bh % p.heads) * p.ptr_stride;
   const size_t head = (size_t)bh * p.N * D;
   const T* K = static_cast<const T*>(p.k) + head;
   const T* V = static_cast<const T*>(p.v) + head;
-  const int q0 = qb * BS + wave * kQRows;
+  const int q0 = qb * BS + qg * kQRows;
   const int row = q0 + (lane & 31);
 
-  const ListHead lh = list_head(p.col_idx, row_ptr[qb], row_ptr[qb + 1], lane);
+  ListHead lh{0, 0, -1};
+  int U;
+  const uint32_t* my_bits = reinterpret_cast<const uint32_t*>(dyn + M) + (1 + g) * ((M + 31) / 32);
+  if constexpr (G == 1) {
+    lh = list_head(p.col_idx, row_ptr[qb], row_ptr[qb + 1], lane);
+    U = lh.n;
+  } else {
+    const int rs = has ? row_ptr[qb] : 0, re = has ? row_ptr[qb + 1] : 0;
+    U = build_union<G>(p.col_idx, rs, re, has && qg == 0, g, qb, CAUSAL ? -1 : 0, M, dyn,
+                       reinterpret_cast<uint32_t*>(dyn + M), &union_size, lane, wave);
+  }
   typename O::template QOperand<D> qop, dop, oop;
   O::template load_q<D>(qop, static_cast<const T*>(p.q) + head + (size_t)q0 * D, lane);
   O::template load_q<D>(dop, static_cast<const T*>(p.dout) + head + (size_t)q0 * D, lane);
   O::template load_q<D>(oop, static_cast<const T*>(p.o) + head + (size_t)q0 * D, lane);
   const float lse2 = p.lse[(size_t)bh * p.N + row] * kLog2e;
 
-  const int U = lh.n;
-
   // D for this lane's row; the lane half h = 0 stores it for bsa_bwd_dkv.
   const float dsum = halves_sum(operand_dot<T, D>(dop, oop));
-  if ((lane >> 5) == 0) p.delta[(size_t)bh * p.N + row] = dsum;
+  if (has && (lane >> 5) == 0) p.delta[(size_t)bh * p.N + row] = dsum;
 
   int chunk_base = -kWave, chunk = -1;
   uint64_t chunk_sel = 0;
@@ -207,8 +316,16 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 0>::W)) void bsa_bwd_dq(B
     if ((t & ~(kWave - 1)) != chunk_base) {
       chunk_base = t & ~(kWave - 1);
       const int idx = chunk_base + lane;
-      chunk = chunk_base == 0 ? lh.first : idx < U ? p.col_idx[lh.start + idx] : -1;
-      chunk_sel = __builtin_amdgcn_ballot_w64(chunk >= 0 && chunk < M && (!CAUSAL || chunk <= qb));
+      bool sel;
+      if constexpr (G == 1) {
+        chunk = chunk_base == 0 ? lh.first : idx < U ? p.col_idx[lh.start + idx] : -1;
+        sel = chunk >= 0 && chunk < M && (!CAUSAL || chunk <= qb);
+      } else {  // the union holds only selected, in-range blocks
+        chunk = idx < U ? dyn[idx] : -1;
+        const int cj = chunk < 0 ? 0 : chunk;
+        sel = has && chunk >= 0 && ((my_bits[cj >> 5] >> (cj & 31)) & 1u) != 0;
+      }
+      chunk_sel = __builtin_amdgcn_ballot_w64(sel);
     }
     use = ((chunk_sel >> (t - chunk_base)) & 1ull) != 0;
     return __builtin_amdgcn_readlane(chunk, t - chunk_base);
@@ -245,9 +362,10 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 0>::W)) void bsa_bwd_dq(B
     LDS_PTR(unsigned char) tile = (LDS_PTR(unsigned char))buf;
 #pragma unroll
     for (int st = 0; st < KSTEPS; ++st) {
-      if (diag && st > wave) continue;
-      f32x16_t s = O::template scores<BS, D>(qop, off, tile, 0, st);  // S^T, lane = query
-      if (diag && st == wave) {
+      if (diag && st > qg) continue;
+      f32x16_t s, dp;  // S^T = K Q^T and dP^T = V dO^T, lane = query
+      score_pair<T, BS, D>(qop, dop, off, tile, st, s, dp);
+      if (diag && st == qg) {
         const int h = lane >> 5;
 #pragma unroll
         for (int r = 0; r < 16; ++r)
@@ -255,7 +373,6 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 0>::W)) void bsa_bwd_dq(B
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = fast_exp2(fmaf(s[r], c2, -lse2));  // P^T
-      const f32x16_t dp = O::template scores<BS, D>(dop, off, tile, L::kTileBytes, st);
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = s[r] * (dp[r] - dsum);  // dS^T
       (void)O::template accumulate<BS, D>(dq, s, off, tile, -L::kTileBytes, st);  // K^T dS^T
@@ -267,18 +384,24 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 0>::W)) void bsa_bwd_dq(B
 #pragma unroll
   for (int e = 0; e < NB; ++e) jq[e] = entry_at(e, mq[e]);
   wait_vm_lgkm0<0>();  // Q, dO, O, LSE loads and the first entries are complete
-  // The first copies, for the entries there are (none for an empty list).
-  if (U > 0) issue(jq[0], buf0);
-  if (NB == 3 && U > 1) issue(jq[1], buf1);
   auto buffer = [&](auto b_c) -> unsigned char* {
     constexpr int b = decltype(b_c)::value;
     if constexpr (b == 0) return buf0;
     else if constexpr (b == 1) return buf1;
-    else return buf2;
+    else if constexpr (b == 2) return buf2;
+    else return buf3;
   };
+  // The first NB - 1 copies, for the entries there are (none for an empty list).
+  if (U > 0) issue(jq[0], buf0);
+  if (NB >= 3 && U > 1) issue(jq[1], buf1);
+  if (NB >= 4 && U > 2) issue(jq[2], buf2);
   auto step = [&](int i, auto b_c) {
     constexpr int b = decltype(b_c)::value;
-    if (NB == 3 && i + 1 < U) wait_vm_lgkm0<C::kParts>();
+    // this wave's copies of entry i have landed; those of the min(NB - 2,
+    // U - 1 - i) later entries already issued may stay in flight
+    const int ahead = U - 1 - i;
+    if (NB >= 4 && ahead >= 2) wait_vm_lgkm0<(NB >= 4 ? 2 : 0) * C::kParts>();
+    else if (NB >= 3 && ahead >= 1) wait_vm_lgkm0<(NB >= 3 ? 1 : 0) * C::kParts>();
     else wait_vm_lgkm0<0>();
     raw_barrier();
     const bool use = mq[0];
@@ -295,51 +418,79 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 0>::W)) void bsa_bwd_dq(B
   for (int i = 0; i < U; i += NB) {
     step(i, std::integral_constant<int, 0>{});
     if (i + 1 < U) step(i + 1, std::integral_constant<int, 1>{});
-    if constexpr (NB == 3)
+    if constexpr (NB >= 3)
       if (i + 2 < U) step(i + 2, std::integral_constant<int, 2>{});
+    if constexpr (NB >= 4)
+      if (i + 3 < U) step(i + 3, std::integral_constant<int, 3>{});
   }
 
   // dQ leaves through this wave's part of the idle ring (whole 16-byte stores).
   wait_vm_lgkm0<0>();  // no copy is still landing (the compiler does not track them)
   __syncthreads();     // every wave is done with the ring
+  if (!has) return;
+  unsigned char* const stage_buf = wave < C::kPerBuf       ? buf0
+                                  : wave < 2 * C::kPerBuf ? buf1
+                                  : wave < 3 * C::kPerBuf ? buf2
+                                                          : buf3;
   store_rows_lds<T, D>(static_cast<T*>(p.dq) + head + (size_t)q0 * D, dq, p.scale, lane,
-                       (LDS_PTR(unsigned char))buf0 + wave * (kQRows * D * (int)sizeof(T)));
+                       (LDS_PTR(unsigned char))stage_buf + (wave % C::kPerBuf) * C::kRowsStage);
 }
 
 // ---------------------------------------------------------------- dK, dV
-template <typename T, int BS, int D, bool CAUSAL>
-__global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 8 * BS>::W)) void bsa_bwd_dkv(BwdParams p) {
-  using C = BwdCfg<T, BS, D, 8 * BS>;  // Q tile, dO tile, then LSE[BS] and D[BS] floats
+// G key blocks per workgroup (G > 1): they share each Q/dO stage of the
+// union of their columns; a wave computes the entries its own column holds.
+template <typename T, int BS, int D, int G, bool CAUSAL>
+__global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 8 * BS, G>::W)) void bsa_bwd_dkv(
+    BwdParams p) {
+  using C = BwdCfg<T, BS, D, 8 * BS, G>;  // Q tile, dO tile, then LSE[BS] and D[BS] floats
   using L = typename C::L;
   using O = Ops<T>;
   constexpr int NB = C::NB;
   constexpr int QSTEPS = BS / kQRows;
   constexpr int kVecOff = L::kEntryBytes;          // LSE floats, then D floats
-  constexpr int kExtra = C::W == 1 ? 2 : 1;        // dword copies per wave per stage
 
   __shared__ __attribute__((aligned(16))) unsigned char buf0[C::kStage];
   __shared__ __attribute__((aligned(16))) unsigned char buf1[C::kStage];
-  __shared__ __attribute__((aligned(16))) unsigned char buf2[NB == 3 ? C::kStage : 16];
+  __shared__ __attribute__((aligned(16))) unsigned char buf2[NB >= 3 ? C::kStage : 16];
+  __shared__ __attribute__((aligned(16))) unsigned char buf3[NB >= 4 ? C::kStage : 16];
+  extern __shared__ __attribute__((aligned(16))) int32_t dyn[];  // (G > 1) union list | bitmaps
+  __shared__ int32_t union_size;
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = uniform(threadIdx.x / kWave);  // 32-key group
+  const int wave = uniform(threadIdx.x / kWave);
+  const int kg = wave % C::QW;  // 32-key group of the block
+  const int g = wave / C::QW;   // block of the workgroup
+  // dword copies per stage by this wave: LSE by wave 0, D by wave 1 (or
+  // both by the one wave of a one-wave workgroup)
+  const int n_vec = C::W == 1 ? 2 : wave < 2 ? 1 : 0;
   const int M = p.M;
-  int bh, kb;
-  block_of(xcd_remap(blockIdx.x, p.num_wg), M, p.num_wg, p.col_order, p.col_ptr, bh, kb);
+  int bh, grp;
+  group_of(xcd_remap(blockIdx.x, p.num_wg), M, G, p.num_wg, p.col_order, p.col_ptr, bh, grp);
+  const int blk = group_block(grp, g, G, M, p.col_order);
+  const bool has = blk >= 0;
+  const int kb = has ? blk : 0;
   const int32_t* const col_ptr = p.col_ptr + (size_t)(bh % p.heads) * p.ptr_stride;
   const size_t head = (size_t)bh * p.N * D;
   const T* Qh = static_cast<const T*>(p.q) + head;
   const T* dOh = static_cast<const T*>(p.dout) + head;
   const float* lse_h = p.lse + (size_t)bh * p.N;
   const float* del_h = p.delta + (size_t)bh * p.N;
-  const int k0 = kb * BS + wave * kQRows;
+  const int k0 = kb * BS + kg * kQRows;
 
-  const ListHead lh = list_head(p.row_idx, col_ptr[kb], col_ptr[kb + 1], lane);
+  ListHead lh{0, 0, -1};
+  int U;
+  const uint32_t* my_bits = reinterpret_cast<const uint32_t*>(dyn + M) + (1 + g) * ((M + 31) / 32);
+  if constexpr (G == 1) {
+    lh = list_head(p.row_idx, col_ptr[kb], col_ptr[kb + 1], lane);
+    U = lh.n;
+  } else {
+    const int cs = has ? col_ptr[kb] : 0, ce = has ? col_ptr[kb + 1] : 0;
+    U = build_union<G>(p.row_idx, cs, ce, has && kg == 0, g, kb, CAUSAL ? 1 : 0, M, dyn,
+                       reinterpret_cast<uint32_t*>(dyn + M), &union_size, lane, wave);
+  }
   typename O::template QOperand<D> kop, vop;
   O::template load_q<D>(kop, static_cast<const T*>(p.k) + head + (size_t)k0 * D, lane);
   O::template load_q<D>(vop, static_cast<const T*>(p.v) + head + (size_t)k0 * D, lane);
-
-  const int U = lh.n;
 
   int chunk_base = -kWave, chunk = -1;
   uint64_t chunk_sel = 0;
@@ -351,8 +502,16 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 8 * BS>::W)) void bsa_bwd
     if ((t & ~(kWave - 1)) != chunk_base) {
       chunk_base = t & ~(kWave - 1);
       const int idx = chunk_base + lane;
-      chunk = chunk_base == 0 ? lh.first : idx < U ? p.row_idx[lh.start + idx] : -1;
-      chunk_sel = __builtin_amdgcn_ballot_w64(chunk >= 0 && chunk < M && (!CAUSAL || chunk >= kb));
+      bool sel;
+      if constexpr (G == 1) {
+        chunk = chunk_base == 0 ? lh.first : idx < U ? p.row_idx[lh.start + idx] : -1;
+        sel = chunk >= 0 && chunk < M && (!CAUSAL || chunk >= kb);
+      } else {  // the union holds only selected, in-range blocks
+        chunk = idx < U ? dyn[idx] : -1;
+        const int cj = chunk < 0 ? 0 : chunk;
+        sel = has && chunk >= 0 && ((my_bits[cj >> 5] >> (cj & 31)) & 1u) != 0;
+      }
+      chunk_sel = __builtin_amdgcn_ballot_w64(sel);
     }
     use = ((chunk_sel >> (t - chunk_base)) & 1ull) != 0;
     return __builtin_amdgcn_readlane(chunk, t - chunk_base);
@@ -376,8 +535,8 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 8 * BS>::W)) void bsa_bwd
       const T* base = (part < kPartsPerTile ? Qh : dOh) + (size_t)q0 * D;
       lds_dma16(base, (uint32_t)dma_off[c], dst + part * kWave * 16);
     }
-    // LSE and D of the block's rows (BS floats each): one wave copies each
-    // vector, or wave 0 both.
+    // LSE and D of the block's rows (BS floats each): waves 0 and 1 copy
+    // one vector each, or the one wave both.
     if (lane < BS) {
       if (C::W == 1 || wave == 0) lds_dma4(lse_h + q0, (uint32_t)lane * 4, dst + kVecOff);
       if (C::W == 1 || wave == 1) lds_dma4(del_h + q0, (uint32_t)lane * 4, dst + kVecOff + 4 * BS);
@@ -400,9 +559,10 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 8 * BS>::W)) void bsa_bwd
     LDS_PTR(const f32x4_t) vec = (LDS_PTR(const f32x4_t))(tile + kVecOff);
 #pragma unroll
     for (int sq = 0; sq < QSTEPS; ++sq) {
-      if (diag && sq < wave) continue;  // those queries precede every key of the wave
-      f32x16_t s = O::template scores<BS, D>(kop, off, tile, 0, sq);  // S, lane = key
-      if (diag && sq == wave) {
+      if (diag && sq < kg) continue;  // those queries precede every key of the wave
+      f32x16_t s, dp;  // S = Q K^T and dP = dO V^T, lane = key
+      score_pair<T, BS, D>(kop, vop, off, tile, sq, s, dp);
+      if (diag && sq == kg) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           if ((lane & 31) > 8 * (r / 4) + 4 * h + (r % 4)) s[r] = -INFINITY;
@@ -417,7 +577,6 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 8 * BS>::W)) void bsa_bwd
           s[4 * g + e] = fast_exp2(fmaf(s[4 * g + e], c2, -l4[e] * kLog2e));
       }
       (void)O::template accumulate<BS, D>(dv, s, off, tile, 0, sq);  // dO^T P
-      const f32x16_t dp = O::template scores<BS, D>(vop, off, tile, L::kTileBytes, sq);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const f32x4_t d4 = vec[(BS + 32 * sq + 8 * g + 4 * h) / 4];
@@ -433,19 +592,31 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 8 * BS>::W)) void bsa_bwd
 #pragma unroll
   for (int e = 0; e < NB; ++e) jq[e] = entry_at(e, mq[e]);
   wait_vm_lgkm0<0>();  // K, V loads and the list are complete
-  // The first copies, for the entries there are (none for an empty list).
-  if (U > 0) issue(jq[0], buf0);
-  if (NB == 3 && U > 1) issue(jq[1], buf1);
   auto buffer = [&](auto b_c) -> unsigned char* {
     constexpr int b = decltype(b_c)::value;
     if constexpr (b == 0) return buf0;
     else if constexpr (b == 1) return buf1;
-    else return buf2;
+    else if constexpr (b == 2) return buf2;
+    else return buf3;
   };
-  constexpr int kPerStage = C::kParts + kExtra;
+  // The first NB - 1 copies, for the entries there are (none for an empty list).
+  if (U > 0) issue(jq[0], buf0);
+  if (NB >= 3 && U > 1) issue(jq[1], buf1);
+  if (NB >= 4 && U > 2) issue(jq[2], buf2);
+  // Waits for this wave's copies of the current entry, leaving those of `k`
+  // later entries in flight (a stage is kParts tile copies plus n_vec).
+  auto wait_leaving = [&](auto k_c) {
+    constexpr int k = decltype(k_c)::value;
+    if (n_vec == 2) wait_vm_lgkm0<k * (C::kParts + 2)>();
+    else if (n_vec == 1) wait_vm_lgkm0<k * (C::kParts + 1)>();
+    else wait_vm_lgkm0<k * C::kParts>();
+  };
   auto step = [&](int i, auto b_c) {
     constexpr int b = decltype(b_c)::value;
-    if (NB == 3 && i + 1 < U) wait_vm_lgkm0<kPerStage>();
+    // the min(NB - 2, U - 1 - i) later entries already issued may stay in flight
+    const int ahead = U - 1 - i;
+    if (NB >= 4 && ahead >= 2) wait_leaving(std::integral_constant<int, NB >= 4 ? 2 : 0>{});
+    else if (NB >= 3 && ahead >= 1) wait_leaving(std::integral_constant<int, NB >= 3 ? 1 : 0>{});
     else wait_vm_lgkm0<0>();
     raw_barrier();
     const bool use = mq[0];
@@ -462,55 +633,113 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 8 * BS>::W)) void bsa_bwd
   for (int i = 0; i < U; i += NB) {
     step(i, std::integral_constant<int, 0>{});
     if (i + 1 < U) step(i + 1, std::integral_constant<int, 1>{});
-    if constexpr (NB == 3)
+    if constexpr (NB >= 3)
       if (i + 2 < U) step(i + 2, std::integral_constant<int, 2>{});
+    if constexpr (NB >= 4)
+      if (i + 3 < U) step(i + 3, std::integral_constant<int, 3>{});
   }
 
   // dK then dV leave through this wave's part of the idle ring.
   wait_vm_lgkm0<0>();  // no copy is still landing (the compiler does not track them)
   __syncthreads();     // every wave is done with the ring
+  if (!has) return;
+  unsigned char* const stage_buf = wave < C::kPerBuf       ? buf0
+                                  : wave < 2 * C::kPerBuf ? buf1
+                                  : wave < 3 * C::kPerBuf ? buf2
+                                                          : buf3;
   LDS_PTR(unsigned char) region =
-      (LDS_PTR(unsigned char))buf0 + wave * (kQRows * D * (int)sizeof(T));
+      (LDS_PTR(unsigned char))stage_buf + (wave % C::kPerBuf) * C::kRowsStage;
   store_rows_lds<T, D>(static_cast<T*>(p.dk) + head + (size_t)k0 * D, dk, p.scale, lane, region);
   store_rows_lds<T, D>(static_cast<T*>(p.dv) + head + (size_t)k0 * D, dv, 1.0f, lane, region);
 }
 
 // ---------------------------------------------------------------- host
 
-template <typename T, int BS, int D, bool CAUSAL>
+constexpr size_t kMaxLds = 160 * 1024;
+
+template <typename T, int BS, int D, int G, bool CAUSAL>
 bsa_status launch_bwd(const BwdParams& p, hipStream_t stream) {
   const dim3 grid(p.num_wg);
-  const dim3 block(kWave * (BS / kQRows));
+  const dim3 block(kWave * BwdCfg<T, BS, D, 0, G>::W);
+  const size_t dyn = union_lds_bytes(G, p.M);
   // Shapes with more than 64 KB of LDS need the per-kernel limit raised, once
   // per device.
   static std::atomic<uint64_t> raised{0};
   uint64_t bit;
+  const void* kernels[2] = {reinterpret_cast<const void*>(&bsa_bwd_dq<T, BS, D, G, CAUSAL>),
+                            reinterpret_cast<const void*>(&bsa_bwd_dkv<T, BS, D, G, CAUSAL>)};
+  for (const void* f : kernels) {
+    hipFuncAttributes attr;
+    if (hipFuncGetAttributes(&attr, f) != hipSuccess) return BSA_ERR_HIP;
+    if (attr.sharedSizeBytes + dyn > kMaxLds) return BSA_ERR_INVALID_ARGUMENT;
+  }
   if (due_on_device(raised, &bit)) {
-    const void* kernels[2] = {reinterpret_cast<const void*>(&bsa_bwd_dq<T, BS, D, CAUSAL>),
-                              reinterpret_cast<const void*>(&bsa_bwd_dkv<T, BS, D, CAUSAL>)};
     for (const void* f : kernels) {
       hipFuncAttributes attr;
       if (hipFuncGetAttributes(&attr, f) != hipSuccess) return BSA_ERR_HIP;
-      if (attr.sharedSizeBytes > 64 * 1024 &&
-          hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              static_cast<int>(160 * 1024 - attr.sharedSizeBytes)) != hipSuccess)
+      if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              static_cast<int>(kMaxLds - attr.sharedSizeBytes)) != hipSuccess)
         return BSA_ERR_HIP;
     }
     mark_done(raised, bit);
   }
-  hipLaunchKernelGGL((bsa_bwd_dq<T, BS, D, CAUSAL>), grid, block, 0, stream, p);
+  hipLaunchKernelGGL((bsa_bwd_dq<T, BS, D, G, CAUSAL>), grid, block, dyn, stream, p);
   if (hipGetLastError() != hipSuccess) return BSA_ERR_HIP;
-  hipLaunchKernelGGL((bsa_bwd_dkv<T, BS, D, CAUSAL>), grid, block, 0, stream, p);
+  hipLaunchKernelGGL((bsa_bwd_dkv<T, BS, D, G, CAUSAL>), grid, block, dyn, stream, p);
   return hipGetLastError() == hipSuccess ? BSA_OK : BSA_ERR_HIP;
 }
 
-template <typename T>
-bsa_status dispatch_bwd(const BwdParams& p, int bs, int d, bool causal, hipStream_t stream) {
-  if (bs == 32 && d == 64) return causal ? launch_bwd<T, 32, 64, true>(p, stream) : launch_bwd<T, 32, 64, false>(p, stream);
-  if (bs == 32 && d == 128) return causal ? launch_bwd<T, 32, 128, true>(p, stream) : launch_bwd<T, 32, 128, false>(p, stream);
-  if (bs == 64 && d == 64) return causal ? launch_bwd<T, 64, 64, true>(p, stream) : launch_bwd<T, 64, 64, false>(p, stream);
-  if (bs == 64 && d == 128) return causal ? launch_bwd<T, 64, 128, true>(p, stream) : launch_bwd<T, 64, 128, false>(p, stream);
+template <typename T, int BS, int D>
+bsa_status launch_group(const BwdParams& p, int group, bool causal, hipStream_t stream) {
+  if (group == 1)
+    return causal ? launch_bwd<T, BS, D, 1, true>(p, stream) : launch_bwd<T, BS, D, 1, false>(p, stream);
+  if constexpr (BS == 32) {
+    if (group == 4)
+      return causal ? launch_bwd<T, BS, D, 4, true>(p, stream)
+                    : launch_bwd<T, BS, D, 4, false>(p, stream);
+  }
   return BSA_ERR_INVALID_ARGUMENT;
+}
+
+template <typename T>
+bsa_status dispatch_bwd(const BwdParams& p, int bs, int d, int group, bool causal,
+                        hipStream_t stream) {
+  if (bs == 32 && d == 64) return launch_group<T, 32, 64>(p, group, causal, stream);
+  if (bs == 32 && d == 128) return launch_group<T, 32, 128>(p, group, causal, stream);
+  if (bs == 64 && d == 64) return launch_group<T, 64, 64>(p, group, causal, stream);
+  if (bs == 64 && d == 128) return launch_group<T, 64, 128>(p, group, causal, stream);
+  return BSA_ERR_INVALID_ARGUMENT;
+}
+
+// Compute units of the current device (cached per device; 256 if the query
+// fails).
+int64_t device_cus() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = -1;
+  if (dev >= 0) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) !=
+          hipSuccess ||
+      n <= 0)
+    n = 256;
+  if (dev >= 0) cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Blocks per workgroup.  Block 32 on a large grid (eight one-wave blocks
+// per SIMD or more): four blocks share each stage of the union of their
+// lists, so a K/V (or Q/dO) tile is copied once for four waves instead of
+// once per wave.  Otherwise (block 64 holds two waves already; small grids
+// want every block's own short chain) one block.  The union list and its
+// bitmaps must fit beside the ring (M up to a few thousand blocks).
+int choose_group(int64_t bhm, int bs, int M) {
+  if (bs != 32 || bhm < 8 * 4 * device_cus()) return 1;
+  if (union_lds_bytes(4, M) > 32 * 1024) return 1;
+  return 4;
 }
 
 }  // namespace
@@ -548,7 +777,8 @@ bsa_status backward_impl(const void* q, const void* k, const void* v, const void
   const int64_t M = seq_len / block_size;
   const int64_t patterns = per_head ? heads : 1;
   if (nnz < patterns * M || nnz > patterns * M * M) return BSA_ERR_SHAPE;
-  const int64_t num_wg = (int64_t)batch * heads * M;
+  const int group = choose_group((int64_t)batch * heads * M, block_size, (int)M);
+  const int64_t num_wg = (int64_t)batch * heads * ((M + group - 1) / group);
   if ((int64_t)batch * heads * seq_len > INT32_MAX || num_wg > INT32_MAX) return BSA_ERR_SHAPE;
   const uintptr_t align = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
                           reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(o) |
@@ -585,8 +815,9 @@ bsa_status backward_impl(const void* q, const void* k, const void* v, const void
   const bool causal = (flags & BSA_FORWARD_CAUSAL) != 0;
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  if (dtype == BSA_DTYPE_F32) return dispatch_bwd<float>(p, block_size, head_dim, causal, st);
-  return dispatch_bwd<__bf16>(p, block_size, head_dim, causal, st);
+  if (dtype == BSA_DTYPE_F32)
+    return dispatch_bwd<float>(p, block_size, head_dim, group, causal, st);
+  return dispatch_bwd<__bf16>(p, block_size, head_dim, group, causal, st);
 }
 
 // The device address of `scratch` on each device (looked up once per device,

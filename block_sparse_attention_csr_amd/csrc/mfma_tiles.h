@@ -194,6 +194,33 @@ struct Ops<__bf16> {
       }
   }
 
+  // Two score tiles of step st from one stage: a = A-tile . qa^T (the tile at
+  // byte `ea`) and b = B-tile . qb^T (at `eb`), their MFMA chains
+  // interleaved so that each has the other's work between its dependent
+  // steps.
+  template <int BS, int D>
+  static __device__ __forceinline__ void scores_pair(const QOperand<D>& qa,
+                                                     const QOperand<D>& qb,
+                                                     const Offsets<BS, D>& off,
+                                                     LDS_PTR(unsigned char) lds, int ea, int eb,
+                                                     int st, f32x16_t& a, f32x16_t& b) {
+    using L = TileLayout<__bf16, BS, D>;
+    a = f32x16_t{};
+    b = f32x16_t{};
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      const int rows = st * kKeyStep * L::kRowBytes;
+      const u32x4_t ka = *(LDS_PTR(const u32x4_t))(lds + off.k[c] + ea + rows);
+      const u32x4_t kb = *(LDS_PTR(const u32x4_t))(lds + off.k[c] + eb + rows);
+      a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ka),
+                                                  __builtin_bit_cast(bf16x8_t, qa.r[c]), a, 0, 0,
+                                                  0);
+      b = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kb),
+                                                  __builtin_bit_cast(bf16x8_t, qb.r[c]), b, 0, 0,
+                                                  0);
+    }
+  }
+
   // V^T operand of step st, 16-key sub-step sc, feature tile dt: lane
   // (feature = 32 dt + lane % 32, half h) holds V[key][feature] for keys
   // kappa(h, j) = 32 st + 16 sc + 8 (j / 4) + 4 h + j % 4, j = 0..7: two

@@ -281,3 +281,33 @@ def test_backward_more_than_4096_blocks_sampled():
         ref = oracle.block_sparse_attention_backward(f(q), f(k), f(v), f(do), ones, bs)
         for name, got, want in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref[:3]):
             _check(f"{name} group {g}", got[:, :, seg], want, torch.bfloat16)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("kind,causal", [("loglinear", False), ("loglinear", True),
+                                         ("random", False), ("random", True)])
+def test_backward_grouped_blocks_sampled_heads(kind, causal, d):
+    """Block 32 on a large grid (B H M = 16384 query blocks): four blocks per
+    workgroup share each stage of the union of their lists.  With the
+    longest-first orders the log-linear pattern's anchor columns share one
+    group.  Sampled heads against the oracle on those heads (every head is
+    independent), and the same result as the ascending order."""
+    B, H, bs, M = 16, 8, 32, 128
+    N = M * bs
+    seed = zlib.crc32(repr(("grouped", kind, causal, d)).encode()) % 1000
+    q, k, v = make_qkv(B, H, N, d, torch.bfloat16, seed)
+    do = make_qkv(B, H, N, d, torch.bfloat16, seed + 1)[0]
+    if kind == "loglinear":
+        mask, user = oracle.block_mask_from_sets(oracle.loglinear_block_sets(N, bs)), None
+    else:
+        mask, user = _mask(kind, M, seed)
+    if causal:
+        mask = np.tril(mask)
+    dq, dk, dv = _run(q, k, v, do, bs, user, causal)
+    for b, h in ((0, 0), (7, 3), (B - 1, H - 1)):
+        f = lambda x: _f64(x[b:b + 1, h:h + 1])
+        ref = oracle.block_sparse_attention_backward(f(q), f(k), f(v), f(do), mask, bs,
+                                                     causal=causal)
+        for name, got, want in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref[:3]):
+            _check(f"{name} ({b}, {h}) {kind} causal={causal} d{d}", got[b:b + 1, h:h + 1],
+                   want, torch.bfloat16)
