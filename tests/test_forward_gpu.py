@@ -140,11 +140,18 @@ def test_worked_example_full():
     _convex_hull_check(_f64(o)[0, 3], vf[0, 3], mask, w.block_size, 1e-2)
 
 
+# Sampled (batch, head) pairs spread over the grid's XCD ranges, and query
+# blocks that include the dense rows, the anchors, both ends and a stride
+# through the rest (None: every block of the head).
+_LONG_QB = sorted({0, 1, 2, 3, 255, 256, 257, 509, 510, 511} | set(range(5, 512, 17)))
+_LG_QB = sorted({0, 1, 2, 5, 63, 64, 100, 126, 127} | set(range(3, 128, 11)))
+
+
 @pytest.mark.parametrize("name,heads,qblocks", [
-    ("local_global", [(0, 0), (1, 15), (1, 6)], [0, 1, 2, 5, 63, 64, 100, 126, 127]),
-    ("random_mask", [(0, 0), (77, 3), (127, 7)], None),
-    ("long", [(0, 0), (0, 31)], [0, 1, 2, 3, 100, 255, 256, 257, 300, 509, 510, 511]),
-    ("worked_example_b32", [(0, 0), (31, 7), (17, 2)], None),
+    ("local_global", [(0, 0), (0, 9), (1, 3), (1, 6), (1, 15)], _LG_QB),
+    ("random_mask", [(0, 0), (19, 5), (45, 2), (77, 3), (101, 6), (127, 7)], None),
+    ("long", [(0, 0), (0, 9), (0, 18), (0, 31)], _LONG_QB),
+    ("worked_example_b32", [(0, 0), (9, 4), (17, 2), (24, 1), (31, 7)], None),
 ])
 def test_full_size_workload_sampled(name, heads, qblocks):
     w = WORKLOADS[name]
