@@ -84,6 +84,10 @@ struct FwdParams {
   const int32_t* split;
   int32_t n_items;
   float* partial;
+  // One launch for both (G > 1): per (batch * head), the first n_tuples
+  // workgroups take the items, item t + g n_tuples as block g; the query
+  // groups follow.
+  int32_t n_tuples;
   // int8 K/V (bsa_forward_int8kv): k and v hold int8 codes, and these one
   // float32 scale per (batch * head, block); NULL for bf16 / float32 K/V.
   const float* k_scale;
@@ -199,16 +203,33 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS, KV8, RING>::W)) void 
   // their order, so neighbouring groups (which share K/V blocks) stay close
   // in time.
   int grp, bh, item = -1;
+  bool item_wg = false;  // a workgroup of items (all its waves)
   if (G == 1 && KS == 1 && p.split != nullptr) {  // split pass: one item of a heavy row
     item = wg % p.n_items;
     bh = wg / p.n_items;
     grp = p.split[3 * item];
+  } else if (G > 1 && KS == 1 && p.split != nullptr) {
+    // items and groups in one launch: a head's items first (each is as long
+    // as an ordinary row or longer), then its groups in the order below
+    const int per_head = p.n_tuples + ngroups;
+    const int r = wg % per_head;
+    bh = wg / per_head;
+    if (r < p.n_tuples) {
+      item_wg = true;
+      const int t = r + g * p.n_tuples;
+      item = t < p.n_items ? t : -1;
+      grp = 0;
+    } else {
+      const int rank = r - p.n_tuples;
+      grp = rank == 0 ? ngroups - 1 : rank - 1;
+    }
   } else {
     const int rank = wg % ngroups;
     grp = rank == 0 ? ngroups - 1 : rank - 1;
     bh = wg / ngroups;
   }
-  const int qb = grp * G + g;
+  // (block g of an item workgroup: its item's row, or none past the last item)
+  const int qb = !item_wg ? grp * G + g : item >= 0 ? p.split[3 * item] : M;
   // (a row the split pass takes is left out of this pass: no entry, no store)
   const bool has_rows = qb < M && (item >= 0 || p.heavy == nullptr || p.heavy[qb] == 0);
   constexpr bool causal = CAUSAL;
@@ -229,8 +250,8 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS, KV8, RING>::W)) void 
   const bool loads_row = G > 1 && has_rows && qg == 0 && ks == 0;
   int row_s = 0, row_e = 0, row_first = -1;
   if (loads_row) {
-    row_s = row_ptr[qb];
-    row_e = row_ptr[qb + 1];
+    row_s = item >= 0 ? p.split[3 * item + 1] : row_ptr[qb];
+    row_e = item >= 0 ? p.split[3 * item + 2] : row_ptr[qb + 1];
     if (row_s + lane < row_e) row_first = p.col_idx[row_s + lane];
   }
 
@@ -687,8 +708,9 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS, KV8, RING>::W)) void 
   wait_vm_lgkm0<0>();
   // ---- split pass: the item's partial state, unnormalised, in accumulator
   // order [register][lane], then m and l per lane (the merge reads the same)
-  if constexpr (G == 1 && KS == 1) {
-    if (item >= 0) {
+  if constexpr (KS == 1) {
+    if (G == 1 ? item >= 0 : item_wg) {
+      if (item < 0) return;  // (a block past the last item)
       float* dst = p.partial + ((size_t)bh * p.n_items + item) * QW * (partial_bytes<D>() / 4) +
                    (size_t)qg * (partial_bytes<D>() / 4);
 #pragma unroll
@@ -1165,7 +1187,20 @@ bsa_status forward_impl(const void* q, const void* k, const void* v, void* o, fl
   const size_t lds = lds_for(dtype, block_size, head_dim, p.group, p.key_split, (int)M, kv8);
   if (lds == 0 || lds > kMaxLds) return BSA_ERR_INVALID_ARGUMENT;
   const int64_t ngroups = (M + p.group - 1) / p.group;
-  const int64_t num_wg = (int64_t)batch * heads * ngroups;
+  // Several query blocks per workgroup and one key slice: the heavy rows'
+  // items run in the same launch as the groups, G per workgroup (the split
+  // pass's own launch is left out).
+  const bool fused = split && p.group > 1 && p.key_split == 1;
+  p.split = nullptr;
+  p.n_items = 0;
+  p.n_tuples = 0;
+  if (fused) {
+    p.split = plan->items;
+    p.n_items = plan->n_items;
+    p.partial = static_cast<float*>(plan->workspace);
+    p.n_tuples = (plan->n_items + p.group - 1) / p.group;
+  }
+  const int64_t num_wg = (int64_t)batch * heads * (ngroups + p.n_tuples);
   if (num_wg > INT32_MAX) return BSA_ERR_SHAPE;
   p.num_wg = static_cast<int32_t>(num_wg);
   const float s = scale > 0.f ? scale : 1.0f / std::sqrt(static_cast<float>(head_dim));
@@ -1176,20 +1211,24 @@ bsa_status forward_impl(const void* q, const void* k, const void* v, void* o, fl
   bsa_status r = dtype == BSA_DTYPE_F32 ? dispatch<float>(p, block_size, head_dim, st)
                                         : dispatch<__bf16>(p, block_size, head_dim, st);
   if (r != BSA_OK || !split) return r;
-  // The heavy rows: their items, one one-block workgroup each, then the merge.
-  // (Forking the items onto a second stream to overlap the main pass was
-  // measured: within a few percent either way, so the calls stay in order.)
+  // The heavy rows: their items (in their own launch of one-block workgroups
+  // unless they ran beside the groups), then the merge.  (Forking the item
+  // launch onto a second stream to overlap the main pass was measured:
+  // within a few percent either way.)
   FwdParams ps = p;
   ps.heavy = nullptr;
-  ps.group = 1;
-  ps.key_split = 1;
   ps.split = plan->items;
   ps.n_items = plan->n_items;
   ps.partial = static_cast<float*>(plan->workspace);
-  ps.num_wg = batch * heads * plan->n_items;
-  r = dtype == BSA_DTYPE_F32 ? dispatch<float>(ps, block_size, head_dim, st)
-                             : dispatch<__bf16>(ps, block_size, head_dim, st);
-  if (r != BSA_OK) return r;
+  if (!fused) {
+    ps.group = 1;
+    ps.key_split = 1;
+    ps.n_tuples = 0;
+    ps.num_wg = batch * heads * plan->n_items;
+    r = dtype == BSA_DTYPE_F32 ? dispatch<float>(ps, block_size, head_dim, st)
+                               : dispatch<__bf16>(ps, block_size, head_dim, st);
+    if (r != BSA_OK) return r;
+  }
   const int64_t grid = (int64_t)batch * heads * plan->n_rows * (head_dim / 32);
   return dtype == BSA_DTYPE_F32
              ? dispatch_merge<float>(ps, block_size, head_dim, plan->rows, plan->n_rows, grid, st)

@@ -147,3 +147,33 @@ def test_split_forward_in_a_graph_replays():
         eo, el = bsa.forward(q, k, v, rp, ci, bs, split=plan)  # eager, own outputs
         torch.cuda.synchronize()
         assert torch.equal(og, eo) and torch.equal(lg, el), f"replay {rep}"
+
+
+@pytest.mark.parametrize("chunk", [12, 5])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dt,bs,d", [("bf16", 32, 64), ("bf16", 64, 128), ("f32", 64, 64)])
+def test_split_items_beside_the_groups(dt, bs, d, causal, chunk):
+    """A grid of 8192 query blocks (B=8, H=32, M=32): several query blocks per
+    workgroup, so the heavy rows' items run in the same launch as the groups,
+    G items per workgroup (item t + g * tuples as block g), and the merge
+    follows.  Chunk 12 gives 3 items per dense row (6 in all: a workgroup
+    whose last block has no item at G = 4); chunk 5 splits ordinary rows
+    too.  Sampled heads against the oracle on every row."""
+    dtype = torch.bfloat16 if dt == "bf16" else torch.float32
+    B, H, M = 8, 32, 32
+    N = bs * M
+    mask = local_global_block_mask(M)
+    q, k, v = make_qkv(B, H, N, d, dtype, 83)
+    rp, ci = bsa.build_pattern(N, bs, mask=mask, causal=causal)
+    plan = bsa.plan_row_split(rp, chunk)
+    assert plan is not None
+    dev = torch.device("cuda")
+    o, lse = bsa.forward(q.to(dev), k.to(dev), v.to(dev), rp.to(dev), ci.to(dev), bs,
+                         causal=causal, split=plan.to(dev))
+    torch.cuda.synchronize()
+    for b, h in ((0, 0), (3, 17), (7, 31)):
+        f = lambda x: _f64(x[b:b + 1, h:h + 1])
+        o_ref, lse_ref = oracle.block_sparse_attention(f(q), f(k), f(v), mask, bs,
+                                                       causal=causal)
+        _compare(f(o), _f64(lse[b:b + 1, h:h + 1]), o_ref, lse_ref, dtype,
+                 f"{dt} bs{bs} d{d} causal={causal} chunk={chunk} ({b}, {h})")
