@@ -20,7 +20,13 @@
 //  * The union's K/V blocks stream through a ring of NB LDS buffers with
 //    direct-to-LDS copies (global_load_lds_dwordx4), NB - 1 entries ahead of
 //    the compute.  16-byte chunks are XOR-swizzled per row to spread LDS
-//    banks.
+//    banks.  bf16 at block 64 with one query block per workgroup holds one
+//    K slot and one V slot instead (each copy lands while the other half of
+//    the step runs), so that two waves per SIMD fit without pairing rows.
+//  * Rows far longer than the mean can be cut into items (a row-split plan):
+//    each item's workgroup writes a partial (O, m, l) that a merge combines.
+//    With several query blocks per workgroup the items run in the same
+//    launch as the query groups.
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (keys = MFMA rows, queries =
 //    MFMA columns): each lane holds the scores of ONE query, so row max and
 //    row sum are in-lane plus one v_permlane32_swap between the lane halves.
