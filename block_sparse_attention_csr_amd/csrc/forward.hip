@@ -494,9 +494,6 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS, KV8, RING>::W)) void 
       lsv = __builtin_amdgcn_logf(sve);
       isv = __builtin_amdgcn_rcpf(sve);
     }
-    // One running-max update per entry, over all of its 32-key steps: one
-    // ballot and one (rarely taken) rescale branch per entry, and the steps'
-    // exponentials and P.V products in one straight run of code.
     if (diag) {  // keys after each query of the diagonal step are masked
       const int qrow = lane & 31;
       const int h = lane >> 5;
@@ -507,31 +504,88 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS, KV8, RING>::W)) void 
           for (int r = 0; r < 16; ++r)
             if (8 * (r / 4) + 4 * h + (r % 4) > qrow) sc[st][r] = -INFINITY;
     }
-    float mx = sc[0][0];
+    // The row max (log2 domain) over the entry's steps, on both lane halves.
+    auto entry_max = [&]() {
+      float mx = sc[0][0];
 #pragma unroll
-    for (int st = 0; st < KSTEPS; ++st)
-      if (st == 0 || !diag || st <= qg)
+      for (int st = 0; st < KSTEPS; ++st)
+        if (st == 0 || !diag || st <= qg)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = __builtin_elementwise_maximum(mx, sc[st][r]);
-    mx = halves_max(mx) * c2k;
-    if (first) {  // O and l are still zero: no rescale
-      m2 = mx;
-      first = false;
-    } else if (__builtin_amdgcn_ballot_w64(mx > m2 + kLazyRescale) != 0) {
-      const float m_new = fmaxf(m2, mx);
-      const float alpha = fast_exp2(m2 - m_new);
-      m2 = m_new;
-      lsum *= alpha;
+          for (int r = 0; r < 16; ++r) mx = __builtin_elementwise_maximum(mx, sc[st][r]);
+      return halves_max(mx) * c2k;
+    };
+    if constexpr (!std::is_same<T, __bf16>::value || D != 64) {
+      // One running-max update per entry, over all of its 32-key steps: one
+      // ballot and one (rarely taken) rescale branch per entry, and the
+      // steps' exponentials and P.V products in one straight run of code.
+      const float mx = entry_max();
+      if (first) {  // O and l are still zero: no rescale
+        m2 = mx;
+        first = false;
+      } else if (__builtin_amdgcn_ballot_w64(mx > m2 + kLazyRescale) != 0) {
+        const float m_new = fmaxf(m2, mx);
+        const float alpha = fast_exp2(m2 - m_new);
+        m2 = m_new;
+        lsum *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
-    }
+        for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
+      }
 #pragma unroll
-    for (int st = 0; st < KSTEPS; ++st) {
-      if (diag && st > qg) continue;
+      for (int st = 0; st < KSTEPS; ++st) {
+        if (diag && st > qg) continue;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sc[st][r] = fast_exp2(fmaf(sc[st][r], c2k, KV8 ? lsv - m2 : -m2));
-      const float ps = O::template accumulate<BS, D>(o, sc[st], off, tile, vpos, st);
-      lsum = KV8 ? fmaf(ps, isv, lsum) : lsum + ps;
+        for (int r = 0; r < 16; ++r) sc[st][r] = fast_exp2(fmaf(sc[st][r], c2k, KV8 ? lsv - m2 : -m2));
+        const float ps = O::template accumulate<BS, D>(o, sc[st], off, tile, vpos, st);
+        lsum = KV8 ? fmaf(ps, isv, lsum) : lsum + ps;
+      }
+    } else {
+      // bf16 at d = 64, where the VALU rather than the matrix cores is the
+      // busier unit: no row max per entry.  The first entry sets the running
+      // max; after that a step's weights are taken with it as it stands, and
+      // only a step whose weights sum past 2^64 (scores risen by about 60 in
+      // the log2 domain, or a NaN) takes the max and rescales O and l before
+      // taking them again.  The check rides on the row sum already formed.
+      if (first) {  // O and l are still zero: no rescale
+        m2 = entry_max();
+        first = false;
+      }
+      const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+      for (int st = 0; st < KSTEPS; ++st) {
+        if (diag && st > qg) continue;
+        uint32_t w[8];  // the weights as packed bf16 pairs (separate scalars)
+        float ps = 0.f;
+        auto weights = [&]() {
+          const float bias = KV8 ? lsv - m2 : -m2;
+          ps = 0.f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float t0 = fast_exp2(fmaf(sc[st][2 * i], c2k, bias));
+            const float t1 = fast_exp2(fmaf(sc[st][2 * i + 1], c2k, bias));
+            w[i] = pack_bf16x2(t0, t1);
+            ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[i]), ones, ps,
+                                                 false);
+          }
+        };
+        weights();
+        const float pchk = KV8 ? ps * isv : ps;
+        if (__builtin_amdgcn_ballot_w64(!(pchk <= 0x1p64f)) != 0) {
+          float mx = sc[st][0];
+#pragma unroll
+          for (int r = 1; r < 16; ++r) mx = __builtin_elementwise_maximum(mx, sc[st][r]);
+          mx = halves_max(mx) * c2k;
+          const float m_new = fmaxf(m2, mx);
+          const float alpha =
+              m2 == -INFINITY || m_new == -INFINITY ? 1.f : fast_exp2(m2 - m_new);
+          m2 = m_new;
+          lsum *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
+          weights();
+        }
+        lsum = KV8 ? fmaf(ps, isv, lsum) : lsum + ps;
+        O::template accumulate_words<BS, D>(o, w, off, tile, vpos, st);
+      }
     }
   };
   auto compute = [&](unsigned char* buf, bool diag, float sk = 1.f, float sv = 1.f) {

@@ -273,6 +273,27 @@ struct Ops<__bf16> {
     return sum;
   }
 
+  // O^T += V^T P^T over 32-key step st, with P given as its eight packed
+  // bf16 words (w[4 sc + k] holds P[8 sc + 2k], P[8 sc + 2k + 1]).
+  template <int BS, int D>
+  static __device__ __forceinline__ void accumulate_words(f32x16_t (&o)[D / 32],
+                                                          const uint32_t (&w)[8],
+                                                          const Offsets<BS, D>& off,
+                                                          LDS_PTR(unsigned char) lds, int entry,
+                                                          int st) {
+#pragma unroll
+    for (int sc = 0; sc < 2; ++sc) {
+      const u32x4_t pb = {w[4 * sc], w[4 * sc + 1], w[4 * sc + 2], w[4 * sc + 3]};
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const u32x4_t va = v_operand<BS, D>(off, lds, entry, st, sc, dt);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, va),
+                                                        __builtin_bit_cast(bf16x8_t, pb), o[dt],
+                                                        0, 0, 0);
+      }
+    }
+  }
+
   // Lane holds O^T[d = 32 dt + 8 g + 4 h + e][query], e = 0..3.
   static __device__ __forceinline__ void store_o4(__bf16* dst, float a, float b, float c,
                                                   float d) {
