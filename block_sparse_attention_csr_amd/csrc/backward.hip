@@ -84,17 +84,22 @@ __device__ __forceinline__ void group_of(int wg, int M, int G, int num_wg, const
     return;
   }
   // Number of long blocks: the leading entries of `order` whose count exceeds
-  // twice the mean (the same test the host applies), by bisection.
+  // twice the mean (the same test the host applies).  The lanes test 64
+  // entries at once (two dependent loads, where a bisection took two per
+  // step); the first chunk that holds a short block ends the prefix.
   const int64_t total = ptr[M];
-  auto is_long = [&](int k) {
-    const int b = order[k];
-    return (int64_t)(ptr[b + 1] - ptr[b]) * M > 2 * total;
-  };
-  int lo = 0, hi = M;  // is_long holds on [0, lo) and fails on [hi, M)
-  while (lo < hi) {
-    const int mid = (lo + hi) / 2;
-    if (is_long(mid)) lo = mid + 1;
-    else hi = mid;
+  const int lane = threadIdx.x & (kWave - 1);
+  int lo = 0;
+  for (int k0 = 0; k0 < M; k0 += kWave) {
+    const int k = k0 + lane;
+    bool is_long = false;
+    if (k < M) {
+      const int b = order[k];
+      is_long = (int64_t)(ptr[b + 1] - ptr[b]) * M > 2 * total;
+    }
+    const uint64_t longs = __builtin_amdgcn_ballot_w64(is_long);
+    lo += __builtin_popcountll(longs);
+    if (longs != ~0ull) break;
   }
   const int nlong = (lo + G - 1) / G;  // groups holding a long block
   const int bhs = num_wg / NG;
@@ -122,17 +127,20 @@ __device__ __forceinline__ int group_block(int grp, int g, int G, int M, const i
 // bitmap[0, MW) marks the union and bitmap[(1 + g) MW, ...) block g's own
 // list (with the causal bound applied: dir < 0 keeps j <= blk, dir > 0 keeps
 // j >= blk).  The block's `loader` wave marks its entries; wave 0 then writes
-// the union into `list`.  Returns the union's size.
+// the union into `list`.  Returns the union's size.  `first` is idx[s + lane]
+// (for s + lane < e), which the loader read before its operand loads: the
+// vector-memory counter drains in order, so a load issued after them would
+// wait for all of them.
 template <int G>
-__device__ int build_union(const int32_t* idx, int s, int e, bool loader, int g, int blk,
-                           int dir, int M, int32_t* list, uint32_t* bitmap, int32_t* size,
-                           int lane, int wave) {
+__device__ int build_union(const int32_t* idx, int s, int e, int first, bool loader, int g,
+                           int blk, int dir, int M, int32_t* list, uint32_t* bitmap,
+                           int32_t* size, int lane, int wave) {
   const int MW = (M + 31) / 32;
   for (int i = threadIdx.x; i < (G + 1) * MW; i += blockDim.x) bitmap[i] = 0;
   __syncthreads();
   if (loader) {
     for (int t = s + lane; t < e; t += kWave) {
-      const int j = idx[t];
+      const int j = t < s + kWave ? first : idx[t];
       if (j >= 0 && j < M && (dir == 0 || (dir < 0 ? j <= blk : j >= blk))) {
         atomicOr(&bitmap[j >> 5], 1u << (j & 31));
         atomicOr(&bitmap[(1 + g) * MW + (j >> 5)], 1u << (j & 31));
@@ -253,8 +261,13 @@ __device__ __forceinline__ ListHead list_head(const int32_t* idx, int start, int
 // ---------------------------------------------------------------- dQ (and D)
 // G query blocks per workgroup (G > 1): they share each K/V stage of the
 // union of their rows; a wave computes the entries its own row selects.
+// bf16, block 32, d = 64, four blocks per workgroup: held to 128 VGPRs (from
+// 130), so four waves per SIMD instead of three (the B = 32 worked example's
+// dQ kernel 12% faster).
 template <typename T, int BS, int D, int G, bool CAUSAL>
-__global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 0, G>::W)) void bsa_bwd_dq(BwdParams p) {
+__global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 0, G>::W))
+__attribute__((amdgpu_waves_per_eu(std::is_same<T, __bf16>::value && BS == 32 && D == 64 && G == 4 ? 4 : 1)))
+void bsa_bwd_dq(BwdParams p) {
   using C = BwdCfg<T, BS, D, 0, G>;
   using L = typename C::L;
   using O = Ops<T>;
@@ -288,23 +301,25 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 0, G>::W)) void bsa_bwd_d
   ListHead lh{0, 0, -1};
   int U;
   const uint32_t* my_bits = reinterpret_cast<const uint32_t*>(dyn + M) + (1 + g) * ((M + 31) / 32);
+  // The list's first entries, then the operand loads, whose latency the
+  // union build and the first copies overlap.
+  const int rs = has ? row_ptr[qb] : 0, re = has ? row_ptr[qb + 1] : 0;
+  int first = -1;
   if constexpr (G == 1) {
-    lh = list_head(p.col_idx, row_ptr[qb], row_ptr[qb + 1], lane);
+    lh = list_head(p.col_idx, rs, re, lane);
     U = lh.n;
   } else {
-    const int rs = has ? row_ptr[qb] : 0, re = has ? row_ptr[qb + 1] : 0;
-    U = build_union<G>(p.col_idx, rs, re, has && qg == 0, g, qb, CAUSAL ? -1 : 0, M, dyn,
-                       reinterpret_cast<uint32_t*>(dyn + M), &union_size, lane, wave);
+    if (has && qg == 0 && lane < re - rs) first = p.col_idx[rs + lane];
   }
   typename O::template QOperand<D> qop, dop, oop;
   O::template load_q<D>(qop, static_cast<const T*>(p.q) + head + (size_t)q0 * D, lane);
   O::template load_q<D>(dop, static_cast<const T*>(p.dout) + head + (size_t)q0 * D, lane);
   O::template load_q<D>(oop, static_cast<const T*>(p.o) + head + (size_t)q0 * D, lane);
-  const float lse2 = p.lse[(size_t)bh * p.N + row] * kLog2e;
-
-  // D for this lane's row; the lane half h = 0 stores it for bsa_bwd_dkv.
-  const float dsum = halves_sum(operand_dot<T, D>(dop, oop));
-  if (has && (lane >> 5) == 0) p.delta[(size_t)bh * p.N + row] = dsum;
+  const float lse_raw = p.lse[(size_t)bh * p.N + row];
+  if constexpr (G > 1)
+    U = build_union<G>(p.col_idx, rs, re, first, has && qg == 0, g, qb, CAUSAL ? -1 : 0, M, dyn,
+                       reinterpret_cast<uint32_t*>(dyn + M), &union_size, lane, wave);
+  float lse2 = 0.f, dsum = 0.f;  // set once the operand loads have landed
 
   int chunk_base = -kWave, chunk = -1;
   uint64_t chunk_sel = 0;
@@ -383,7 +398,6 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 0, G>::W)) void bsa_bwd_d
   bool mq[NB];
 #pragma unroll
   for (int e = 0; e < NB; ++e) jq[e] = entry_at(e, mq[e]);
-  wait_vm_lgkm0<0>();  // Q, dO, O, LSE loads and the first entries are complete
   auto buffer = [&](auto b_c) -> unsigned char* {
     constexpr int b = decltype(b_c)::value;
     if constexpr (b == 0) return buf0;
@@ -391,10 +405,18 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 0, G>::W)) void bsa_bwd_d
     else if constexpr (b == 2) return buf2;
     else return buf3;
   };
-  // The first NB - 1 copies, for the entries there are (none for an empty list).
+  // The first NB - 1 copies, for the entries there are (none for an empty
+  // list), go out while the operand loads are still in flight; then
+  // everything issued so far is waited for (the compiler does not count the
+  // copies, so a later wait of its own for the operands would be a full one).
   if (U > 0) issue(jq[0], buf0);
   if (NB >= 3 && U > 1) issue(jq[1], buf1);
   if (NB >= 4 && U > 2) issue(jq[2], buf2);
+  wait_vm_lgkm0<0>();
+  lse2 = lse_raw * kLog2e;
+  // D for this lane's row; the lane half h = 0 stores it for bsa_bwd_dkv.
+  dsum = halves_sum(operand_dot<T, D>(dop, oop));
+  if (has && (lane >> 5) == 0) p.delta[(size_t)bh * p.N + row] = dsum;
   auto step = [&](int i, auto b_c) {
     constexpr int b = decltype(b_c)::value;
     // this wave's copies of entry i have landed; those of the min(NB - 2,
@@ -480,17 +502,22 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 8 * BS, G>::W)) void bsa_
   ListHead lh{0, 0, -1};
   int U;
   const uint32_t* my_bits = reinterpret_cast<const uint32_t*>(dyn + M) + (1 + g) * ((M + 31) / 32);
+  // The list's first entries, then the operand loads, whose latency the
+  // union build and the first copies overlap.
+  const int cs = has ? col_ptr[kb] : 0, ce = has ? col_ptr[kb + 1] : 0;
+  int first = -1;
   if constexpr (G == 1) {
-    lh = list_head(p.row_idx, col_ptr[kb], col_ptr[kb + 1], lane);
+    lh = list_head(p.row_idx, cs, ce, lane);
     U = lh.n;
   } else {
-    const int cs = has ? col_ptr[kb] : 0, ce = has ? col_ptr[kb + 1] : 0;
-    U = build_union<G>(p.row_idx, cs, ce, has && kg == 0, g, kb, CAUSAL ? 1 : 0, M, dyn,
-                       reinterpret_cast<uint32_t*>(dyn + M), &union_size, lane, wave);
+    if (has && kg == 0 && lane < ce - cs) first = p.row_idx[cs + lane];
   }
   typename O::template QOperand<D> kop, vop;
   O::template load_q<D>(kop, static_cast<const T*>(p.k) + head + (size_t)k0 * D, lane);
   O::template load_q<D>(vop, static_cast<const T*>(p.v) + head + (size_t)k0 * D, lane);
+  if constexpr (G > 1)
+    U = build_union<G>(p.row_idx, cs, ce, first, has && kg == 0, g, kb, CAUSAL ? 1 : 0, M, dyn,
+                       reinterpret_cast<uint32_t*>(dyn + M), &union_size, lane, wave);
 
   int chunk_base = -kWave, chunk = -1;
   uint64_t chunk_sel = 0;
@@ -591,7 +618,6 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 8 * BS, G>::W)) void bsa_
   bool mq[NB];
 #pragma unroll
   for (int e = 0; e < NB; ++e) jq[e] = entry_at(e, mq[e]);
-  wait_vm_lgkm0<0>();  // K, V loads and the list are complete
   auto buffer = [&](auto b_c) -> unsigned char* {
     constexpr int b = decltype(b_c)::value;
     if constexpr (b == 0) return buf0;
@@ -599,10 +625,13 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 8 * BS, G>::W)) void bsa_
     else if constexpr (b == 2) return buf2;
     else return buf3;
   };
-  // The first NB - 1 copies, for the entries there are (none for an empty list).
+  // The first NB - 1 copies, for the entries there are (none for an empty
+  // list), go out while the K and V loads are still in flight; then
+  // everything issued so far is waited for.
   if (U > 0) issue(jq[0], buf0);
   if (NB >= 3 && U > 1) issue(jq[1], buf1);
   if (NB >= 4 && U > 2) issue(jq[2], buf2);
+  wait_vm_lgkm0<0>();
   // Waits for this wave's copies of the current entry, leaving those of `k`
   // later entries in flight (a stage is kParts tile copies plus n_vec).
   auto wait_leaving = [&](auto k_c) {
