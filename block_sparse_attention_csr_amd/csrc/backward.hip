@@ -10,10 +10,11 @@
 //   dV = P^T dO,  dP = dO V^T,  D_r = dO_r . O_r,  dS = P * (dP - D),
 //   dQ = scale dS K,  dK = scale dS^T Q.
 //
-// Two kernels, both one workgroup per (batch, head, block) with 32 rows per
-// wave, both streaming tiles through an LDS ring with direct-to-LDS copies:
-//  * bsa_bwd_dq: per query block, walks its CSR row (the K blocks it
-//    selects); K and V tiles in the ring.  It also writes D for its rows.
+// Two kernels with 32 rows per wave, both streaming tiles through an LDS ring
+// with direct-to-LDS copies:
+//  * bsa_bwd_dq: per query block (or per group of four at block 32 on a large
+//    grid), walks its CSR row (the K blocks it selects); K and V tiles in the
+//    ring.  It also writes D for its rows.
 //    S^T = K Q^T and dP^T = V dO^T keep one query per lane, so P and dS are
 //    per-lane arithmetic; dQ^T += K^T dS^T reads K transposed from LDS.
 //  * bsa_bwd_dkv: per key block, walks its CSC column (the query blocks that
@@ -61,7 +62,7 @@ struct BwdParams {
   const int32_t* col_order;  // key blocks, most entries first (or NULL: ascending)
   int32_t M;
   int32_t N;
-  int32_t num_wg;  // batch * heads * M
+  int32_t num_wg;  // workgroups of the launch: batch * heads * ceil(M / blocks per workgroup)
   int32_t heads;
   int32_t ptr_stride;  // row_ptr / col_ptr entries per head: M + 1 (one pattern per head) or 0
   float scale;
@@ -459,38 +460,35 @@ void bsa_bwd_dq(BwdParams p) {
 }
 
 // ---------------------------------------------------------------- dK, dV
-// G key blocks per workgroup (G > 1): they share each Q/dO stage of the
-// union of their columns; a wave computes the entries its own column holds.
-template <typename T, int BS, int D, int G, bool CAUSAL>
-__global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 8 * BS, G>::W)) void bsa_bwd_dkv(
+// One key block per workgroup.  (Four blocks sharing the stages of the union
+// of their columns, as bsa_bwd_dq does at block 32, measured slower here:
+// the log-linear columns of neighbouring key blocks share few query blocks,
+// so each wave idled through about 40% of the union's steps.)
+template <typename T, int BS, int D, bool CAUSAL>
+__global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 8 * BS>::W)) void bsa_bwd_dkv(
     BwdParams p) {
-  using C = BwdCfg<T, BS, D, 8 * BS, G>;  // Q tile, dO tile, then LSE[BS] and D[BS] floats
+  using C = BwdCfg<T, BS, D, 8 * BS>;  // Q tile, dO tile, then LSE[BS] and D[BS] floats
   using L = typename C::L;
   using O = Ops<T>;
   constexpr int NB = C::NB;
+  static_assert(NB <= 3, "one key block per workgroup keeps a ring of up to three stages");
   constexpr int QSTEPS = BS / kQRows;
   constexpr int kVecOff = L::kEntryBytes;          // LSE floats, then D floats
 
   __shared__ __attribute__((aligned(16))) unsigned char buf0[C::kStage];
   __shared__ __attribute__((aligned(16))) unsigned char buf1[C::kStage];
   __shared__ __attribute__((aligned(16))) unsigned char buf2[NB >= 3 ? C::kStage : 16];
-  __shared__ __attribute__((aligned(16))) unsigned char buf3[NB >= 4 ? C::kStage : 16];
-  extern __shared__ __attribute__((aligned(16))) int32_t dyn[];  // (G > 1) union list | bitmaps
-  __shared__ int32_t union_size;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = uniform(threadIdx.x / kWave);
-  const int kg = wave % C::QW;  // 32-key group of the block
-  const int g = wave / C::QW;   // block of the workgroup
+  const int kg = wave;  // 32-key group of the block
   // dword copies per stage by this wave: LSE by wave 0, D by wave 1 (or
   // both by the one wave of a one-wave workgroup)
   const int n_vec = C::W == 1 ? 2 : wave < 2 ? 1 : 0;
   const int M = p.M;
-  int bh, grp;
-  group_of(xcd_remap(blockIdx.x, p.num_wg), M, G, p.num_wg, p.col_order, p.col_ptr, bh, grp);
-  const int blk = group_block(grp, g, G, M, p.col_order);
-  const bool has = blk >= 0;
-  const int kb = has ? blk : 0;
+  int bh, kb;
+  group_of(xcd_remap(blockIdx.x, p.num_wg), M, 1, p.num_wg, p.col_order, p.col_ptr, bh, kb);
+  kb = group_block(kb, 0, 1, M, p.col_order);
   const int32_t* const col_ptr = p.col_ptr + (size_t)(bh % p.heads) * p.ptr_stride;
   const size_t head = (size_t)bh * p.N * D;
   const T* Qh = static_cast<const T*>(p.q) + head;
@@ -499,25 +497,13 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 8 * BS, G>::W)) void bsa_
   const float* del_h = p.delta + (size_t)bh * p.N;
   const int k0 = kb * BS + kg * kQRows;
 
-  ListHead lh{0, 0, -1};
-  int U;
-  const uint32_t* my_bits = reinterpret_cast<const uint32_t*>(dyn + M) + (1 + g) * ((M + 31) / 32);
-  // The list's first entries, then the operand loads, whose latency the
-  // union build and the first copies overlap.
-  const int cs = has ? col_ptr[kb] : 0, ce = has ? col_ptr[kb + 1] : 0;
-  int first = -1;
-  if constexpr (G == 1) {
-    lh = list_head(p.row_idx, cs, ce, lane);
-    U = lh.n;
-  } else {
-    if (has && kg == 0 && lane < ce - cs) first = p.row_idx[cs + lane];
-  }
+  // The column's first entries, then the K and V loads, whose latency the
+  // first copies overlap.
+  const ListHead lh = list_head(p.row_idx, col_ptr[kb], col_ptr[kb + 1], lane);
+  const int U = lh.n;
   typename O::template QOperand<D> kop, vop;
   O::template load_q<D>(kop, static_cast<const T*>(p.k) + head + (size_t)k0 * D, lane);
   O::template load_q<D>(vop, static_cast<const T*>(p.v) + head + (size_t)k0 * D, lane);
-  if constexpr (G > 1)
-    U = build_union<G>(p.row_idx, cs, ce, first, has && kg == 0, g, kb, CAUSAL ? 1 : 0, M, dyn,
-                       reinterpret_cast<uint32_t*>(dyn + M), &union_size, lane, wave);
 
   int chunk_base = -kWave, chunk = -1;
   uint64_t chunk_sel = 0;
@@ -529,15 +515,8 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 8 * BS, G>::W)) void bsa_
     if ((t & ~(kWave - 1)) != chunk_base) {
       chunk_base = t & ~(kWave - 1);
       const int idx = chunk_base + lane;
-      bool sel;
-      if constexpr (G == 1) {
-        chunk = chunk_base == 0 ? lh.first : idx < U ? p.row_idx[lh.start + idx] : -1;
-        sel = chunk >= 0 && chunk < M && (!CAUSAL || chunk >= kb);
-      } else {  // the union holds only selected, in-range blocks
-        chunk = idx < U ? dyn[idx] : -1;
-        const int cj = chunk < 0 ? 0 : chunk;
-        sel = has && chunk >= 0 && ((my_bits[cj >> 5] >> (cj & 31)) & 1u) != 0;
-      }
+      chunk = chunk_base == 0 ? lh.first : idx < U ? p.row_idx[lh.start + idx] : -1;
+      const bool sel = chunk >= 0 && chunk < M && (!CAUSAL || chunk >= kb);
       chunk_sel = __builtin_amdgcn_ballot_w64(sel);
     }
     use = ((chunk_sel >> (t - chunk_base)) & 1ull) != 0;
@@ -622,15 +601,13 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 8 * BS, G>::W)) void bsa_
     constexpr int b = decltype(b_c)::value;
     if constexpr (b == 0) return buf0;
     else if constexpr (b == 1) return buf1;
-    else if constexpr (b == 2) return buf2;
-    else return buf3;
+    else return buf2;
   };
   // The first NB - 1 copies, for the entries there are (none for an empty
   // list), go out while the K and V loads are still in flight; then
   // everything issued so far is waited for.
   if (U > 0) issue(jq[0], buf0);
   if (NB >= 3 && U > 1) issue(jq[1], buf1);
-  if (NB >= 4 && U > 2) issue(jq[2], buf2);
   wait_vm_lgkm0<0>();
   // Waits for this wave's copies of the current entry, leaving those of `k`
   // later entries in flight (a stage is kParts tile copies plus n_vec).
@@ -644,8 +621,7 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 8 * BS, G>::W)) void bsa_
     constexpr int b = decltype(b_c)::value;
     // the min(NB - 2, U - 1 - i) later entries already issued may stay in flight
     const int ahead = U - 1 - i;
-    if (NB >= 4 && ahead >= 2) wait_leaving(std::integral_constant<int, NB >= 4 ? 2 : 0>{});
-    else if (NB >= 3 && ahead >= 1) wait_leaving(std::integral_constant<int, NB >= 3 ? 1 : 0>{});
+    if (NB >= 3 && ahead >= 1) wait_leaving(std::integral_constant<int, NB >= 3 ? 1 : 0>{});
     else wait_vm_lgkm0<0>();
     raw_barrier();
     const bool use = mq[0];
@@ -664,18 +640,12 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 8 * BS, G>::W)) void bsa_
     if (i + 1 < U) step(i + 1, std::integral_constant<int, 1>{});
     if constexpr (NB >= 3)
       if (i + 2 < U) step(i + 2, std::integral_constant<int, 2>{});
-    if constexpr (NB >= 4)
-      if (i + 3 < U) step(i + 3, std::integral_constant<int, 3>{});
   }
 
   // dK then dV leave through this wave's part of the idle ring.
   wait_vm_lgkm0<0>();  // no copy is still landing (the compiler does not track them)
   __syncthreads();     // every wave is done with the ring
-  if (!has) return;
-  unsigned char* const stage_buf = wave < C::kPerBuf       ? buf0
-                                  : wave < 2 * C::kPerBuf ? buf1
-                                  : wave < 3 * C::kPerBuf ? buf2
-                                                          : buf3;
+  unsigned char* const stage_buf = wave < C::kPerBuf ? buf0 : wave < 2 * C::kPerBuf ? buf1 : buf2;
   LDS_PTR(unsigned char) region =
       (LDS_PTR(unsigned char))stage_buf + (wave % C::kPerBuf) * C::kRowsStage;
   store_rows_lds<T, D>(static_cast<T*>(p.dk) + head + (size_t)k0 * D, dk, p.scale, lane, region);
@@ -688,19 +658,21 @@ constexpr size_t kMaxLds = 160 * 1024;
 
 template <typename T, int BS, int D, int G, bool CAUSAL>
 bsa_status launch_bwd(const BwdParams& p, hipStream_t stream) {
-  const dim3 grid(p.num_wg);
-  const dim3 block(kWave * BwdCfg<T, BS, D, 0, G>::W);
+  // dQ: G blocks per workgroup; dK/dV: one
   const size_t dyn = union_lds_bytes(G, p.M);
+  BwdParams pk = p;
+  pk.num_wg = p.num_wg / ((p.M + G - 1) / G) * p.M;
   // Shapes with more than 64 KB of LDS need the per-kernel limit raised, once
   // per device.
   static std::atomic<uint64_t> raised{0};
   uint64_t bit;
   const void* kernels[2] = {reinterpret_cast<const void*>(&bsa_bwd_dq<T, BS, D, G, CAUSAL>),
-                            reinterpret_cast<const void*>(&bsa_bwd_dkv<T, BS, D, G, CAUSAL>)};
-  for (const void* f : kernels) {
+                            reinterpret_cast<const void*>(&bsa_bwd_dkv<T, BS, D, CAUSAL>)};
+  const size_t dyns[2] = {dyn, 0};
+  for (int i = 0; i < 2; ++i) {
     hipFuncAttributes attr;
-    if (hipFuncGetAttributes(&attr, f) != hipSuccess) return BSA_ERR_HIP;
-    if (attr.sharedSizeBytes + dyn > kMaxLds) return BSA_ERR_INVALID_ARGUMENT;
+    if (hipFuncGetAttributes(&attr, kernels[i]) != hipSuccess) return BSA_ERR_HIP;
+    if (attr.sharedSizeBytes + dyns[i] > kMaxLds) return BSA_ERR_INVALID_ARGUMENT;
   }
   if (due_on_device(raised, &bit)) {
     for (const void* f : kernels) {
@@ -712,9 +684,11 @@ bsa_status launch_bwd(const BwdParams& p, hipStream_t stream) {
     }
     mark_done(raised, bit);
   }
-  hipLaunchKernelGGL((bsa_bwd_dq<T, BS, D, G, CAUSAL>), grid, block, dyn, stream, p);
+  hipLaunchKernelGGL((bsa_bwd_dq<T, BS, D, G, CAUSAL>), dim3(p.num_wg),
+                     dim3(kWave * BwdCfg<T, BS, D, 0, G>::W), dyn, stream, p);
   if (hipGetLastError() != hipSuccess) return BSA_ERR_HIP;
-  hipLaunchKernelGGL((bsa_bwd_dkv<T, BS, D, G, CAUSAL>), grid, block, dyn, stream, p);
+  hipLaunchKernelGGL((bsa_bwd_dkv<T, BS, D, CAUSAL>), dim3(pk.num_wg),
+                     dim3(kWave * BwdCfg<T, BS, D, 8 * BS>::W), 0, stream, pk);
   return hipGetLastError() == hipSuccess ? BSA_OK : BSA_ERR_HIP;
 }
 
@@ -759,12 +733,13 @@ int64_t device_cus() {
   return n;
 }
 
-// Blocks per workgroup.  Block 32 on a large grid (eight one-wave blocks
-// per SIMD or more): four blocks share each stage of the union of their
-// lists, so a K/V (or Q/dO) tile is copied once for four waves instead of
-// once per wave.  Otherwise (block 64 holds two waves already; small grids
-// want every block's own short chain) one block.  The union list and its
-// bitmaps must fit beside the ring (M up to a few thousand blocks).
+// Query blocks per dQ workgroup.  Block 32 on a large grid (eight one-wave
+// blocks per SIMD or more): four blocks share each stage of the union of
+// their rows, so a K/V tile is copied once for four waves instead of once per
+// wave.  Otherwise (block 64 holds two waves already; small grids want every
+// block's own short chain) one block.  The union list and its bitmaps must
+// fit beside the ring (M up to a few thousand blocks).  The dK/dV kernel
+// always takes one key block per workgroup.
 int choose_group(int64_t bhm, int bs, int M) {
   if (bs != 32 || bhm < 8 * 4 * device_cus()) return 1;
   if (union_lds_bytes(4, M) > 32 * 1024) return 1;
