@@ -287,11 +287,11 @@ def test_backward_more_than_4096_blocks_sampled():
 @pytest.mark.parametrize("kind,causal", [("loglinear", False), ("loglinear", True),
                                          ("random", False), ("random", True)])
 def test_backward_grouped_blocks_sampled_heads(kind, causal, d):
-    """Block 32 on a large grid (B H M = 16384 query blocks): four blocks per
-    workgroup share each stage of the union of their lists.  With the
-    longest-first orders the log-linear pattern's anchor columns share one
-    group.  Sampled heads against the oracle on those heads (every head is
-    independent), and the same result as the ascending order."""
+    """Block 32 on a large grid (B H M = 16384 query blocks): four query
+    blocks per dQ workgroup share each K/V stage of the union of their rows
+    (the dK/dV kernel takes one key block per workgroup).  Sampled heads
+    against the oracle on those heads (every head is independent), and the
+    same result as the ascending order."""
     B, H, bs, M = 16, 8, 32, 128
     N = M * bs
     seed = zlib.crc32(repr(("grouped", kind, causal, d)).encode()) % 1000
@@ -311,3 +311,35 @@ def test_backward_grouped_blocks_sampled_heads(kind, causal, d):
         for name, got, want in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref[:3]):
             _check(f"{name} ({b}, {h}) {kind} causal={causal} d{d}", got[b:b + 1, h:h + 1],
                    want, torch.bfloat16)
+
+
+@pytest.mark.parametrize("which", ["rows", "columns"])
+def test_backward_more_than_64_long_blocks(which):
+    """70 of M = 160 blocks are long (more than twice the mean entry count):
+    the kernels count the long blocks of a work order 64 at a time, so this
+    count spans two chunks.  "rows": query blocks 0..69 select every key
+    block, the others their own; "columns": the transpose, key blocks 0..69
+    selected by every query block.  On a grid large enough for grouped dQ
+    workgroups (B H M = 10240); the ordered result must equal the ascending
+    one bit for bit (a miscounted prefix would drop or repeat blocks), and
+    sampled heads match the oracle."""
+    B, H, bs, d, M, L = 8, 8, 32, 64, 160, 70
+    N = M * bs
+    mask = np.zeros((M, M), np.uint8)
+    if which == "rows":
+        mask[:L, :] = 1
+    else:
+        mask[:, :L] = 1
+    np.fill_diagonal(mask, 1)
+    counts = mask.sum(axis=1 if which == "rows" else 0)
+    assert int((counts * M > 2 * counts.sum()).sum()) == L
+    seed = zlib.crc32(repr(("long blocks", which)).encode()) % 1000
+    q, k, v = make_qkv(B, H, N, d, torch.bfloat16, seed)
+    do = make_qkv(B, H, N, d, torch.bfloat16, seed + 1)[0]
+    dq, dk, dv = _run(q, k, v, do, bs, mask, False)
+    for b, h in ((0, 0), (B - 1, H - 1)):
+        f = lambda x: _f64(x[b:b + 1, h:h + 1])
+        ref = oracle.block_sparse_attention_backward(f(q), f(k), f(v), f(do), mask, bs)
+        for name, got, want in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref[:3]):
+            _check(f"{name} ({b}, {h}) long {which}", got[b:b + 1, h:h + 1], want,
+                   torch.bfloat16)
