@@ -35,6 +35,7 @@ PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix
 PEAK_HBM_GBPS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "block_sparse_attention_csr_amd", "csrc", "forward.hip")
 DECODE_SRC = os.path.join(ROOT, "block_sparse_attention_csr_amd", "csrc", "decode.hip")
+BACKWARD_SRC = os.path.join(ROOT, "block_sparse_attention_csr_amd", "csrc", "backward.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 DECODE_METRIC = "decode GB/s (algorithmic bytes: visible K/V rows) + % of 8 TB/s HBM peak"
 
@@ -635,7 +636,8 @@ def side_line(name, args, device, causal, backward=False, int8_kv=False):
     s_step = s_graph if s_graph is not None else time_eager(sat, sat_steps)
     s_kernel = s_evt if s_evt is not None else s_launch
     record = name + ("_int8kv" if int8_kv else "")
-    s_traffic = None if causal or backward else load_traffic(record)
+    s_traffic = (None if causal else load_traffic(record, "bsa_bwd", BACKWARD_SRC) if backward
+                 else load_traffic(record))
     s_mfma = None if causal or backward else load_mfma(record)
     line = {
         "value": round(sat.flops / s_step / 1e12, 3),
