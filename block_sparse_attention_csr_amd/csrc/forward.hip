@@ -292,13 +292,19 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS, KV8, RING>::W)) void 
       (KV8 ? buf0 : NB == 3 ? buf2 : buf1) + (ks * QW + qg) * QL::kTileBytes;
   if constexpr (kStageQ) {
     const uint32_t dst = (uint32_t)(uintptr_t)(LDS_PTR(unsigned char))q_stage;
+    constexpr int kQParts = QL::kTileBytes / (kWave * 16);
+    constexpr int kQRun = dma_run(kQParts, kQParts);
 #pragma unroll
-    for (int part = 0; part < QL::kTileBytes / (kWave * 16); ++part) {
-      const int slot = part * kWave + lane;
-      const int row = slot / QL::kChunksPerRow;
-      const int chunk = (slot % QL::kChunksPerRow) ^ QL::swz(row);
-      lds_dma16(Q + (size_t)q0 * D, (uint32_t)(row * QL::kRowBytes + chunk * 16),
-                dst + part * kWave * 16);
+    for (int r = 0; r < kQParts / kQRun; ++r) {
+      uint32_t v[kQRun];
+#pragma unroll
+      for (int k = 0; k < kQRun; ++k) {
+        const int slot = (r * kQRun + k) * kWave + lane;
+        const int row = slot / QL::kChunksPerRow;
+        const int chunk = (slot % QL::kChunksPerRow) ^ QL::swz(row);
+        v[k] = (uint32_t)(row * QL::kRowBytes + chunk * 16 - k * kWave * 16);
+      }
+      lds_dma16_run<kQRun>(Q + (size_t)q0 * D, v, dst + r * kQRun * kWave * 16);
     }
   } else {
     O::template load_q<D>(qop, Q + (size_t)q0 * D, lane);
@@ -399,23 +405,33 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS, KV8, RING>::W)) void 
   // entry (1 KB: slots 64 (ws + c SW) .. +64); lane i fetches the 16-byte
   // global chunk the swizzle places in its slot.
   constexpr int kPartsPerTile = L::kCopies / 2;
-  int dma_off[C::kParts];
+  // Wave ws copies parts ws kParts .. ws kParts + kParts - 1 of each entry,
+  // in runs of kRun consecutive parts behind one M0 write (a run lies in the
+  // K tile or in the V tile, never both); dma_off carries the run's
+  // immediate offset taken off.
+  constexpr int kRun = dma_run(C::kParts, kPartsPerTile);
+  uint32_t dma_off[C::kParts];
 #pragma unroll
   for (int c = 0; c < C::kParts; ++c) {
-    const int part = (ws + c * SW) % kPartsPerTile;
+    const int part = (ws * C::kParts + c) % kPartsPerTile;
     const int slot = part * kWave + lane;
     const int row = slot / L::kChunksPerRow;
     const int chunk = (slot % L::kChunksPerRow) ^ L::swz(row);
-    dma_off[c] = row * L::kRowBytes + chunk * 16;
+    dma_off[c] = (uint32_t)(row * L::kRowBytes + chunk * 16 - (c % kRun) * kWave * 16);
   }
   auto issue = [&](int j, unsigned char* buf) {
-    const int key0 = (j < 0 || j >= M ? 0 : j) * BS;  // a missing entry copies block 0 (unused)
-    const uint32_t dst = (uint32_t)(uintptr_t)(LDS_PTR(unsigned char))buf + ks * C::kEntry;
+    // a missing entry copies block 0 (unused)
+    const size_t key0 = (size_t)((uint32_t)j < (uint32_t)M ? (uint32_t)j : 0u) * BS;
+    const uint32_t dst = (uint32_t)(uintptr_t)(LDS_PTR(unsigned char))buf + ks * C::kEntry +
+                         ws * C::kParts * kWave * 16;
 #pragma unroll
-    for (int c = 0; c < C::kParts; ++c) {
-      const int part = ws + c * SW;
-      const T* base = (part < kPartsPerTile ? K : V) + (size_t)key0 * D;
-      lds_dma16(base, (uint32_t)dma_off[c], dst + part * kWave * 16);
+    for (int r = 0; r < C::kParts / kRun; ++r) {
+      const int part = ws * C::kParts + r * kRun;
+      uint32_t v[kRun];
+#pragma unroll
+      for (int k = 0; k < kRun; ++k) v[k] = dma_off[r * kRun + k];
+      lds_dma16_run<kRun>((part < kPartsPerTile ? K : V) + key0 * D, v,
+                          dst + r * kRun * kWave * 16);
     }
   };
   // (KV8) copies of an entry's int8 codes as they are: part c of this wave
@@ -616,20 +632,29 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS, KV8, RING>::W)) void 
     // (no wave idles on another row's entries) keeps two waves per SIMD.
     constexpr int kTile = L::kTileBytes;
     constexpr int kPartsT = kPartsPerTile / SW;  // 1 KB copies per wave per tile
-    int toff[kPartsT];
+    constexpr int kRunT = dma_run(kPartsT, kPartsT);
+    uint32_t toff[kPartsT];  // wave ws: parts ws kPartsT .. + kPartsT - 1 of a tile
 #pragma unroll
     for (int c = 0; c < kPartsT; ++c) {
-      const int slot = (ws + c * SW) * kWave + lane;
+      const int slot = (ws * kPartsT + c) * kWave + lane;
       const int row = slot / L::kChunksPerRow;
-      toff[c] = row * L::kRowBytes + (((slot % L::kChunksPerRow) ^ L::swz(row)) << 4);
+      toff[c] = (uint32_t)(row * L::kRowBytes +
+                           (((slot % L::kChunksPerRow) ^ L::swz(row)) << 4) -
+                           (c % kRunT) * kWave * 16);
     }
     const uint32_t kslot = (uint32_t)(uintptr_t)(LDS_PTR(unsigned char))buf0;
     const uint32_t vslot = (uint32_t)(uintptr_t)(LDS_PTR(unsigned char))buf1;
     auto issue_tile = [&](const T* src, int j, uint32_t dst) {
-      const int key0 = (j < 0 || j >= M ? 0 : j) * BS;  // a missing entry copies block 0 (unused)
+      // a missing entry copies block 0 (unused)
+      const size_t key0 = (size_t)((uint32_t)j < (uint32_t)M ? (uint32_t)j : 0u) * BS;
 #pragma unroll
-      for (int c = 0; c < kPartsT; ++c)
-        lds_dma16(src + (size_t)key0 * D, (uint32_t)toff[c], dst + (ws + c * SW) * kWave * 16);
+      for (int r = 0; r < kPartsT / kRunT; ++r) {
+        uint32_t v[kRunT];
+#pragma unroll
+        for (int k = 0; k < kRunT; ++k) v[k] = toff[r * kRunT + k];
+        lds_dma16_run<kRunT>(src + key0 * D, v,
+                             dst + (ws * kPartsT + r * kRunT) * kWave * 16);
+      }
     };
     bool m0, m1;
     int j0 = entry_at(0, m0);

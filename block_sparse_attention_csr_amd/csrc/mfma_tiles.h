@@ -498,6 +498,45 @@ __device__ __forceinline__ void lds_dma16(const void* sbase, uint32_t voff, uint
                : "memory", "m0");
 }
 
+// N (1, 2 or 4) such copies behind one M0 write.  Copy c reads
+// sbase + voff[c] + c KB and lands at m0 + c KB + 16 i: the instruction's
+// immediate offset is added to both the global and the LDS address, so the
+// caller passes voff[c] = (its global offset) - c KB.  The offsets stay
+// within the signed 13-bit field (at most 3 KB).
+template <int N>
+__device__ __forceinline__ void lds_dma16_run(const void* sbase, const uint32_t (&voff)[N],
+                                              uint32_t m0) {
+  static_assert(N == 1 || N == 2 || N == 4, "runs of 1, 2 or 4 copies");
+  const void* b = uniform_ptr(sbase);
+  const uint32_t m = (uint32_t)__builtin_amdgcn_readfirstlane((int)m0);
+  if constexpr (N == 1) {
+    lds_dma16(b, voff[0], m);
+  } else if constexpr (N == 2) {
+    asm volatile(
+        "s_mov_b32 m0, %3\n\t"
+        "global_load_lds_dwordx4 %0, %2\n\t"
+        "global_load_lds_dwordx4 %1, %2 offset:1024"
+        :
+        : "v"(voff[0]), "v"(voff[1]), "s"(b), "s"(m)
+        : "memory", "m0");
+  } else {
+    asm volatile(
+        "s_mov_b32 m0, %5\n\t"
+        "global_load_lds_dwordx4 %0, %4\n\t"
+        "global_load_lds_dwordx4 %1, %4 offset:1024\n\t"
+        "global_load_lds_dwordx4 %2, %4 offset:2048\n\t"
+        "global_load_lds_dwordx4 %3, %4 offset:3072"
+        :
+        : "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(b), "s"(m)
+        : "memory", "m0");
+  }
+}
+
+// Longest run length (4, 2 or 1) that divides both n and m.
+constexpr int dma_run(int n, int m) {
+  return n % 4 == 0 && m % 4 == 0 ? 4 : n % 2 == 0 && m % 2 == 0 ? 2 : 1;
+}
+
 // Workgroup barrier without a memory fence: the caller has already waited for
 // the memory operations the barrier publishes.  The empty asm statements keep
 // the compiler from moving memory accesses across it.
