@@ -348,22 +348,32 @@ void bsa_bwd_dq(BwdParams p) {
   };
 
   constexpr int kPartsPerTile = L::kCopies / 2;
-  int dma_off[C::kParts];
+  // One-wave workgroups copy every part of a stage, in runs of kRun behind
+  // one M0 write (within one tile; dma_off carries the run's immediate offset
+  // taken off).  Several waves interleave their parts: wave w copies parts
+  // w, w + W, ..., one copy per M0 write (at block 64 and d = 128, the long
+  // workload's backward ran 3.7% slower with each wave copying a whole tile).
+  constexpr int kRun = C::W == 1 ? dma_run(C::kParts, kPartsPerTile) : 1;
+  auto part_of = [&](int c) { return C::W == 1 ? c : wave + c * C::W; };
+  uint32_t dma_off[C::kParts];
 #pragma unroll
   for (int c = 0; c < C::kParts; ++c) {
-    const int part = (wave + c * C::W) % kPartsPerTile;
+    const int part = part_of(c) % kPartsPerTile;
     const int slot = part * kWave + lane;
     const int r = slot / L::kChunksPerRow;
-    dma_off[c] = r * L::kRowBytes + (((slot % L::kChunksPerRow) ^ L::swz(r)) << 4);
+    dma_off[c] = (uint32_t)(r * L::kRowBytes + (((slot % L::kChunksPerRow) ^ L::swz(r)) << 4) -
+                            (c % kRun) * kWave * 16);
   }
   auto issue = [&](int j, unsigned char* buf) {
-    const int key0 = (j < 0 || j >= M ? 0 : j) * BS;
+    const size_t key0 = (size_t)((uint32_t)j < (uint32_t)M ? (uint32_t)j : 0u) * BS;
     const uint32_t dst = (uint32_t)(uintptr_t)(LDS_PTR(unsigned char))buf;
 #pragma unroll
-    for (int c = 0; c < C::kParts; ++c) {
-      const int part = wave + c * C::W;
-      const T* base = (part < kPartsPerTile ? K : V) + (size_t)key0 * D;
-      lds_dma16(base, (uint32_t)dma_off[c], dst + part * kWave * 16);
+    for (int r = 0; r < C::kParts / kRun; ++r) {
+      const int part = part_of(r * kRun);
+      uint32_t v[kRun];
+#pragma unroll
+      for (int k = 0; k < kRun; ++k) v[k] = dma_off[r * kRun + k];
+      lds_dma16_run<kRun>((part < kPartsPerTile ? K : V) + key0 * D, v, dst + part * kWave * 16);
     }
   };
 
@@ -524,22 +534,33 @@ __global__ __launch_bounds__((kWave * BwdCfg<T, BS, D, 8 * BS>::W)) void bsa_bwd
   };
 
   constexpr int kPartsPerTile = L::kCopies / 2;
-  int dma_off[C::kParts];
+  // One-wave workgroups copy every part of a stage, in runs of kRun behind
+  // one M0 write (within one tile; dma_off carries the run's immediate offset
+  // taken off).  Several waves interleave their parts: wave w copies parts
+  // w, w + W, ..., one copy per M0 write (at block 64 and d = 128, the long
+  // workload's backward ran 3.7% slower with each wave copying a whole tile).
+  constexpr int kRun = C::W == 1 ? dma_run(C::kParts, kPartsPerTile) : 1;
+  auto part_of = [&](int c) { return C::W == 1 ? c : wave + c * C::W; };
+  uint32_t dma_off[C::kParts];
 #pragma unroll
   for (int c = 0; c < C::kParts; ++c) {
-    const int part = (wave + c * C::W) % kPartsPerTile;
+    const int part = part_of(c) % kPartsPerTile;
     const int slot = part * kWave + lane;
     const int r = slot / L::kChunksPerRow;
-    dma_off[c] = r * L::kRowBytes + (((slot % L::kChunksPerRow) ^ L::swz(r)) << 4);
+    dma_off[c] = (uint32_t)(r * L::kRowBytes + (((slot % L::kChunksPerRow) ^ L::swz(r)) << 4) -
+                            (c % kRun) * kWave * 16);
   }
   auto issue = [&](int i, unsigned char* buf) {
-    const int q0 = (i < 0 || i >= M ? 0 : i) * BS;
+    const int q0 = (int)((uint32_t)i < (uint32_t)M ? (uint32_t)i : 0u) * BS;
     const uint32_t dst = (uint32_t)(uintptr_t)(LDS_PTR(unsigned char))buf;
 #pragma unroll
-    for (int c = 0; c < C::kParts; ++c) {
-      const int part = wave + c * C::W;
-      const T* base = (part < kPartsPerTile ? Qh : dOh) + (size_t)q0 * D;
-      lds_dma16(base, (uint32_t)dma_off[c], dst + part * kWave * 16);
+    for (int r = 0; r < C::kParts / kRun; ++r) {
+      const int part = part_of(r * kRun);
+      uint32_t v[kRun];
+#pragma unroll
+      for (int k = 0; k < kRun; ++k) v[k] = dma_off[r * kRun + k];
+      lds_dma16_run<kRun>((part < kPartsPerTile ? Qh : dOh) + (size_t)q0 * D, v,
+                          dst + part * kWave * 16);
     }
     // LSE and D of the block's rows (BS floats each): waves 0 and 1 copy
     // one vector each, or the one wave both.
