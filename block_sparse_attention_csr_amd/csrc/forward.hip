@@ -401,14 +401,13 @@ __global__ __launch_bounds__((kWave * Cfg<T, BS, D, G, KS, KV8, RING>::W)) void 
     return __builtin_amdgcn_readlane(chunk, l);
   };
 
-  // ---- direct-to-LDS copies.  Part c of this wave is part ws + c*SW of the
-  // entry (1 KB: slots 64 (ws + c SW) .. +64); lane i fetches the 16-byte
-  // global chunk the swizzle places in its slot.
+  // ---- direct-to-LDS copies.  An entry is 1 KB parts (part p: slots
+  // 64 p .. 64 p + 63); lane i fetches the 16-byte global chunk the swizzle
+  // places in its slot.  Wave ws copies parts ws kParts .. ws kParts +
+  // kParts - 1, in runs of kRun consecutive parts behind one M0 write (a run
+  // lies in the K tile or in the V tile, never both); dma_off carries the
+  // run's immediate offset taken off.
   constexpr int kPartsPerTile = L::kCopies / 2;
-  // Wave ws copies parts ws kParts .. ws kParts + kParts - 1 of each entry,
-  // in runs of kRun consecutive parts behind one M0 write (a run lies in the
-  // K tile or in the V tile, never both); dma_off carries the run's
-  // immediate offset taken off.
   constexpr int kRun = dma_run(C::kParts, kPartsPerTile);
   uint32_t dma_off[C::kParts];
 #pragma unroll
